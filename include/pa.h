@@ -1,0 +1,240 @@
+/*
+ * pa.h - paged KV cache and single-token decode attention for AMD MI355X (gfx950).
+ *
+ * C ABI of libpa.so.  Plain pointers and sizes only.
+ *
+ * Sources this interface follows (one page each):
+ *   [KVP] "Insights into LLM Serving Systems: KV-Cache Memory Allocation
+ *         Patterns", section 4, Observations 1 and 2.
+ *   [PAS] "Efficient Memory Management for Large Language Model Serving with
+ *         PagedAttention" (summary page), Summary and Key points.
+ *   [ROC] "Running Out of Cache" (serving plate XXIII.3): paging paragraph,
+ *         block-size paragraph, Workshop, "Fragmentation is lost users", Terms.
+ *   [VAC] "Leveraging Low-Level CUDA APIs for vAttention's Dynamic Memory",
+ *         section 5.2.3 (request-level KV-cache indexing).
+ *
+ * ---------------------------------------------------------------------------
+ * Cache layout (device memory owned by the caller)
+ * ---------------------------------------------------------------------------
+ * The K cache and the V cache are two separate device arrays of identical
+ * shape, element type kv_dtype, for all layers:
+ *
+ *   PA_PAGED:      [num_layers][num_blocks][num_kv_heads][block_size][head_dim]
+ *   PA_CONTIGUOUS: [num_layers][max_seqs][num_kv_heads][max_seq_len][head_dim]
+ *
+ * Paged: block b of a layer holds, for every KV head, block_size consecutive
+ * token rows; a sequence's blocks need not be adjacent and its block table maps
+ * logical block j (tokens j*BS .. j*BS+BS-1) to a physical block ([ROC] paging
+ * paragraph and Terms; [PAS] Summary).  One block id names the same block in
+ * every layer, in K and in V.
+ * Contiguous: request r owns the sub-tensor at offset r x (max K-cache size of
+ * one request) of each layer's tensor ([VAC] 5.2.3); the library hands out r.
+ *
+ * A "slot" names one token row:  slot = u*U + o, with U = block_size (paged:
+ * u = physical block, o = row in the block) or U = max_seq_len (contiguous:
+ * u = reqId, o = position).  Element (slot, head h, dim e) of layer l is at
+ *   ((l*units + u)*num_kv_heads + h)*U*head_dim + o*head_dim + e
+ * with units = num_blocks (paged) or max_seqs (contiguous).
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions
+ * ---------------------------------------------------------------------------
+ * Ownership: the caller owns all device memory (caches, q, out, tables, slots,
+ *   workspace) and keeps it alive while the pool uses it.  The library owns
+ *   only the opaque host-side pa_pool and frees it in pa_destroy_pool.  No
+ *   function allocates device memory.
+ * Errors: every call returns a pa_status; PA_OK is 0, errors are negative.
+ *   Nothing throws across the ABI.  On error no state changes (pa_reserve is
+ *   all-or-nothing) and pa_last_error() gives a message for the calling thread.
+ * Validation: host-visible arguments are checked on the host.  Device arrays
+ *   (tables, lengths, slots, pairs) are trusted: their entries must be in
+ *   range; out-of-range entries give undefined results.
+ * Threads and streams: a pool is not thread-safe.  Device calls only enqueue
+ *   work on the given stream (hipStream_t passed as void*, NULL = the default
+ *   stream) and never synchronise; the caller orders them.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,   /* bad argument; nothing changed */
+  PA_ERR_NO_BLOCKS = -2,     /* not enough free blocks: pre-empt a request and retry */
+  PA_ERR_NO_REQ_ID = -3,     /* all max_seqs request ids are live */
+  PA_ERR_UNKNOWN_SEQ = -4,   /* request id is not live */
+  PA_ERR_WORKSPACE = -5,     /* decode workspace missing or too small */
+  PA_ERR_HIP = -6,           /* a HIP call failed (launch error) */
+  PA_ERR_UNSUPPORTED = -7    /* valid request this build has no kernel for */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+typedef enum pa_layout { PA_PAGED = 0, PA_CONTIGUOUS = 1 } pa_layout;
+
+typedef struct pa_pool_desc {
+  int32_t num_layers;    /* >= 1 */
+  int32_t num_blocks;    /* paged: physical blocks (>= 1); contiguous: ignored */
+  int32_t block_size;    /* tokens per block: 8, 16 (the pages' default) or 32 */
+  int32_t num_kv_heads;  /* >= 1 */
+  int32_t head_dim;      /* 64 or 128 */
+  pa_dtype kv_dtype;     /* element type of both caches */
+  pa_layout layout;
+  int32_t max_seqs;      /* live requests at once; reqIds are 0 .. max_seqs-1 */
+  int32_t max_seq_len;   /* S: most tokens per request; contiguous: multiple of block_size */
+} pa_pool_desc;
+
+typedef struct pa_stats {
+  int64_t free_blocks;      /* paged: blocks on the free list */
+  int64_t used_blocks;      /* paged: blocks held by at least one request */
+  int64_t tokens;           /* token rows physically held (a shared row counts once) */
+  int64_t logical_tokens;   /* sum of live requests' lengths */
+  int64_t reserved_tokens;  /* paged: used_blocks*block_size; contiguous: live*S */
+  int64_t live_seqs;
+  int64_t cow_copies;       /* copy-on-write copies made since creation */
+  double utilisation;       /* tokens / reserved_tokens: share of reserved cache
+                               holding real tokens ([ROC] readouts, [PAS] Key points) */
+} pa_stats;
+
+typedef struct pa_pool pa_pool; /* opaque, host memory */
+
+/* Bytes of ONE of the two cache arrays (K or V) described by desc, or 0 if
+ * desc is invalid.  The caller allocates two arrays of this size. */
+size_t pa_cache_bytes(const pa_pool_desc* desc);
+
+/* KV bytes one token takes over all layers, K plus V:
+ * 2 * num_layers * num_kv_heads * head_dim * sizeof(kv_dtype)  ([KVP]
+ * Observation-2 prints 64, 128 and 240 KB for Yi-6B, Llama-3-8B and Yi-34B). */
+size_t pa_bytes_per_token(const pa_pool_desc* desc);
+
+/* Create a cache of fixed-size blocks over caller memory ([ROC] paging
+ * paragraph).  d_k_cache / d_v_cache: device arrays of pa_cache_bytes(desc)
+ * bytes each, 16-byte aligned.  Host-only: touches no device memory.  All
+ * blocks start free and are handed out in ascending id order; all request ids
+ * start free, 0 first.  *out receives the handle. */
+pa_status pa_create_pool(const pa_pool_desc* desc, void* d_k_cache, void* d_v_cache,
+                         pa_pool** out);
+
+/* Free the host handle.  The caches are the caller's. */
+pa_status pa_destroy_pool(pa_pool* pool);
+
+/* Replace the order in which free blocks are handed out: block_ids[0] first.
+ * block_ids must be a permutation of 0..num_blocks-1 and no block may be in
+ * use.  Paged only.  (Seeded placements: results must not depend on it.) */
+pa_status pa_set_free_order(pa_pool* pool, const int32_t* block_ids, int32_t n);
+
+/* ---- host block allocator: synchronous, touches no device memory ---------- */
+
+/* Admit a request: *req_id_out gets a free id in [0, max_seqs) ([VAC] 5.2.3:
+ * the library allocates reqId).  Its length is 0 and it holds no block. */
+pa_status pa_seq_add(pa_pool* pool, int32_t* req_id_out);
+
+/* Share all of parent's blocks with a new request ([PAS] Summary and Key
+ * points: sharing within a request for parallel samples or beam search, and
+ * across requests).  Each shared block's share count goes up by one; the
+ * child's length equals the parent's.  Paged only. */
+pa_status pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* child_out);
+
+/* End a request or pre-empt it ([ROC] "Fragmentation is lost users" and the
+ * Pre-emption term): each of its blocks loses one share and returns to the
+ * free list (in table order, last freed is reused first) when none is left;
+ * its id becomes free. */
+pa_status pa_seq_free(pa_pool* pool, int32_t req_id);
+
+/* Grow requests by counts[i] tokens each (counts NULL: one token each, the
+ * decode step of [KVP] Observation-1).  Allocate-on-fill: a request takes a
+ * new block only when its last block is full, so it wastes under one block
+ * ([ROC] paging paragraph).  Copy-on-write: if the next position falls inside
+ * a last block that is still shared, the request first moves to a fresh copy
+ * and drops its share; the last holder writes in place; full shared blocks are
+ * never copied ([PAS] Summary, [ROC] "Fragmentation is lost users").
+ * Requests are handled in the order given; each may appear once.
+ *   slots_out:     receives sum(counts) slots, request by request, position
+ *                  order (capacity slots_cap).
+ *   cow_pairs_out: receives *n_cow_out pairs {src_block, dst_block}
+ *                  (capacity cow_cap pairs; may be NULL if cow_cap is 0).
+ *                  Copy them with pa_copy_blocks BEFORE appending any slot
+ *                  returned by this call.
+ * All-or-nothing: PA_ERR_NO_BLOCKS (caller pre-empts and retries),
+ * PA_ERR_INVALID_ARG (cap too small, length beyond max_seq_len, duplicate id)
+ * and PA_ERR_UNKNOWN_SEQ change nothing.  Contiguous: slot = reqId*S + pos,
+ * no blocks, no copies. */
+pa_status pa_reserve(pa_pool* pool, const int32_t* req_ids, int32_t n, const int32_t* counts,
+                     int32_t* slots_out, int64_t slots_cap, int32_t* cow_pairs_out,
+                     int32_t cow_cap, int32_t* n_cow_out);
+
+/* Read block tables ([ROC] Terms: block table) into tables_out[n][stride],
+ * padded with -1, and lengths into lens_out[n] (either may be NULL).
+ * PA_ERR_INVALID_ARG if a table has more than stride entries.  Contiguous:
+ * tables are all -1 (none exist). */
+pa_status pa_get_block_tables(const pa_pool* pool, const int32_t* req_ids, int32_t n,
+                              int32_t stride, int32_t* tables_out, int32_t* lens_out);
+
+pa_status pa_get_stats(const pa_pool* pool, pa_stats* out);
+
+/* ---- device calls: enqueue on stream, asynchronous ------------------------ */
+
+/* Copy-on-write copies: for each of the n pairs d_pairs[i] = {src, dst}
+ * (device int32[n][2]), block dst takes block src's rows in every layer, K and
+ * V.  No dst may be a src of another pair (pa_reserve never makes such pairs).
+ * Paged only.  n == 0 is a no-op. */
+pa_status pa_copy_blocks(pa_pool* pool, const int32_t* d_pairs, int32_t n, void* stream);
+
+/* KV append ([KVP] Observation-1): for i < n with d_slots[i] >= 0, write token
+ * i's rows d_k[i][h][:] and d_v[i][h][:] (device, [n][num_kv_heads][head_dim],
+ * kv_dtype, 16-byte aligned) into slot d_slots[i] of layer `layer`, for every
+ * KV head.  A bit copy: no rounding.  Negative slots are skipped.  Slots in
+ * one call must be distinct. */
+pa_status pa_append_kv(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                       const int32_t* d_slots, int32_t n, void* stream);
+
+/* Context partition pa_decode uses for these sizes (partition_tokens 0 =
+ * the library's choice), in tokens: a multiple of block_size. */
+int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t max_context,
+                                   int32_t partition_tokens);
+
+/* Workspace bytes pa_decode needs (0 when one partition covers max_context). */
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context, int32_t partition_tokens);
+
+/* Single-token decode attention over the cache ([PAS] Summary, [ROC] paging
+ * paragraph and Terms: attention reads K and V through the block table).
+ * For each sequence s < num_seqs and query head h (KV head h / G, G =
+ * num_q_heads / num_kv_heads):
+ *     out[s][h][:] = sum_t w_t V_s[t],  w = softmax_t(scale * <q[s][h], K_s[t]>)
+ * over the L_s = d_context_lens[s] tokens of sequence s (L_s = 0 gives zeros).
+ *   d_q:            device [num_seqs][num_q_heads][head_dim], q_dtype (must
+ *                   equal kv_dtype); 16-byte aligned.
+ *   d_block_tables: paged: device int32 [num_seqs][table_stride], entry j the
+ *                   physical block of tokens j*BS..; contiguous: ignored.
+ *   d_req_ids:      contiguous: device int32 [num_seqs] request ids, or NULL
+ *                   for "request id = s"; paged: ignored.
+ *   d_context_lens: device int32 [num_seqs], each in [0, max_context].
+ *   max_context:    bound on the lengths; sizes the launch.
+ *   d_out:          device fp32 [num_seqs][num_q_heads][head_dim].
+ *   d_workspace:    device scratch of >= pa_decode_workspace_bytes(...) bytes
+ *                   (may be NULL when that is 0).
+ * Softmax is computed online in fp32 per context partition; partitions are
+ * merged in a fixed order, so results depend only on logical positions, never
+ * on which physical blocks hold them.  Supported: G <= 8, head_dim 64/128. */
+pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
+                    int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                    int32_t table_stride, const int32_t* d_req_ids,
+                    const int32_t* d_context_lens, int32_t num_seqs, int32_t max_context,
+                    int32_t partition_tokens, float* d_out, void* d_workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Message of the calling thread's last error ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,120 @@
+"""ctypes declarations of libpa.so (include/pa.h), same names as the C ABI.
+
+Only argument marshalling lives here: every step of the hot path runs in the
+library's C++ allocator and HIP kernels.  Loading fails loudly if the library
+has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = -1
+PA_ERR_NO_BLOCKS = -2
+PA_ERR_NO_REQ_ID = -3
+PA_ERR_UNKNOWN_SEQ = -4
+PA_ERR_WORKSPACE = -5
+PA_ERR_HIP = -6
+PA_ERR_UNSUPPORTED = -7
+
+PA_F32 = 0
+PA_BF16 = 1
+PA_PAGED = 0
+PA_CONTIGUOUS = 1
+
+STATUS_NAMES = {
+    PA_OK: "PA_OK", PA_ERR_INVALID_ARG: "PA_ERR_INVALID_ARG", PA_ERR_NO_BLOCKS: "PA_ERR_NO_BLOCKS",
+    PA_ERR_NO_REQ_ID: "PA_ERR_NO_REQ_ID", PA_ERR_UNKNOWN_SEQ: "PA_ERR_UNKNOWN_SEQ",
+    PA_ERR_WORKSPACE: "PA_ERR_WORKSPACE", PA_ERR_HIP: "PA_ERR_HIP",
+    PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED",
+}
+
+# every function include/pa.h declares
+EXPORTS = (
+    "pa_cache_bytes", "pa_bytes_per_token", "pa_create_pool", "pa_destroy_pool",
+    "pa_set_free_order", "pa_seq_add", "pa_seq_fork", "pa_seq_free", "pa_reserve",
+    "pa_get_block_tables", "pa_get_stats", "pa_copy_blocks", "pa_append_kv",
+    "pa_decode_partition_tokens", "pa_decode_workspace_bytes", "pa_decode", "pa_last_error",
+)
+
+
+class pa_pool_desc(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int),
+        ("layout", ctypes.c_int), ("max_seqs", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+    ]
+
+
+class pa_stats(ctypes.Structure):
+    _fields_ = [
+        ("free_blocks", ctypes.c_int64), ("used_blocks", ctypes.c_int64),
+        ("tokens", ctypes.c_int64), ("logical_tokens", ctypes.c_int64),
+        ("reserved_tokens", ctypes.c_int64), ("live_seqs", ctypes.c_int64),
+        ("cow_copies", ctypes.c_int64), ("utilisation", ctypes.c_double),
+    ]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_p32 = ctypes.POINTER(ctypes.c_int32)
+
+
+def load() -> ctypes.CDLL:
+    """The loaded library; raises if libpa.so is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_241_amd.build` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "pa_cache_bytes": (ctypes.c_size_t, [ctypes.POINTER(pa_pool_desc)]),
+        "pa_bytes_per_token": (ctypes.c_size_t, [ctypes.POINTER(pa_pool_desc)]),
+        "pa_create_pool": (ctypes.c_int, [ctypes.POINTER(pa_pool_desc), _vp, _vp, ctypes.POINTER(_vp)]),
+        "pa_destroy_pool": (ctypes.c_int, [_vp]),
+        "pa_set_free_order": (ctypes.c_int, [_vp, _p32, _i32]),
+        "pa_seq_add": (ctypes.c_int, [_vp, _p32]),
+        "pa_seq_fork": (ctypes.c_int, [_vp, _i32, _p32]),
+        "pa_seq_free": (ctypes.c_int, [_vp, _i32]),
+        "pa_reserve": (ctypes.c_int, [_vp, _p32, _i32, _p32, _p32, _i64, _p32, _i32, _p32]),
+        "pa_get_block_tables": (ctypes.c_int, [_vp, _p32, _i32, _i32, _p32, _p32]),
+        "pa_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(pa_stats)]),
+        "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _i32, _vp]),
+        "pa_append_kv": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i32, _vp]),
+        "pa_decode_partition_tokens": (ctypes.c_int32, [_vp, _i32, _i32, _i32]),
+        "pa_decode_workspace_bytes": (ctypes.c_size_t, [_vp, _i32, _i32, _i32, _i32]),
+        "pa_decode": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _i32, ctypes.c_float, _vp, _i32,
+                                     _vp, _vp, _i32, _i32, _i32, _vp, _vp, ctypes.c_size_t, _vp]),
+        "pa_last_error": (ctypes.c_char_p, []),
+    }
+    assert set(sig) == set(EXPORTS)
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(status: int, where: str) -> None:
+    if status != PA_OK:
+        msg = load().pa_last_error().decode(errors="replace")
+        raise PaError(status, where, msg)

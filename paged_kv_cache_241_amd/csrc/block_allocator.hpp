@@ -1,0 +1,89 @@
+// Host-side block allocator of the paged KV cache.  Plain C++17, no HIP: it
+// builds and runs on any CPU.
+//
+// Rules (pages: "Running Out of Cache" paging paragraph, block-size paragraph,
+// "Fragmentation is lost users"; the PagedAttention summary page, Summary and
+// Key points; "Leveraging Low-Level CUDA APIs for vAttention's Dynamic
+// Memory" 5.2.3):
+//   * fixed blocks of block_size tokens; a block table per request maps its
+//     logical blocks to physical ones;
+//   * allocate-on-fill: a request takes a block only when its last one is full;
+//   * requests can share blocks (fork); a shared partially filled last block is
+//     copied when a sharer first writes into it, the last holder writes in
+//     place;
+//   * finishing or pre-empting a request returns its unshared blocks;
+//   * reqIds in [0, max_seqs) are handed out by the allocator.
+// Choices where the pages are silent: the free list and the reqId list are
+// stacks (last returned, first reused); reserve is all-or-nothing and handles
+// requests in the order given.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace pa {
+
+enum Status : int {
+  kOk = 0,
+  kInvalidArg = -1,
+  kNoBlocks = -2,
+  kNoReqId = -3,
+  kUnknownSeq = -4,
+};
+
+struct AllocStats {
+  int64_t free_blocks = 0, used_blocks = 0, tokens = 0, logical_tokens = 0;
+  int64_t reserved_tokens = 0, live_seqs = 0, cow_copies = 0;
+  double utilisation = 0.0;
+};
+
+class BlockAllocator {
+ public:
+  // paged == false: contiguous per-request layout (no blocks; slot = reqId*S + pos).
+  BlockAllocator(int32_t num_blocks, int32_t block_size, int32_t max_seqs, int32_t max_seq_len,
+                 bool paged);
+
+  Status set_free_order(const int32_t* ids, int32_t n, std::string* err);
+  Status add(int32_t* rid, std::string* err);
+  Status fork(int32_t parent, int32_t* child, std::string* err);
+  Status free_seq(int32_t rid, std::string* err);
+  Status reserve(const int32_t* rids, int32_t n, const int32_t* counts, int32_t* slots,
+                 int64_t slots_cap, int32_t* pairs, int32_t pair_cap, int32_t* n_pairs,
+                 std::string* err);
+  Status tables(const int32_t* rids, int32_t n, int32_t stride, int32_t* out, int32_t* lens,
+                std::string* err) const;
+  AllocStats stats() const;
+
+  bool paged() const { return paged_; }
+  int32_t block_size() const { return block_size_; }
+  int32_t num_blocks() const { return num_blocks_; }
+  int32_t max_seqs() const { return max_seqs_; }
+  int32_t max_seq_len() const { return max_seq_len_; }
+
+ private:
+  struct Seq {
+    bool live = false;
+    int32_t len = 0;
+    std::vector<int32_t> table;
+  };
+
+  Status check_live(int32_t rid, std::string* err) const;
+  int32_t pop_block();
+
+  bool paged_;
+  int32_t num_blocks_, block_size_, max_seqs_, max_seq_len_;
+  std::vector<int32_t> free_;      // stack: back() is handed out next
+  std::vector<int32_t> refcount_;  // share count per block
+  std::vector<int32_t> fill_;      // token rows written per block
+  std::vector<int32_t> free_ids_;  // stack of free reqIds
+  std::vector<Seq> seqs_;          // indexed by reqId
+  int64_t cow_copies_ = 0;
+  // per-call scratch (kept to avoid reallocating on every reserve)
+  std::vector<uint32_t> mark_;
+  uint32_t epoch_ = 0;
+  std::vector<int32_t> touched_;   // last blocks whose share count a dry run lowered
+  std::vector<int32_t> share_;     // dry-run share count of touched blocks
+};
+
+}  // namespace pa

@@ -1,0 +1,63 @@
+// Launchers of the HIP kernels behind libpa.so (internal; the public ABI is
+// include/pa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pa {
+
+enum Kind : int { kF32 = 0, kBF16 = 1 };
+
+// Token-row addressing shared by append and decode: a slot u*U + o of a layer
+// sits at ((u*num_kv_heads + h)*U + o)*head_dim elements from the layer base.
+struct CacheGeom {
+  char* k_base = nullptr;      // layer 0 of the K cache
+  char* v_base = nullptr;
+  int64_t layer_bytes = 0;     // bytes of one layer of one cache
+  int32_t num_layers = 0;
+  int32_t num_kv_heads = 0;
+  int32_t head_dim = 0;
+  int32_t elt = 0;             // bytes per element
+  int32_t unit = 0;            // U: block_size (paged) or max_seq_len (contiguous)
+  int32_t block_size = 0;
+  int32_t paged = 1;
+};
+
+hipError_t launch_append(const CacheGeom& g, int32_t layer, const void* k, const void* v,
+                         const int32_t* slots, int32_t n, hipStream_t stream);
+
+hipError_t launch_copy_blocks(const CacheGeom& g, const int32_t* pairs, int32_t n,
+                              hipStream_t stream);
+
+struct DecodeArgs {
+  const void* q = nullptr;           // [B][Hq][D]
+  const int32_t* tables = nullptr;   // paged: [B][stride]
+  const int32_t* req_ids = nullptr;  // contiguous: [B] or null
+  const int32_t* lens = nullptr;     // [B]
+  float* out = nullptr;              // [B][Hq][D]
+  float* ws = nullptr;               // partials when num_partitions > 1
+  int32_t layer = 0;
+  int32_t num_seqs = 0;
+  int32_t num_q_heads = 0;
+  int32_t table_stride = 0;
+  int32_t partition_blocks = 0;      // blocks of block_size tokens per partition
+  int32_t num_partitions = 1;
+  float scale = 1.0f;
+};
+
+// Returns hipErrorInvalidValue-free codes from the launch; *supported is set
+// to false (and nothing is launched) when no kernel exists for the shape.
+hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool* supported,
+                         hipStream_t stream);
+
+// Bytes of decode partials for these sizes.
+inline size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                     int32_t num_partitions) {
+  if (num_partitions <= 1) return 0;
+  return static_cast<size_t>(num_seqs) * num_q_heads * num_partitions *
+         (static_cast<size_t>(head_dim) + 2) * sizeof(float);
+}
+
+}  // namespace pa

@@ -1,0 +1,310 @@
+// C ABI of libpa.so (include/pa.h): argument checks, error text, the host
+// block allocator and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <new>
+#include <string>
+
+#include "../../include/pa.h"
+#include "block_allocator.hpp"
+#include "kernels.hpp"
+
+struct pa_pool {
+  pa_pool_desc desc;
+  pa::CacheGeom geom;
+  pa::BlockAllocator alloc;
+  pa_pool(const pa_pool_desc& d, const pa::CacheGeom& g)
+      : desc(d),
+        geom(g),
+        alloc(d.num_blocks, d.block_size, d.max_seqs, d.max_seq_len, d.layout == PA_PAGED) {}
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+pa_status fail(pa_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+pa_status from_alloc(pa::Status st, const std::string& msg) {
+  if (st == pa::kOk) return PA_OK;
+  g_err = msg;
+  return static_cast<pa_status>(static_cast<int>(st));
+}
+
+int32_t elt_bytes(pa_dtype t) { return t == PA_BF16 ? 2 : (t == PA_F32 ? 4 : 0); }
+
+// Empty string if desc is valid, else the reason.
+std::string check_desc(const pa_pool_desc* d) {
+  if (d == nullptr) return "null pool descriptor";
+  if (d->num_layers < 1) return "num_layers must be >= 1";
+  if (d->block_size != 8 && d->block_size != 16 && d->block_size != 32)
+    return "block_size must be 8, 16 or 32";
+  if (d->num_kv_heads < 1) return "num_kv_heads must be >= 1";
+  if (d->head_dim != 64 && d->head_dim != 128) return "head_dim must be 64 or 128";
+  if (elt_bytes(d->kv_dtype) == 0) return "kv_dtype must be PA_F32 or PA_BF16";
+  if (d->layout != PA_PAGED && d->layout != PA_CONTIGUOUS) return "unknown layout";
+  if (d->max_seqs < 1) return "max_seqs must be >= 1";
+  if (d->max_seq_len < 1) return "max_seq_len must be >= 1";
+  if (d->layout == PA_PAGED) {
+    if (d->num_blocks < 1) return "num_blocks must be >= 1";
+    if (static_cast<int64_t>(d->num_blocks) * d->block_size > INT32_MAX)
+      return "num_blocks * block_size must fit in int32 slots";
+  } else {
+    if (d->max_seq_len % d->block_size != 0)
+      return "contiguous layout: max_seq_len must be a multiple of block_size";
+    if (static_cast<int64_t>(d->max_seqs) * d->max_seq_len > INT32_MAX)
+      return "max_seqs * max_seq_len must fit in int32 slots";
+  }
+  return "";
+}
+
+int64_t layer_bytes(const pa_pool_desc* d) {
+  const int64_t units = d->layout == PA_PAGED ? d->num_blocks : d->max_seqs;
+  const int64_t unit = d->layout == PA_PAGED ? d->block_size : d->max_seq_len;
+  return units * d->num_kv_heads * unit * d->head_dim * elt_bytes(d->kv_dtype);
+}
+
+int32_t choose_partition_blocks(const pa_pool* p, int32_t num_seqs, int32_t max_context,
+                                int32_t partition_tokens) {
+  const int32_t bs = p->desc.block_size;
+  const int32_t nblk = (max_context + bs - 1) / bs;
+  if (nblk <= 0) return 1;
+  if (partition_tokens > 0) return partition_tokens / bs;
+  // Enough workgroups to fill 256 CUs several times over, but partitions of
+  // at least 256 tokens so each of the 4 waves streams several blocks.
+  const int64_t base = static_cast<int64_t>(num_seqs) * p->desc.num_kv_heads;
+  const int64_t target = 1024;
+  int64_t parts = (target + base - 1) / base;
+  const int64_t min_blocks = (256 + bs - 1) / bs;
+  const int64_t max_parts = (nblk + min_blocks - 1) / min_blocks;
+  if (parts > max_parts) parts = max_parts;
+  if (parts < 1) parts = 1;
+  return static_cast<int32_t>((nblk + parts - 1) / parts);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_cache_bytes(const pa_pool_desc* desc) {
+  if (!check_desc(desc).empty()) return 0;
+  return static_cast<size_t>(layer_bytes(desc) * desc->num_layers);
+}
+
+size_t pa_bytes_per_token(const pa_pool_desc* desc) {
+  if (!check_desc(desc).empty()) return 0;
+  return static_cast<size_t>(2) * desc->num_layers * desc->num_kv_heads * desc->head_dim *
+         elt_bytes(desc->kv_dtype);
+}
+
+pa_status pa_create_pool(const pa_pool_desc* desc, void* d_k_cache, void* d_v_cache,
+                         pa_pool** out) {
+  if (out == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool: null output");
+  *out = nullptr;
+  const std::string why = check_desc(desc);
+  if (!why.empty()) return fail(PA_ERR_INVALID_ARG, "create_pool: " + why);
+  if (d_k_cache == nullptr || d_v_cache == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "create_pool: null cache pointer");
+  if ((reinterpret_cast<uintptr_t>(d_k_cache) | reinterpret_cast<uintptr_t>(d_v_cache)) & 15)
+    return fail(PA_ERR_INVALID_ARG, "create_pool: caches must be 16-byte aligned");
+  pa::CacheGeom g;
+  g.k_base = static_cast<char*>(d_k_cache);
+  g.v_base = static_cast<char*>(d_v_cache);
+  g.layer_bytes = layer_bytes(desc);
+  g.num_layers = desc->num_layers;
+  g.num_kv_heads = desc->num_kv_heads;
+  g.head_dim = desc->head_dim;
+  g.elt = elt_bytes(desc->kv_dtype);
+  g.block_size = desc->block_size;
+  g.paged = desc->layout == PA_PAGED ? 1 : 0;
+  g.unit = g.paged ? desc->block_size : desc->max_seq_len;
+  pa_pool* p = new (std::nothrow) pa_pool(*desc, g);
+  if (p == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool: out of host memory");
+  *out = p;
+  return PA_OK;
+}
+
+pa_status pa_destroy_pool(pa_pool* pool) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "destroy_pool: null pool");
+  delete pool;
+  return PA_OK;
+}
+
+pa_status pa_set_free_order(pa_pool* pool, const int32_t* block_ids, int32_t n) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "set_free_order: null pool");
+  std::string err;
+  pa::Status st = pool->alloc.set_free_order(block_ids, n, &err);
+  return from_alloc(st, err);
+}
+
+pa_status pa_seq_add(pa_pool* pool, int32_t* req_id_out) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "seq_add: null pool");
+  std::string err;
+  pa::Status st = pool->alloc.add(req_id_out, &err);
+  return from_alloc(st, err);
+}
+
+pa_status pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* child_out) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "seq_fork: null pool");
+  std::string err;
+  pa::Status st = pool->alloc.fork(parent, child_out, &err);
+  return from_alloc(st, err);
+}
+
+pa_status pa_seq_free(pa_pool* pool, int32_t req_id) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "seq_free: null pool");
+  std::string err;
+  pa::Status st = pool->alloc.free_seq(req_id, &err);
+  return from_alloc(st, err);
+}
+
+pa_status pa_reserve(pa_pool* pool, const int32_t* req_ids, int32_t n, const int32_t* counts,
+                     int32_t* slots_out, int64_t slots_cap, int32_t* cow_pairs_out,
+                     int32_t cow_cap, int32_t* n_cow_out) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "reserve: null pool");
+  std::string err;
+  pa::Status st = pool->alloc.reserve(req_ids, n, counts, slots_out, slots_cap, cow_pairs_out,
+                                      cow_cap, n_cow_out, &err);
+  return from_alloc(st, err);
+}
+
+pa_status pa_get_block_tables(const pa_pool* pool, const int32_t* req_ids, int32_t n,
+                              int32_t stride, int32_t* tables_out, int32_t* lens_out) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "get_block_tables: null pool");
+  std::string err;
+  pa::Status st = pool->alloc.tables(req_ids, n, stride, tables_out, lens_out, &err);
+  return from_alloc(st, err);
+}
+
+pa_status pa_get_stats(const pa_pool* pool, pa_stats* out) {
+  if (pool == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARG, "get_stats: null argument");
+  const pa::AllocStats s = pool->alloc.stats();
+  out->free_blocks = s.free_blocks;
+  out->used_blocks = s.used_blocks;
+  out->tokens = s.tokens;
+  out->logical_tokens = s.logical_tokens;
+  out->reserved_tokens = s.reserved_tokens;
+  out->live_seqs = s.live_seqs;
+  out->cow_copies = s.cow_copies;
+  out->utilisation = s.utilisation;
+  return PA_OK;
+}
+
+pa_status pa_copy_blocks(pa_pool* pool, const int32_t* d_pairs, int32_t n, void* stream) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "copy_blocks: null pool");
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "copy_blocks: negative pair count");
+  if (n == 0) return PA_OK;
+  if (!pool->geom.paged) return fail(PA_ERR_INVALID_ARG, "copy_blocks: contiguous pool has no blocks");
+  if (d_pairs == nullptr) return fail(PA_ERR_INVALID_ARG, "copy_blocks: null pairs");
+  hipError_t e = pa::launch_copy_blocks(pool->geom, d_pairs, n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("copy_blocks: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+pa_status pa_append_kv(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                       const int32_t* d_slots, int32_t n, void* stream) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "append_kv: null pool");
+  if (layer < 0 || layer >= pool->desc.num_layers)
+    return fail(PA_ERR_INVALID_ARG, "append_kv: layer out of range");
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "append_kv: negative token count");
+  if (n == 0) return PA_OK;
+  if (d_k == nullptr || d_v == nullptr || d_slots == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "append_kv: null device pointer");
+  if ((reinterpret_cast<uintptr_t>(d_k) | reinterpret_cast<uintptr_t>(d_v)) & 15)
+    return fail(PA_ERR_INVALID_ARG, "append_kv: k and v must be 16-byte aligned");
+  hipError_t e = pa::launch_append(pool->geom, layer, d_k, d_v, d_slots, n,
+                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("append_kv: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t max_context,
+                                   int32_t partition_tokens) {
+  if (pool == nullptr || num_seqs < 0 || max_context < 0 || partition_tokens < 0) return 0;
+  if (partition_tokens % pool->desc.block_size != 0) return 0;
+  return choose_partition_blocks(pool, num_seqs, max_context, partition_tokens) *
+         pool->desc.block_size;
+}
+
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context, int32_t partition_tokens) {
+  if (pool == nullptr || num_seqs < 0 || max_context < 0 || partition_tokens < 0) return 0;
+  if (partition_tokens % pool->desc.block_size != 0) return 0;
+  const int32_t bs = pool->desc.block_size;
+  const int32_t pb = choose_partition_blocks(pool, num_seqs, max_context, partition_tokens);
+  const int32_t nblk = (max_context + bs - 1) / bs;
+  const int32_t parts = nblk <= 0 ? 1 : (nblk + pb - 1) / pb;
+  return pa::decode_workspace_bytes(num_seqs, num_q_heads, pool->desc.head_dim, parts);
+}
+
+pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
+                    int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                    int32_t table_stride, const int32_t* d_req_ids,
+                    const int32_t* d_context_lens, int32_t num_seqs, int32_t max_context,
+                    int32_t partition_tokens, float* d_out, void* d_workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "decode: null pool");
+  const pa_pool_desc& d = pool->desc;
+  if (layer < 0 || layer >= d.num_layers) return fail(PA_ERR_INVALID_ARG, "decode: layer out of range");
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "decode: negative num_seqs");
+  if (num_seqs == 0) return PA_OK;
+  if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "decode: num_q_heads must be a positive multiple of num_kv_heads");
+  if (q_dtype != d.kv_dtype)
+    return fail(PA_ERR_UNSUPPORTED, "decode: q_dtype must equal the cache's kv_dtype");
+  if (num_q_heads / d.num_kv_heads > 8)
+    return fail(PA_ERR_UNSUPPORTED, "decode: GQA groups of more than 8 query heads");
+  if (max_context < 0 || max_context > d.max_seq_len)
+    return fail(PA_ERR_INVALID_ARG, "decode: max_context must be in [0, max_seq_len]");
+  if (partition_tokens < 0 || partition_tokens % d.block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, "decode: partition_tokens must be 0 or a positive multiple of block_size");
+  if (d_q == nullptr || d_context_lens == nullptr || d_out == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "decode: null device pointer");
+  if (reinterpret_cast<uintptr_t>(d_q) & 15) return fail(PA_ERR_INVALID_ARG, "decode: q must be 16-byte aligned");
+  const int32_t bs = d.block_size;
+  const int32_t nblk = (max_context + bs - 1) / bs;
+  if (d.layout == PA_PAGED) {
+    if (d_block_tables == nullptr) return fail(PA_ERR_INVALID_ARG, "decode: null block tables");
+    if (table_stride < nblk)
+      return fail(PA_ERR_INVALID_ARG, "decode: table_stride is shorter than ceil(max_context / block_size)");
+  }
+  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "decode: scale is NaN");
+  const int64_t grid = static_cast<int64_t>(num_seqs) * d.num_kv_heads;
+  pa::DecodeArgs a;
+  a.q = d_q;
+  a.tables = d.layout == PA_PAGED ? d_block_tables : nullptr;
+  a.req_ids = d.layout == PA_PAGED ? nullptr : d_req_ids;
+  a.lens = d_context_lens;
+  a.out = d_out;
+  a.layer = layer;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.table_stride = table_stride;
+  a.partition_blocks = choose_partition_blocks(pool, num_seqs, max_context, partition_tokens);
+  a.num_partitions = nblk <= 0 ? 1 : (nblk + a.partition_blocks - 1) / a.partition_blocks;
+  a.scale = scale;
+  if (grid * a.num_partitions > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "decode: launch too large");
+  const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, d.head_dim, a.num_partitions);
+  if (need > 0) {
+    if (d_workspace == nullptr || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "decode: workspace needs " + std::to_string(need) + " bytes, got " +
+                                        std::to_string(d_workspace ? workspace_bytes : 0));
+    if (reinterpret_cast<uintptr_t>(d_workspace) & 15)
+      return fail(PA_ERR_INVALID_ARG, "decode: workspace must be 16-byte aligned");
+    a.ws = static_cast<float*>(d_workspace);
+  }
+  bool supported = true;
+  const int kind = d.kv_dtype == PA_BF16 ? pa::kBF16 : pa::kF32;
+  hipError_t e = pa::launch_decode(pool->geom, kind, a, &supported, static_cast<hipStream_t>(stream));
+  if (!supported) return fail(PA_ERR_UNSUPPORTED, "decode: no kernel for this shape");
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("decode: ") + hipGetErrorString(e));
+  return PA_OK;
+}
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,222 @@
+"""A paged KV cache over torch device memory, driven through libpa.so.
+
+PyTorch supplies the device memory (the two cache arrays, q, out, tables,
+workspace) and the stream; every allocator step and every kernel is the C
+library's.  Method names follow the C ABI (``pa_seq_add`` -> ``add``, ...).
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import capi
+
+_DTYPES = {"f32": capi.PA_F32, "bf16": capi.PA_BF16}
+_LAYOUTS = {"paged": capi.PA_PAGED, "contiguous": capi.PA_CONTIGUOUS}
+
+
+def _ptr32(a: np.ndarray):
+    assert a.dtype == np.int32 and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream_handle(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Pool:
+    """K and V caches for ``num_layers`` layers plus the host block allocator.
+
+    Cache tensors (``k_cache``, ``v_cache``) have shape
+    ``[num_layers][units][num_kv_heads][U][head_dim]`` with ``units, U`` =
+    ``num_blocks, block_size`` (paged) or ``max_seqs, max_seq_len`` (contiguous).
+    """
+
+    def __init__(self, num_layers: int, num_blocks: int, block_size: int, num_kv_heads: int,
+                 head_dim: int, kv_dtype: str = "bf16", layout: str = "paged",
+                 max_seqs: int = 256, max_seq_len: int = 8192, device="cuda", fill=None,
+                 host_only: bool = False):
+        """``host_only``: no cache memory is allocated and only the host
+        allocator calls may be used (the library never touches the caches in
+        those calls); device calls then fail."""
+        import torch
+
+        self.lib = capi.load()
+        self.kv_dtype = kv_dtype
+        self.layout = layout
+        self.desc = capi.pa_pool_desc(num_layers, num_blocks if layout == "paged" else 0,
+                                      block_size, num_kv_heads, head_dim, _DTYPES[kv_dtype],
+                                      _LAYOUTS[layout], max_seqs, max_seq_len)
+        nbytes = self.lib.pa_cache_bytes(ctypes.byref(self.desc))
+        if nbytes == 0:
+            raise capi.PaError(capi.PA_ERR_INVALID_ARG, "Pool", "invalid pool description")
+        tdt = torch.bfloat16 if kv_dtype == "bf16" else torch.float32
+        units, unit = ((num_blocks, block_size) if layout == "paged" else (max_seqs, max_seq_len))
+        shape = (num_layers, units, num_kv_heads, unit, head_dim)
+        if host_only:
+            self.k_cache = self.v_cache = None
+            self._fake = torch.empty(16, dtype=torch.uint8)
+        elif fill is None:
+            self.k_cache = torch.empty(shape, dtype=tdt, device=device)
+            self.v_cache = torch.empty(shape, dtype=tdt, device=device)
+        else:
+            self.k_cache = torch.full(shape, fill, dtype=tdt, device=device)
+            self.v_cache = torch.full(shape, fill, dtype=tdt, device=device)
+        if host_only:
+            # any 16-byte aligned address: allocator calls never dereference it
+            kp = vp = (self._fake.data_ptr() + 15) // 16 * 16
+        else:
+            assert self.k_cache.numel() * self.k_cache.element_size() == nbytes
+            kp, vp = self.k_cache.data_ptr(), self.v_cache.data_ptr()
+        h = ctypes.c_void_p()
+        capi.check(self.lib.pa_create_pool(ctypes.byref(self.desc), kp, vp, ctypes.byref(h)),
+                   "pa_create_pool")
+        self.handle = h
+        self.num_layers, self.num_blocks, self.block_size = num_layers, num_blocks, block_size
+        self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        self.max_seqs, self.max_seq_len = max_seqs, max_seq_len
+        self.torch_dtype = tdt
+
+    # -- lifetime --------------------------------------------------------------
+    def close(self) -> None:
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            capi.check(self.lib.pa_destroy_pool(self.handle), "pa_destroy_pool")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- host allocator --------------------------------------------------------
+    def bytes_per_token(self) -> int:
+        return int(self.lib.pa_bytes_per_token(ctypes.byref(self.desc)))
+
+    def set_free_order(self, order) -> None:
+        order = np.ascontiguousarray(order, dtype=np.int32)
+        capi.check(self.lib.pa_set_free_order(self.handle, _ptr32(order), len(order)),
+                   "pa_set_free_order")
+
+    def add(self) -> int:
+        rid = ctypes.c_int32()
+        capi.check(self.lib.pa_seq_add(self.handle, ctypes.byref(rid)), "pa_seq_add")
+        return rid.value
+
+    def fork(self, parent: int) -> int:
+        rid = ctypes.c_int32()
+        capi.check(self.lib.pa_seq_fork(self.handle, parent, ctypes.byref(rid)), "pa_seq_fork")
+        return rid.value
+
+    def free_seq(self, rid: int) -> None:
+        capi.check(self.lib.pa_seq_free(self.handle, rid), "pa_seq_free")
+
+    def reserve(self, req_ids, counts=None):
+        """Grow requests; returns (slots int32[total], cow pairs int32[k][2])."""
+        rids = np.ascontiguousarray(req_ids, dtype=np.int32)
+        n = len(rids)
+        if counts is None:
+            cnt = None
+            total = n
+        else:
+            cnt = np.ascontiguousarray(counts, dtype=np.int32)
+            total = int(cnt.sum())
+        slots = np.empty(max(total, 1), dtype=np.int32)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        ncow = ctypes.c_int32()
+        capi.check(self.lib.pa_reserve(self.handle, _ptr32(rids), n,
+                                       _ptr32(cnt) if cnt is not None else None,
+                                       _ptr32(slots), total, _ptr32(pairs), n, ctypes.byref(ncow)),
+                   "pa_reserve")
+        return slots[:total], pairs[: ncow.value]
+
+    def block_tables(self, req_ids, stride: int | None = None):
+        """(tables int32[n][stride] padded with -1, lengths int32[n])."""
+        rids = np.ascontiguousarray(req_ids, dtype=np.int32)
+        n = len(rids)
+        lens = np.empty(max(n, 1), dtype=np.int32)
+        if stride is None:
+            capi.check(self.lib.pa_get_block_tables(self.handle, _ptr32(rids), n, 0, None,
+                                                    _ptr32(lens)), "pa_get_block_tables")
+            stride = max(1, -(-int(lens[:n].max(initial=0)) // self.block_size))
+        tables = np.empty((max(n, 1), stride), dtype=np.int32)
+        capi.check(self.lib.pa_get_block_tables(self.handle, _ptr32(rids), n, stride,
+                                                _ptr32(tables), _ptr32(lens)), "pa_get_block_tables")
+        return tables[:n], lens[:n]
+
+    def stats(self) -> dict:
+        st = capi.pa_stats()
+        capi.check(self.lib.pa_get_stats(self.handle, ctypes.byref(st)), "pa_get_stats")
+        return {name: getattr(st, name) for name, _ in capi.pa_stats._fields_}
+
+    # -- device ----------------------------------------------------------------
+    def copy_blocks(self, pairs, stream=None) -> None:
+        """pairs: device int32 tensor [n][2] of (src, dst) blocks."""
+        n = int(pairs.shape[0]) if pairs is not None else 0
+        if n == 0:
+            return
+        assert self.k_cache is not None, "host-only pool"
+        assert pairs.dtype.is_floating_point is False and pairs.is_cuda and pairs.is_contiguous()
+        assert tuple(pairs.shape) == (n, 2)
+        capi.check(self.lib.pa_copy_blocks(self.handle, pairs.data_ptr(), n, _stream_handle(stream)),
+                   "pa_copy_blocks")
+
+    def append_kv(self, layer: int, k, v, slots, stream=None) -> None:
+        """k, v: device [n][Hkv][D] in the cache dtype; slots: device int32 [n]."""
+        n = int(slots.shape[0])
+        if n == 0:
+            return
+        assert self.k_cache is not None, "host-only pool"
+        for t in (k, v):
+            assert t.is_cuda and t.is_contiguous() and t.dtype == self.torch_dtype
+            assert tuple(t.shape) == (n, self.num_kv_heads, self.head_dim)
+        assert slots.is_cuda and slots.is_contiguous() and str(slots.dtype) == "torch.int32"
+        capi.check(self.lib.pa_append_kv(self.handle, layer, k.data_ptr(), v.data_ptr(),
+                                         slots.data_ptr(), n, _stream_handle(stream)), "pa_append_kv")
+
+    def partition_tokens(self, num_seqs: int, max_context: int, partition_tokens: int = 0) -> int:
+        return int(self.lib.pa_decode_partition_tokens(self.handle, num_seqs, max_context,
+                                                        partition_tokens))
+
+    def workspace_bytes(self, num_seqs: int, num_q_heads: int, max_context: int,
+                        partition_tokens: int = 0) -> int:
+        return int(self.lib.pa_decode_workspace_bytes(self.handle, num_seqs, num_q_heads,
+                                                      max_context, partition_tokens))
+
+    def decode(self, layer: int, q, scale: float, block_tables, context_lens, max_context: int,
+               out=None, partition_tokens: int = 0, req_ids=None, workspace=None, stream=None):
+        """Decode attention for q [B][Hq][D]; returns out fp32 [B][Hq][D]."""
+        import torch
+
+        assert self.k_cache is not None, "host-only pool"
+        b, hq, d = q.shape
+        assert q.is_cuda and q.is_contiguous() and q.dtype == self.torch_dtype and d == self.head_dim
+        assert context_lens.is_cuda and context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (b,)
+        stride = 0
+        if self.layout == "paged":
+            assert block_tables.is_cuda and block_tables.dtype == torch.int32
+            assert block_tables.is_contiguous() and block_tables.shape[0] == b
+            stride = int(block_tables.shape[1])
+        if req_ids is not None:
+            assert req_ids.is_cuda and req_ids.dtype == torch.int32 and tuple(req_ids.shape) == (b,)
+        if out is None:
+            out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
+        assert out.is_contiguous() and out.dtype == torch.float32 and tuple(out.shape) == (b, hq, d)
+        need = self.workspace_bytes(b, hq, max_context, partition_tokens)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        capi.check(self.lib.pa_decode(
+            self.handle, layer, q.data_ptr(), _DTYPES[self.kv_dtype], hq, float(scale),
+            block_tables.data_ptr() if self.layout == "paged" else None, stride,
+            req_ids.data_ptr() if req_ids is not None else None, context_lens.data_ptr(), b,
+            int(max_context), int(partition_tokens), out.data_ptr(), ws_ptr, ws_bytes,
+            _stream_handle(stream)), "pa_decode")
+        return out
