@@ -1,0 +1,358 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+One step = one decode iteration of the whole batch over every layer pool:
+  host  pa_reserve: one new token per sequence (allocate-on-fill, copy-on-write)
+  H2D   slots, block tables and context lengths (pinned, asynchronous)
+  GPU   pa_copy_blocks for any copy-on-write pairs
+        pa_append_kv for each layer (the new token's K/V)
+        pa_decode for each layer (paged attention; split-K merge if needed)
+NL distinct layer pools are rotated so that the 256 MB Infinity Cache cannot
+serve repeated reads.  Contexts grow by one token per step; the workload's
+prefill is set so that the timed steps are centred on the nominal context.
+
+Prints ONE JSON line: KV-read GB/s over the timed steps (metric), the decode
+kernels' roofline fraction from HIP events, and the CPU oracle's rate.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
+METRIC = "paged decode-attn KV GB/s (% of HBM peak), Llama-3-8B shape, batch 64"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = the metric's)")
+    ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"])
+    ap.add_argument("--prompt-len", type=int, default=0, help="workload 5: prompt length")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=0, help="layer pools rotated (0: workload's)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized buffer 3 times (calibrates byte counters)")
+    return ap.parse_args()
+
+
+def copy_probe(mib: int) -> None:
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
+class Bench:
+    """The workload built in device memory through libpa.so."""
+
+    def __init__(self, cfg, layout, num_layers, extra_steps, partition_tokens):
+        import torch
+
+        import workloads as W
+        from paged_kv_cache_241_amd import Pool
+
+        self.torch = torch
+        self.cfg = cfg
+        self.layout = layout
+        self.nl = num_layers
+        self.pt = partition_tokens
+        dev = torch.device("cuda")
+        self.dev = dev
+        pl = W.plan(cfg)
+        self.pl = pl
+        bs = cfg.block_size
+        headroom = len(pl.batch_handles) * (-(-extra_steps // bs) + 1)
+        nb = pl.num_blocks + headroom
+        self.max_seqs = 4096 if layout == "paged" else cfg.batch
+        self.pool = Pool(num_layers, nb, bs, cfg.num_kv_heads, cfg.head_dim, cfg.kv_dtype, layout,
+                         max_seqs=self.max_seqs, max_seq_len=cfg.max_seq_len, device=dev)
+        if layout == "paged":
+            order = np.concatenate([W.free_order(pl.num_blocks, cfg.seed),
+                                    np.arange(pl.num_blocks, nb, dtype=np.int32)])
+            self.pool.set_free_order(order)
+        # per-layer values; the prefill writes every layer through pa_append_kv
+        self.q, self.rows = [], []
+        for layer in range(num_layers):
+            q, kr, vr = W.values(cfg, pl, dev, layer=layer)
+            self.q.append(q)
+            self.rows.append((kr, vr))
+        self.length = {}
+        self.rids = {}
+
+        pool = self.pool
+
+        class Tracked:
+            def add(_):
+                r = pool.add()
+                self.length[r] = 0
+                return r
+
+            def fork(_, parent):
+                r = pool.fork(parent)
+                self.length[r] = self.length[parent]
+                return r
+
+            def free_seq(_, rid):
+                pool.free_seq(rid)
+                del self.length[rid]
+
+            def reserve(_, rids, counts):
+                out = pool.reserve(rids, counts)
+                for r, c in zip(rids, counts):
+                    self.length[r] += c
+                return out
+
+        W.run_ops(pl.ops, Tracked(), self.rids, on_reserve=self._prefill)
+        torch.cuda.synchronize()
+        for layer in range(num_layers):   # values no longer needed
+            self.rows[layer] = None
+        self.batch = [self.rids[h] for h in pl.batch_handles]
+        self.rids_np = np.array(self.batch, dtype=np.int32)
+        b = len(self.batch)
+        self.req_ids = torch.tensor(self.batch, dtype=torch.int32, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(cfg.seed + 99)
+        tdt = self.pool.torch_dtype
+        self.k_new = [torch.randn((b, cfg.num_kv_heads, cfg.head_dim), generator=g, device=dev).to(tdt)
+                      for _ in range(num_layers)]
+        self.v_new = [torch.randn((b, cfg.num_kv_heads, cfg.head_dim), generator=g, device=dev).to(tdt)
+                      for _ in range(num_layers)]
+        self.out = torch.empty((b, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+        self.max_context = cfg.max_seq_len   # sizes the workspace: enough for any step
+        self.stride = -(-cfg.max_seq_len // bs)
+        self.ws = None
+        self.scale = float(np.float32(1.0 / np.sqrt(cfg.head_dim)))
+
+    def _prefill(self, handles, counts, slots, pairs):
+        torch = self.torch
+        if len(pairs):
+            self.pool.copy_blocks(torch.from_numpy(np.ascontiguousarray(pairs)).to(self.dev))
+        idx, sl = [], []
+        k = 0
+        for h, c in zip(handles, counts):
+            r = self.rids[h]
+            p0 = self.length[r] - c
+            if h in self.pl.rows:
+                idx.extend(self.pl.rows[h][p0:p0 + c])
+                sl.extend(int(x) for x in slots[k:k + c])
+            k += c
+        if not idx:
+            return
+        it = torch.tensor(idx, dtype=torch.int64, device=self.dev)
+        st = torch.tensor(sl, dtype=torch.int32, device=self.dev)
+        for layer in range(self.nl):
+            kr, vr = self.rows[layer]
+            self.pool.append_kv(layer, kr.index_select(0, it).contiguous(),
+                                vr.index_select(0, it).contiguous(), st)
+
+    def step(self, ev=None):
+        """One decode iteration over all layers; returns the KV bytes it read."""
+        torch = self.torch
+        pool = self.pool
+        slots, pairs = pool.reserve(self.rids_np)
+        if self.layout == "paged":
+            tables, lens = pool.block_tables(self.rids_np, self.stride)
+            tables_d = torch.from_numpy(tables).pin_memory().to(self.dev, non_blocking=True)
+        else:
+            _, lens = pool.block_tables(self.rids_np, 1)
+            tables_d = None
+        lens_d = torch.from_numpy(lens).pin_memory().to(self.dev, non_blocking=True)
+        slots_d = torch.from_numpy(slots).pin_memory().to(self.dev, non_blocking=True)
+        if len(pairs):
+            pool.copy_blocks(torch.from_numpy(np.ascontiguousarray(pairs)).pin_memory()
+                             .to(self.dev, non_blocking=True))
+        for layer in range(self.nl):
+            pool.append_kv(layer, self.k_new[layer], self.v_new[layer], slots_d)
+        if self.ws is None:
+            need = pool.workspace_bytes(len(self.batch), self.cfg.num_q_heads, self.max_context, self.pt)
+            self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.dev)
+        if ev is not None:
+            ev[0].record()
+        max_context = int(lens.max())
+        for layer in range(self.nl):
+            pool.decode(layer, self.q[layer], self.scale, tables_d, lens_d, max_context,
+                        out=self.out, partition_tokens=self.pt, workspace=self.ws,
+                        req_ids=self.req_ids if self.layout != "paged" else None)
+        if ev is not None:
+            ev[1].record()
+        return lens.astype(np.int64)
+
+
+def kv_bytes(cfg, lens) -> int:
+    elt = 2 if cfg.kv_dtype == "bf16" else 4
+    return int(lens.sum()) * cfg.num_kv_heads * cfg.head_dim * elt * 2
+
+
+def algorithmic_bytes(cfg, lens) -> int:
+    """Bytes a decode launch must move: K/V, q, out, block-table entries, lengths."""
+    elt = 2 if cfg.kv_dtype == "bf16" else 4
+    b = len(lens)
+    tables = int(sum(-(-int(n) // cfg.block_size) for n in lens)) * 4
+    return (kv_bytes(cfg, lens) + b * cfg.num_q_heads * cfg.head_dim * (elt + 4) + tables + b * 4)
+
+
+def cpu_baseline(bench, seconds: float) -> dict:
+    """The oracle (fp64 gather + attend) on host cores over a bounded sample."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as A
+
+    cfg = bench.cfg
+    pool = bench.pool
+    with threadpool_limits(limits=1):
+        kc = pool.k_cache[0]
+        vc = pool.v_cache[0]
+        if cfg.kv_dtype == "bf16":
+            kb = kc.view(torch.int16).cpu().numpy().view(np.uint16)
+            vb = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+            conv = A.bf16_bits_to_f64
+        else:
+            kb = kc.cpu().numpy()
+            vb = vc.cpu().numpy()
+            conv = A.f32_to_f64
+        q = bench.q[0].float().cpu().numpy().astype(np.float64)
+        if bench.layout == "paged":
+            tables, lens = pool.block_tables(bench.rids_np, bench.stride)
+        else:
+            _, lens = pool.block_tables(bench.rids_np, 1)
+        done_bytes = 0
+        n = 0
+        t0 = time.perf_counter()
+        for i in range(1 << 30):
+            s = i % len(lens)
+            length = int(lens[s])
+            if bench.layout == "paged":
+                t = tables[s][: -(-length // cfg.block_size)]
+                k = A.gather_paged(conv(A.k_rows(kb[t])), range(len(t)), length, cfg.block_size)
+                v = A.gather_paged(conv(A.v_rows(vb[t])), range(len(t)), length, cfg.block_size)
+            else:
+                r = bench.batch[s]
+                per = cfg.max_seq_len // cfg.block_size
+                kr = A.contiguous_rows(conv(A.k_rows(kb[r * per:(r + 1) * per])), 1, cfg.max_seq_len)
+                vr = A.contiguous_rows(conv(A.v_rows(vb[r * per:(r + 1) * per])), 1, cfg.max_seq_len)
+                k = A.gather_contiguous(kr, 0, length)
+                v = A.gather_contiguous(vr, 0, length)
+            A.attend(q[s], k, v, bench.scale)
+            done_bytes += kv_bytes(cfg, np.array([length]))
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} sequence-decodes (cycling over the {len(lens)} sequences of one layer: "
+                      f"gather through the block table + fp64 attention), {dt:.1f} s, single thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is described, not built)"}))
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    import torch
+
+    import workloads as W
+
+    over = {}
+    if args.config == 5 and args.prompt_len:
+        over["prompt_len"] = args.prompt_len
+    base = W.get(args.config, **over)
+    nominal = base.context
+    if nominal:
+        # centre the timed steps on the nominal context
+        over["context"] = nominal - args.warmup - (args.steps - 1) // 2
+    cfg = W.get(args.config, **over)
+    nl = args.layers or cfg.num_layers
+    bench = Bench(cfg, args.layout, nl, args.warmup + args.steps + 1, args.partition_tokens)
+    for _ in range(args.warmup):
+        bench.step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    total_kv = 0
+    total_alg = 0
+    lens_seen = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        lens = bench.step(evs[i])
+        total_kv += kv_bytes(cfg, lens) * nl
+        total_alg += algorithmic_bytes(cfg, lens) * nl
+        lens_seen.append(float(lens.mean()))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dt = t1 - t0
+    decode_ms = sum(a.elapsed_time(b) for a, b in evs)
+    per_launch_s = decode_ms / 1e3 / (args.steps * nl)
+    achieved = total_alg / (args.steps * nl) / per_launch_s / 1e9
+    value = total_kv / dt / 1e9
+    b = len(bench.batch)
+    part = bench.pool.partition_tokens(b, int(max(lens)), args.partition_tokens)
+    stats = bench.pool.stats()
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name + ("" if args.layout == "paged" else ", contiguous reqId x S layout"),
+            "batch": b, "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": cfg.head_dim, "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
+            "mean_context_timed": round(float(np.mean(lens_seen)), 2),
+            "layers_rotated": nl, "partition_tokens": part, "layout": args.layout,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_us_per_layer": round(per_launch_s * 1e6, 3),
+        "decode_kv_gbs": round(total_kv / (args.steps * nl) / per_launch_s / 1e9, 2),
+        "tokens_per_s_per_layer": round(b / per_launch_s, 1),
+        "pool_utilisation": round(stats["utilisation"], 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode (decode_partition_kernel + decode_merge_kernel when split)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(bench, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -3,19 +3,23 @@
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Plain float64 NumPy;
 nothing is blocked, fused or reordered beyond the definitions below.
 
-Cache layout read by the gather functions (the pages fix no layout; this is the
-layout the C library documents for its pools):
+Cache layout.  The pages fix none; the C library documents this one, and the
+functions here read it as written there:
 
-* paged:      one array per layer and per K/V, shape ``[num_blocks][Hkv][BS][d]``.
-  Block ``b`` holds, for every KV head, BS consecutive token rows of d elements.
-* contiguous: one array per layer and per K/V, shape ``[max_seqs][Hkv][S][d]``.
-  Request ``r`` owns the sub-tensor that begins ``r * (Hkv*S*d)`` elements into
-  the array, i.e. at ``reqId x S`` where S is one request's maximum cache size
-  ([VAC] 5.2.3, request-level KV-cache indexing).
+* A layer's K (or V) cache is an array of tiles, one per (block, KV head):
+  shape ``[units][Hkv][tile]``.  The K tile is ``[d/VE][BS][VE]`` (the row of a
+  token cut into 16-byte chunks of ``VE`` elements, chunk-major), the V tile is
+  ``[d][BS]`` (dimension-major).  ``k_rows`` / ``v_rows`` turn tiles into plain
+  token rows ``[units][Hkv][BS][d]``, which is what the gathers read.
+* paged: ``units`` are the physical blocks; block ``b`` holds BS consecutive
+  token rows of every KV head.
+* contiguous: request ``r`` owns the ``S/BS`` consecutive blocks starting at
+  block ``r*S/BS``, i.e. the sub-tensor at ``reqId x S`` where S is one
+  request's maximum cache size ([VAC] 5.2.3, request-level KV-cache indexing).
+  ``contiguous_rows`` views that as ``[max_seqs][Hkv][S][d]``.
 
-A "slot" names one token row: ``slot = u*U + o`` with ``U = BS`` (paged: ``u`` is
-the physical block, ``o`` the row inside it) or ``U = S`` (contiguous: ``u`` is
-the reqId, ``o`` the token position).
+A "slot" names one token row: ``slot = u*BS + o`` (``u`` the block, ``o`` the row
+inside it); in the contiguous layout that is ``reqId*S + position``.
 """
 
 from __future__ import annotations
@@ -49,6 +53,35 @@ def f32_to_f64(x: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# reading the documented tile layout
+# --------------------------------------------------------------------------
+
+def k_rows(k_tiles: np.ndarray) -> np.ndarray:
+    """K tiles ``[..., d/VE, BS, VE]`` as token rows ``[..., BS, d]``.
+
+    Element (row o, dim e) of a tile is chunk ``e // VE``, row ``o``, lane
+    ``e % VE``.
+    """
+    *lead, nq, bs, ve = k_tiles.shape
+    return np.swapaxes(k_tiles, -3, -2).reshape(*lead, bs, nq * ve)
+
+
+def v_rows(v_tiles: np.ndarray) -> np.ndarray:
+    """V tiles ``[..., d, BS]`` as token rows ``[..., BS, d]``."""
+    return np.swapaxes(v_tiles, -1, -2)
+
+
+def contiguous_rows(rows: np.ndarray, max_seqs: int, max_len: int) -> np.ndarray:
+    """Token rows ``[max_seqs*S/BS][Hkv][BS][d]`` of a contiguous cache as
+    ``[max_seqs][Hkv][S][d]``: request r's blocks, in order, are its tokens."""
+    units, hkv, bs, d = rows.shape
+    assert units == max_seqs * (max_len // bs)
+    per = max_len // bs
+    return rows.reshape(max_seqs, per, hkv, bs, d).transpose(0, 2, 1, 3, 4).reshape(
+        max_seqs, hkv, max_len, d)
+
+
+# --------------------------------------------------------------------------
 # gather ([ROC] paging paragraph and Terms: block table; [PAS] Summary)
 # --------------------------------------------------------------------------
 
@@ -77,8 +110,8 @@ def gather_contiguous(pool: np.ndarray, req_id: int, length: int) -> np.ndarray:
     """Logical K (or V) of one request in a per-request contiguous layout.
 
     Request ``req_id`` owns the non-overlapping sub-tensor at offset
-    ``reqId x S`` of the layer's tensor ([VAC] 5.2.3); inside it the token at
-    position ``t`` of KV head ``h`` is row ``t`` of head ``h``.
+    ``reqId x S`` of the layer's tensor ([VAC] 5.2.3); in this per-request
+    view the token at position ``t`` of KV head ``h`` is row ``t`` of head ``h``.
 
     pool:   ``[max_seqs][Hkv][S][d]``
     return: ``[length][Hkv][d]`` float64
@@ -201,10 +234,10 @@ def append_scatter(pool: np.ndarray, slots, new_rows: np.ndarray) -> np.ndarray:
 
     Each decode iteration adds exactly one token to every running request
     ([KVP] Observation-1); its K (or V) row goes to the slot the allocator gave
-    it.  ``pool`` is ``[units][Hkv][U][d]`` of raw values (any dtype, compared
-    bytewise by callers), ``new_rows`` is ``[n][Hkv][d]`` of the same dtype and
-    ``slots[i] = u*U + o``; a negative slot means "skip this row".  Returns a
-    new array; the input is not modified.
+    it.  ``pool`` is token rows ``[units][Hkv][BS][d]`` of raw values (any
+    dtype, compared bytewise by callers), ``new_rows`` is ``[n][Hkv][d]`` of the
+    same dtype and ``slots[i] = u*BS + o``; a negative slot means "skip this
+    row".  Returns a new array; the input is not modified.
     """
     out = np.array(pool, copy=True)
     units, hkv, unit, d = out.shape
@@ -222,7 +255,8 @@ def copy_blocks(pool: np.ndarray, pairs) -> np.ndarray:
     """Pool after the copy-on-write copies: block ``dst`` takes block ``src``'s rows.
 
     Shared blocks are copied only when one of the sharers writes ([PAS] Summary,
-    [ROC] "Fragmentation is lost users").  ``pool`` is ``[NB][Hkv][BS][d]``.
+    [ROC] "Fragmentation is lost users").  ``pool`` is ``[NB][...]`` (rows or
+    tiles: a block is copied whole).
     """
     out = np.array(pool, copy=True)
     for src, dst in pairs:

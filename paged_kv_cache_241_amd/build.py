@@ -18,9 +18,12 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-# Packed-FP32 instructions are left to no one: the compiler must not form them.
+# Packed-FP32 instructions are not formed (-packed-fp32-ops).  MFMA operands
+# and results stay in ordinary VGPRs (no copies to and from AGPRs around the
+# accumulator's VALU rescale).
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wall", "-Wno-unused-function"]
 HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall"]
 

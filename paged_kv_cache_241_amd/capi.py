@@ -11,7 +11,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PAGED_KV_LIB names another build of the same library (e.g. one compiled
+# with different tuning constants); by default the in-tree build is used.
+LIB_PATH = os.environ.get("PAGED_KV_LIB") or os.path.join(_HERE, "libpa.so")
 
 PA_OK = 0
 PA_ERR_INVALID_ARG = -1

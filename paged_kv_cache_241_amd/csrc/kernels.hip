@@ -18,14 +18,20 @@
 //
 // Decode design (the pages give no kernel; this one is built for gfx950):
 //   * one 256-thread workgroup (4 waves of 64) per (sequence, KV head, context
-//     partition); the G query heads of the GQA group share every K/V load;
-//   * waves take the partition's blocks round-robin; each (block, head) is
-//     BS rows of head_dim elements, contiguous in memory, read with coalesced
-//     16-byte loads: a row is LPR lanes, a wave instruction covers RPI rows;
-//   * q.k: bf16 pairs through v_dot2_f32_bf16 (fp32 FMAs for fp32 caches),
-//     then a butterfly over the LPR lanes of the row with DPP (quad_perm,
-//     row_half_mirror, row_mirror) so every lane holds the same fp32 score;
-//   * online softmax in fp32 with exp2 on pre-scaled scores; p*V in fp32;
+//     partition); the G <= 16 query heads of the GQA group share every K/V
+//     load; waves take the partition's 16-token chunks round-robin;
+//   * per chunk, S = K q^T is one 16x16 MFMA tile (16 tokens x 16 head
+//     columns, the unused columns hold zero queries): bf16 caches use
+//     v_mfma_f32_16x16x32_bf16 over head_dim/32 steps, fp32 caches
+//     v_mfma_f32_16x16x4_f32 over head_dim/4 steps.  The lane that holds
+//     S[token 4j+i][head n] is exactly the lane the P V MFMA wants P[head n]
+//     [token 4j+i] in, so the softmax weights never move between lanes;
+//   * online softmax in fp32 (exp2 on pre-scaled scores), one running max per
+//     head; P V: bf16 caches split each weight into a bf16 high and low part
+//     (two v_mfma_f32_16x16x16_bf16 per 16x16 output tile, weights exact to
+//     ~2^-17), fp32 caches multiply fp32 weights with v_mfma_f32_16x16x4_f32;
+//   * the tile formats make every operand load one contiguous wave access:
+//     K chunks [D/VE][BS][VE] give 1 KiB per load, V [D][BS] 512 B (bf16);
 //   * waves merge through LDS in a fixed order; partitions are merged by a
 //     second small kernel in partition order.  Every reduction order depends
 //     only on logical token positions, so results do not depend on which
@@ -34,6 +40,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -44,7 +51,14 @@ constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kMergeThreads = 64;
+constexpr int kChunk = 16;        // tokens per MFMA tile
+constexpr int kMaxGroup = 16;     // query heads per KV head the tile can hold
 constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 // Workgroups of a launch are dealt to the 8 XCDs round-robin by id.  Give
 // each XCD one contiguous range of work items so that neighbours (partitions
@@ -58,121 +72,48 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// DPP lane exchange inside a 16-lane row.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+// lane ^ 16 and lane ^ 32
+__device__ __forceinline__ float xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (16 << 10)));
 }
-constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kRowMirror = 0x140;     // lane i <- 15-i
-constexpr int kRowHalfMirror = 0x141; // lane i <- 7-i within each half row
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
-// lane ^ M for M in {8, 16} (ds_swizzle bit mode, within 32 lanes) or 32.
-template <int M>
-__device__ __forceinline__ float lane_xor(float x) {
-  if constexpr (M < 32) {
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (M << 10)));
-  } else {
-    return __shfl_xor(x, 32);
-  }
-}
+__device__ __forceinline__ uint4 ld16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint2 ld8(const char* p) { return *reinterpret_cast<const uint2*>(p); }
 
-// Sum over the LPR consecutive lanes of a token row; every lane of the row
-// ends with the same bits (each step adds two equal-valued halves).
-template <int LPR>
-__device__ __forceinline__ float row_sum(float x) {
-  if constexpr (LPR >= 2) x += dpp<kQuadXor1>(x);
-  if constexpr (LPR >= 4) x += dpp<kQuadXor2>(x);
-  if constexpr (LPR >= 8) x += dpp<kRowHalfMirror>(x);
-  if constexpr (LPR >= 16) x += dpp<kRowMirror>(x);
-  if constexpr (LPR >= 32) x += lane_xor<16>(x);
-  return x;
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Combine the RPI rows of a wave (lanes that differ by multiples of LPR).
-template <int LPR>
-__device__ __forceinline__ float rows_sum(float x) {
-  if constexpr (LPR <= 8) x += lane_xor<8>(x);
-  if constexpr (LPR <= 16) x += lane_xor<16>(x);
-  if constexpr (LPR <= 32) x += lane_xor<32>(x);
-  return x;
-}
-template <int LPR>
-__device__ __forceinline__ float rows_max(float x) {
-  if constexpr (LPR <= 8) x = fmaxf(x, lane_xor<8>(x));
-  if constexpr (LPR <= 16) x = fmaxf(x, lane_xor<16>(x));
-  if constexpr (LPR <= 32) x = fmaxf(x, lane_xor<32>(x));
-  return x;
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(bf16x2_t, w);
-}
-
-// <q, k> over one 16-byte chunk.
-template <int KIND>
-__device__ __forceinline__ float dot16(const uint4& q, const uint4& k) {
-  if constexpr (KIND == kBF16) {
-    float x = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.x), as_bf16x2(k.x), 0.0f, false);
-    x = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.y), as_bf16x2(k.y), x, false);
-    x = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.z), as_bf16x2(k.z), x, false);
-    x = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w), as_bf16x2(k.w), x, false);
-    return x;
-  } else {
-    float x = __uint_as_float(q.x) * __uint_as_float(k.x);
-    x = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), x);
-    x = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), x);
-    x = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), x);
-    return x;
-  }
-}
-
-// 16-byte chunk to fp32 values (exact).
-template <int KIND, int VE>
-__device__ __forceinline__ void unpack(const uint4& v, float (&f)[VE]) {
-  if constexpr (KIND == kBF16) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      f[2 * k] = __uint_as_float(w[k] << 16);
-      f[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-    }
-  } else {
-    f[0] = __uint_as_float(v.x);
-    f[1] = __uint_as_float(v.y);
-    f[2] = __uint_as_float(v.z);
-    f[3] = __uint_as_float(v.w);
-  }
-}
-
-__device__ __forceinline__ uint4 ld16(const char* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
+template <int KIND, int D, int BS>
+struct Geo {
+  static constexpr int ELT = KIND == kBF16 ? 2 : 4;
+  static constexpr int VE = 16 / ELT;          // elements per 16-byte K chunk
+  static constexpr int NX = D / (4 * VE);      // 16-byte K loads per lane per chunk
+  static constexpr int NN = D / 16;            // 16-column output tiles
+  static constexpr int TILE = D * BS * ELT;    // bytes of one (block, head) tile
+};
 
 // ---------------------------------------------------------------------------
 // decode: one workgroup per (sequence, KV head, partition)
 // ---------------------------------------------------------------------------
-template <int KIND, int D, int BS, int G>
+template <int KIND, int D, int BS>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
-  constexpr int ELT = KIND == kBF16 ? 2 : 4;
-  constexpr int VE = 16 / ELT;      // elements per 16-byte chunk
-  constexpr int LPR = D / VE;       // lanes per token row
-  constexpr int RPI = kWave / LPR;  // token rows per wave instruction
-  constexpr int NI = BS / RPI;      // wave instructions per block
-  constexpr int ROW = D * ELT;      // bytes per (token, head) row
-  constexpr int BLK = BS * ROW;     // bytes per (block, head)
-  static_assert(LPR * VE == D && RPI * LPR == kWave && NI * RPI == BS && NI >= 1, "shape");
+  using GG = Geo<KIND, D, BS>;
+  constexpr int NX = GG::NX, NN = GG::NN, TILE = GG::TILE, ELT = GG::ELT;
+  // V operand per lane per output tile: 4 consecutive tokens of one dim
+  using VOp = typename std::conditional<KIND == kBF16, uint2, uint4>::type;
 
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-  __shared__ float sm_acc[kWaves][G][D];
+  __shared__ float sm_m[kWaves][kMaxGroup];
+  __shared__ float sm_l[kWaves][kMaxGroup];
+  __shared__ float sm_acc[kWaves][kMaxGroup][D];
 
   const int P = a.num_partitions;
   const int hkv = geo.num_kv_heads;
+  const int G = a.num_q_heads / hkv;
   const int work = xcd_remap(blockIdx.x, gridDim.x);
   const int part = work % P;
   const int sk = work / P;
@@ -182,10 +123,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(CacheGeom ge
   const int h0 = kvh * G;
 
   const int L = a.lens[s];
-  const int nblk = (L + BS - 1) / BS;
-  const int jb = part * a.partition_blocks;
-  const int je = min(nblk, jb + a.partition_blocks);
-  if (jb >= je) {
+  const int nch = (L + kChunk - 1) / kChunk;
+  const int cb = part * a.partition_chunks;
+  const int ce = min(nch, cb + a.partition_chunks);
+  if (cb >= ce) {
     if (P == 1) {  // empty context: zero output
       float* o = a.out + (static_cast<int64_t>(s) * a.num_q_heads + h0) * D;
       for (int e = tid; e < G * D; e += kThreads) o[e] = 0.0f;
@@ -195,133 +136,204 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(CacheGeom ge
 
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int r = lane / LPR;
-  const int c = lane % LPR;
+  const int n = lane & 15;   // head column of S / row of the K tile
+  const int j4 = lane >> 4;  // lane group: tokens 4*j4 .. 4*j4+3
 
-  uint4 qv[G];
+  // q operand: head n of the group, zero beyond G (the row address is
+  // clamped to a head of this group so that it always exists)
+  uint4 qop[NX];
   {
+    const int hq = h0 + min(n, G - 1);
     const char* qb = static_cast<const char*>(a.q) +
-                     (static_cast<int64_t>(s) * a.num_q_heads + h0) * ROW + c * 16;
+                     ((static_cast<int64_t>(s) * a.num_q_heads + hq) * D) * ELT;
 #pragma unroll
-    for (int g = 0; g < G; ++g) qv[g] = ld16(qb + g * ROW);
+    for (int x = 0; x < NX; ++x) {
+      const uint4 w = ld16(qb + (x * 4 + j4) * 16);
+      qop[x] = n < G ? w : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
   const float c2 = a.scale * kLog2e;
 
-  const char* kl = geo.k_base + static_cast<int64_t>(a.layer) * geo.layer_bytes + r * ROW + c * 16;
-  const char* vl = geo.v_base + static_cast<int64_t>(a.layer) * geo.layer_bytes + r * ROW + c * 16;
+  const char* kl = geo.k_base + static_cast<int64_t>(a.layer) * geo.layer_bytes;
+  const char* vl = geo.v_base + static_cast<int64_t>(a.layer) * geo.layer_bytes;
   const int32_t* table = nullptr;
-  int64_t seq_off = 0;
+  int64_t first_block = 0;
   if (geo.paged) {
     table = a.tables + static_cast<int64_t>(s) * a.table_stride;
   } else {
     const int rid = a.req_ids ? a.req_ids[s] : s;
-    seq_off = (static_cast<int64_t>(rid) * hkv + kvh) * geo.unit * ROW;
+    first_block = static_cast<int64_t>(rid) * geo.blocks_per_seq;
   }
-  auto block_off = [&](int j) -> int64_t {
-    if (geo.paged) return (static_cast<int64_t>(table[j]) * hkv + kvh) * BLK;
-    return seq_off + static_cast<int64_t>(j) * BLK;
+  // byte offset of tile (block of token t, kvh); t is clamped into the
+  // context so that every address stays inside a block the sequence owns
+  auto tile_of = [&](int t) -> int64_t {
+    t = min(t, L - 1);
+    const int64_t u = geo.paged ? static_cast<int64_t>(table[t / BS]) : first_block + t / BS;
+    return (u * hkv + kvh) * TILE;
   };
 
-  float m[G], lsum[G], acc[G][VE];
+  float m = -INFINITY;  // running max of head n (log2 units)
+  float lsum = 0.0f;    // this lane's share of head n's weight sum
+  floatx4_t acc[NN];    // acc[nb][i] = O[head 4*j4+i][dim nb*16+n]
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    lsum[g] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
-  }
+  for (int nb = 0; nb < NN; ++nb) acc[nb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  uint4 kr[NI], vr[NI];
-  int j = jb + wave;
-  if (j < je) {
-    const int64_t off = block_off(j);
+  uint4 kop[NX];
+  VOp vop[NN];
+  auto load = [&](int c, uint4 (&kk)[NX], VOp (&vv)[NN]) {
+    if constexpr (BS >= kChunk) {
+      // the chunk lies in one block: a wave-uniform tile base plus a 32-bit
+      // lane offset (rows past the context stay inside the tile)
+      const int blk = (c * kChunk) / BS;
+      const int64_t u = geo.paged ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(table[blk]))
+                                  : first_block + blk;
+      const int64_t tile = (u * hkv + kvh) * TILE;
+      const char* kt = kl + tile;
+      const char* vt = vl + tile;
+      const int row0 = (c * kChunk) % BS;
+      const uint32_t ko = static_cast<uint32_t>((j4 * BS + row0 + n) * 16);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      kr[i] = ld16(kl + off + i * RPI * ROW);
-      vr[i] = ld16(vl + off + i * RPI * ROW);
-    }
-  }
-  while (j < je) {
-    const int jn = j + kWaves;
-    uint4 kn[NI], vn[NI];
-    if (jn < je) {
-      const int64_t off = block_off(jn);
+      for (int x = 0; x < NX; ++x) kk[x] = ld16(kt + ko + x * 4 * BS * 16);
+      const uint32_t vo = static_cast<uint32_t>((n * BS + row0 + 4 * j4) * ELT);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        kn[i] = ld16(kl + off + i * RPI * ROW);
-        vn[i] = ld16(vl + off + i * RPI * ROW);
+      for (int nb = 0; nb < NN; ++nb) {
+        if constexpr (KIND == kBF16) vv[nb] = ld8(vt + vo + nb * 16 * BS * ELT);
+        else vv[nb] = ld16(vt + vo + nb * 16 * BS * ELT);
+      }
+    } else {
+      // blocks shorter than a chunk: each lane finds its own block
+      const int tk = c * kChunk + n;
+      const char* kt = kl + tile_of(tk) + (tk % BS) * 16;
+#pragma unroll
+      for (int x = 0; x < NX; ++x) kk[x] = ld16(kt + (x * 4 + j4) * BS * 16);
+      int tv = c * kChunk + 4 * j4;
+      tv = min(tv, ((L - 1) / 4) * 4);
+      const char* vt = vl + tile_of(tv) + (tv % BS) * ELT;
+#pragma unroll
+      for (int nb = 0; nb < NN; ++nb) {
+        if constexpr (KIND == kBF16) vv[nb] = ld8(vt + (nb * 16 + n) * BS * ELT);
+        else vv[nb] = ld16(vt + (nb * 16 + n) * BS * ELT);
       }
     }
-    // scores of this lane's rows, pre-scaled to log2 units
-    float sc[NI][G];
+  };
+
+  int c = cb + wave;
+  if (c < ce) load(c, kop, vop);
+  while (c < ce) {
+    const int cn = c + kWaves;
+    uint4 kn[NX];
+    VOp vn[NN];
+    // always issue the next chunk's loads (the last iteration re-reads a chunk
+    // of this partition): a branch here would make the wait for the current
+    // chunk also wait for these
+    load(min(cn, ce - 1), kn, vn);
+
+    // S[token 4*j4+i][head n]
+    floatx4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int g = 0; g < G; ++g) sc[i][g] = row_sum<LPR>(dot16<KIND>(qv[g], kr[i])) * c2;
-    const int t0 = j * BS + r;
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if (t0 + i * RPI >= L)
-#pragma unroll
-        for (int g = 0; g < G; ++g) sc[i][g] = -INFINITY;
-    // online softmax update
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float bm = sc[0][g];
-#pragma unroll
-      for (int i = 1; i < NI; ++i) bm = fmaxf(bm, sc[i][g]);
-      bm = rows_max<LPR>(bm);
-      const float mn = fmaxf(m[g], bm);
-      const float alpha = fexp2(m[g] - mn);
-      m[g] = mn;
-      lsum[g] *= alpha;
-#pragma unroll
-      for (int e = 0; e < VE; ++e) acc[g][e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const float p = fexp2(sc[i][g] - mn);
-        sc[i][g] = p;
-        lsum[g] += p;
+    for (int x = 0; x < NX; ++x) {
+      if constexpr (KIND == kBF16) {
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[x]),
+                                                    __builtin_bit_cast(bf16x8_t, qop[x]), S, 0, 0, 0);
+      } else {
+        S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kop[x].x), __uint_as_float(qop[x].x), S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kop[x].y), __uint_as_float(qop[x].y), S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kop[x].z), __uint_as_float(qop[x].z), S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kop[x].w), __uint_as_float(qop[x].w), S, 0, 0, 0);
       }
     }
-    // p * V
+    float sc[4];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float vf[VE];
-      unpack<KIND, VE>(vr[i], vf);
+    for (int i = 0; i < 4; ++i) sc[i] = S[i] * c2;
+    const int t0 = c * kChunk + 4 * j4;
+    if ((c + 1) * kChunk > L) {
+      // last, partly filled chunk: rows past the context hold whatever the
+      // cache held (possibly NaN or Inf patterns): zero weight and zero V
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int i = 0; i < 4; ++i)
+        if (t0 + i >= L) sc[i] = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(sc[i][g], vf[e], acc[g][e]);
+      for (int nb = 0; nb < NN; ++nb) {
+        if constexpr (KIND == kBF16) {
+          const uint32_t m0 = t0 + 0 < L ? 0x0000FFFFu : 0u, m1 = t0 + 1 < L ? 0xFFFF0000u : 0u;
+          const uint32_t m2 = t0 + 2 < L ? 0x0000FFFFu : 0u, m3 = t0 + 3 < L ? 0xFFFF0000u : 0u;
+          vop[nb].x &= (m0 | m1);
+          vop[nb].y &= (m2 | m3);
+        } else {
+          if (t0 + 0 >= L) vop[nb].x = 0u;
+          if (t0 + 1 >= L) vop[nb].y = 0u;
+          if (t0 + 2 >= L) vop[nb].z = 0u;
+          if (t0 + 3 >= L) vop[nb].w = 0u;
+        }
+      }
     }
-    j = jn;
+    // online softmax for head n
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, xor16(mx));
+    mx = fmaxf(mx, xor32(mx));
+    const float mn = fmaxf(m, mx);
+    const float alpha = fexp2(m - mn);
+    m = mn;
+    float p[4];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      kr[i] = kn[i];
-      vr[i] = vn[i];
+    for (int i = 0; i < 4; ++i) p[i] = fexp2(sc[i] - mn);
+    if (__any(alpha != 1.0f)) {
+      // rows of acc belong to heads 4*j4+i: fetch their factors
+      float ai[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j4 + i);
+#pragma unroll
+      for (int nb = 0; nb < NN; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[nb][i] *= ai[i];
     }
+    if constexpr (KIND == kBF16) {
+      // weight = high + low, both bf16; the sum is what the MFMA multiplies
+      uint32_t hi01 = pack_bf16(p[0], p[1]), hi23 = pack_bf16(p[2], p[3]);
+      const float h0f = bf16_lo(hi01), h1f = bf16_hi(hi01), h2f = bf16_lo(hi23), h3f = bf16_hi(hi23);
+      const float r0 = p[0] - h0f, r1 = p[1] - h1f, r2 = p[2] - h2f, r3 = p[3] - h3f;
+      uint32_t lo01 = pack_bf16(r0, r1), lo23 = pack_bf16(r2, r3);
+      lsum = lsum * alpha + (((h0f + bf16_lo(lo01)) + (h1f + bf16_hi(lo01))) +
+                             ((h2f + bf16_lo(lo23)) + (h3f + bf16_hi(lo23))));
+      const short4_t phi = __builtin_bit_cast(short4_t, make_uint2(hi01, hi23));
+      const short4_t plo = __builtin_bit_cast(short4_t, make_uint2(lo01, lo23));
+#pragma unroll
+      for (int nb = 0; nb < NN; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, __builtin_bit_cast(short4_t, vop[nb]),
+                                                           acc[nb], 0, 0, 0);
+#pragma unroll
+      for (int nb = 0; nb < NN; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, __builtin_bit_cast(short4_t, vop[nb]),
+                                                           acc[nb], 0, 0, 0);
+    } else {
+      lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+      for (int nb = 0; nb < NN; ++nb) {
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[0], __uint_as_float(vop[nb].x), acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[1], __uint_as_float(vop[nb].y), acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[2], __uint_as_float(vop[nb].z), acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[3], __uint_as_float(vop[nb].w), acc[nb], 0, 0, 0);
+      }
+    }
+    c = cn;
+#pragma unroll
+    for (int x = 0; x < NX; ++x) kop[x] = kn[x];
+#pragma unroll
+    for (int nb = 0; nb < NN; ++nb) vop[nb] = vn[nb];
   }
 
-  // combine the rows of the wave, then the waves of the workgroup
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    lsum[g] = rows_sum<LPR>(lsum[g]);
-#pragma unroll
-    for (int e = 0; e < VE; ++e) acc[g][e] = rows_sum<LPR>(acc[g][e]);
+  // weight sum of head n over the wave's tokens, then merge the waves
+  lsum += xor16(lsum);
+  lsum += xor32(lsum);
+  if (j4 == 0 && n < G) {
+    sm_m[wave][n] = m;
+    sm_l[wave][n] = lsum;
   }
-  if (lane < LPR) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+  for (int nb = 0; nb < NN; ++nb)
 #pragma unroll
-      for (int e = 0; e < VE; ++e) sm_acc[wave][g][c * VE + e] = acc[g][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      sm_m[wave][g] = m[g];
-      sm_l[wave][g] = lsum[g];
-    }
-  }
+    for (int i = 0; i < 4; ++i)
+      if (4 * j4 + i < G) sm_acc[wave][4 * j4 + i][nb * 16 + n] = acc[nb][i];
   __syncthreads();
   const int64_t row0 = static_cast<int64_t>(s) * a.num_q_heads + h0;
   for (int idx = tid; idx < G * D; idx += kThreads) {
@@ -352,12 +364,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(CacheGeom ge
 
 // Merge context partitions in partition order: one workgroup per (seq, q head).
 template <int D>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a, int block_size) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
   const int sh = blockIdx.x;
   const int s = sh / a.num_q_heads;
   const int P = a.num_partitions;
   const int L = a.lens[s];
-  const int tp = a.partition_blocks * block_size;
+  const int tp = a.partition_chunks * kChunk;
   const int ps = (L + tp - 1) / tp;
   const float* ml = a.ws + static_cast<int64_t>(sh) * P * 2;
   const float* accp = a.ws + static_cast<int64_t>(a.num_seqs) * a.num_q_heads * P * 2 +
@@ -383,27 +395,46 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 // ---------------------------------------------------------------------------
 // append and copy-on-write copies
 // ---------------------------------------------------------------------------
+// One thread per (token, KV head, 16-byte chunk of the row): the K chunk is
+// stored whole, the V chunk's elements go to their dims' rows of the V tile.
 __global__ __launch_bounds__(256) void append_kv_kernel(CacheGeom g, int32_t layer,
                                                         const uint4* __restrict__ k,
                                                         const uint4* __restrict__ v,
                                                         const int32_t* __restrict__ slots,
                                                         int32_t n) {
-  const int chunks = g.head_dim * g.elt / 16;
+  const int ve = 16 / g.elt;
+  const int chunks = g.head_dim / ve;
   const int per_tok = g.num_kv_heads * chunks;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= static_cast<int64_t>(n) * per_tok) return;
   const int i = static_cast<int>(idx / per_tok);
   const int rem = static_cast<int>(idx % per_tok);
-  const int h = rem / chunks, ch = rem % chunks;
+  const int h = rem / chunks, q = rem % chunks;
   const int slot = slots[i];
   if (slot < 0) return;
-  const int u = slot / g.unit, o = slot % g.unit;
-  const int64_t dst = static_cast<int64_t>(layer) * g.layer_bytes +
-                      ((static_cast<int64_t>(u) * g.num_kv_heads + h) * g.unit + o) *
-                          (static_cast<int64_t>(g.head_dim) * g.elt) +
-                      ch * 16;
-  *reinterpret_cast<uint4*>(g.k_base + dst) = k[idx];
-  *reinterpret_cast<uint4*>(g.v_base + dst) = v[idx];
+  const int64_t u = slot / g.block_size;
+  const int o = slot % g.block_size;
+  const int64_t tile = static_cast<int64_t>(layer) * g.layer_bytes +
+                       (u * g.num_kv_heads + h) * (static_cast<int64_t>(g.head_dim) * g.block_size * g.elt);
+  *reinterpret_cast<uint4*>(g.k_base + tile + (static_cast<int64_t>(q) * g.block_size + o) * 16) = k[idx];
+  const uint4 w = v[idx];
+  char* vt = g.v_base + tile;
+  const int d0 = q * ve;
+  if (g.elt == 2) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      *reinterpret_cast<uint16_t*>(vt + ((d0 + 2 * e) * g.block_size + o) * 2) =
+          static_cast<uint16_t>(ws[e] & 0xFFFFu);
+      *reinterpret_cast<uint16_t*>(vt + ((d0 + 2 * e + 1) * g.block_size + o) * 2) =
+          static_cast<uint16_t>(ws[e] >> 16);
+    }
+  } else {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      *reinterpret_cast<uint32_t*>(vt + ((d0 + e) * g.block_size + o) * 4) = ws[e];
+  }
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CacheGeom g,
@@ -423,41 +454,24 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CacheGeom g,
   }
 }
 
-template <int KIND, int D, int BS, int G>
+template <int KIND, int D, int BS>
 hipError_t launch_decode_t(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
   const int64_t nwork = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
-  hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, G>), dim3(static_cast<uint32_t>(nwork)),
+  hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS>), dim3(static_cast<uint32_t>(nwork)),
                      dim3(kThreads), 0, st, g, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(static_cast<uint32_t>(a.num_seqs) * a.num_q_heads),
-                     dim3(kMergeThreads), 0, st, a, g.block_size);
+                     dim3(kMergeThreads), 0, st, a);
   return hipGetLastError();
 }
 
-template <int KIND, int D, int BS>
-hipError_t launch_decode_g(const CacheGeom& g, const DecodeArgs& a, int G, bool* ok,
-                           hipStream_t st) {
-  switch (G) {
-    case 1: return launch_decode_t<KIND, D, BS, 1>(g, a, st);
-    case 2: return launch_decode_t<KIND, D, BS, 2>(g, a, st);
-    case 3: return launch_decode_t<KIND, D, BS, 3>(g, a, st);
-    case 4: return launch_decode_t<KIND, D, BS, 4>(g, a, st);
-    case 5: return launch_decode_t<KIND, D, BS, 5>(g, a, st);
-    case 6: return launch_decode_t<KIND, D, BS, 6>(g, a, st);
-    case 7: return launch_decode_t<KIND, D, BS, 7>(g, a, st);
-    case 8: return launch_decode_t<KIND, D, BS, 8>(g, a, st);
-    default: *ok = false; return hipSuccess;
-  }
-}
-
 template <int KIND, int D>
-hipError_t launch_decode_bs(const CacheGeom& g, const DecodeArgs& a, int G, bool* ok,
-                            hipStream_t st) {
+hipError_t launch_decode_bs(const CacheGeom& g, const DecodeArgs& a, bool* ok, hipStream_t st) {
   switch (g.block_size) {
-    case 8: return launch_decode_g<KIND, D, 8>(g, a, G, ok, st);
-    case 16: return launch_decode_g<KIND, D, 16>(g, a, G, ok, st);
-    case 32: return launch_decode_g<KIND, D, 32>(g, a, G, ok, st);
+    case 8: return launch_decode_t<KIND, D, 8>(g, a, st);
+    case 16: return launch_decode_t<KIND, D, 16>(g, a, st);
+    case 32: return launch_decode_t<KIND, D, 32>(g, a, st);
     default: *ok = false; return hipSuccess;
   }
 }
@@ -486,11 +500,14 @@ hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool
                          hipStream_t stream) {
   *supported = true;
   if (a.num_seqs <= 0) return hipSuccess;
-  const int G = a.num_q_heads / g.num_kv_heads;
-  if (kind == kBF16 && g.head_dim == 128) return launch_decode_bs<kBF16, 128>(g, a, G, supported, stream);
-  if (kind == kBF16 && g.head_dim == 64) return launch_decode_bs<kBF16, 64>(g, a, G, supported, stream);
-  if (kind == kF32 && g.head_dim == 128) return launch_decode_bs<kF32, 128>(g, a, G, supported, stream);
-  if (kind == kF32 && g.head_dim == 64) return launch_decode_bs<kF32, 64>(g, a, G, supported, stream);
+  if (a.num_q_heads / g.num_kv_heads > kMaxGroup) {
+    *supported = false;
+    return hipSuccess;
+  }
+  if (kind == kBF16 && g.head_dim == 128) return launch_decode_bs<kBF16, 128>(g, a, supported, stream);
+  if (kind == kBF16 && g.head_dim == 64) return launch_decode_bs<kBF16, 64>(g, a, supported, stream);
+  if (kind == kF32 && g.head_dim == 128) return launch_decode_bs<kF32, 128>(g, a, supported, stream);
+  if (kind == kF32 && g.head_dim == 64) return launch_decode_bs<kF32, 64>(g, a, supported, stream);
   *supported = false;
   return hipSuccess;
 }

@@ -10,8 +10,14 @@ namespace pa {
 
 enum Kind : int { kF32 = 0, kBF16 = 1 };
 
-// Token-row addressing shared by append and decode: a slot u*U + o of a layer
-// sits at ((u*num_kv_heads + h)*U + o)*head_dim elements from the layer base.
+// Cache geometry.  Per layer, K and V are arrays of tiles, one tile per
+// (block, KV head):
+//   K tile [head_dim/VE][block_size][VE]  (16-byte chunks, VE = 16/elt)
+//   V tile [head_dim][block_size]
+// Tile (u, h) starts at (u*num_kv_heads + h) * tile_bytes from the layer base.
+// Paged: u is the physical block.  Contiguous: request r owns blocks
+// r*blocks_per_seq .. r*blocks_per_seq + blocks_per_seq - 1.  A slot is
+// u*block_size + row.
 struct CacheGeom {
   char* k_base = nullptr;      // layer 0 of the K cache
   char* v_base = nullptr;
@@ -20,8 +26,8 @@ struct CacheGeom {
   int32_t num_kv_heads = 0;
   int32_t head_dim = 0;
   int32_t elt = 0;             // bytes per element
-  int32_t unit = 0;            // U: block_size (paged) or max_seq_len (contiguous)
   int32_t block_size = 0;
+  int32_t blocks_per_seq = 0;  // contiguous: max_seq_len / block_size
   int32_t paged = 1;
 };
 
@@ -42,7 +48,7 @@ struct DecodeArgs {
   int32_t num_seqs = 0;
   int32_t num_q_heads = 0;
   int32_t table_stride = 0;
-  int32_t partition_blocks = 0;      // blocks of block_size tokens per partition
+  int32_t partition_chunks = 0;      // 16-token chunks per partition
   int32_t num_partitions = 1;
   float scale = 1.0f;
 };

@@ -68,22 +68,33 @@ int64_t layer_bytes(const pa_pool_desc* d) {
   return units * d->num_kv_heads * unit * d->head_dim * elt_bytes(d->kv_dtype);
 }
 
-int32_t choose_partition_blocks(const pa_pool* p, int32_t num_seqs, int32_t max_context,
+// Tokens per context partition: a multiple of 16 (the MFMA tile) and of the
+// block size.  Enough workgroups to fill 256 CUs several times over, but at
+// least 256 tokens so each of the 4 waves streams several chunks.
+int32_t partition_unit(const pa_pool* p) { return p->desc.block_size > 16 ? p->desc.block_size : 16; }
+
+int32_t choose_partition_tokens(const pa_pool* p, int32_t num_seqs, int32_t max_context,
                                 int32_t partition_tokens) {
-  const int32_t bs = p->desc.block_size;
-  const int32_t nblk = (max_context + bs - 1) / bs;
-  if (nblk <= 0) return 1;
-  if (partition_tokens > 0) return partition_tokens / bs;
-  // Enough workgroups to fill 256 CUs several times over, but partitions of
-  // at least 256 tokens so each of the 4 waves streams several blocks.
+  const int32_t unit = partition_unit(p);
+  const int32_t nunits = (max_context + unit - 1) / unit;
+  if (nunits <= 0) return unit;
+  if (partition_tokens > 0) return partition_tokens;
   const int64_t base = static_cast<int64_t>(num_seqs) * p->desc.num_kv_heads;
   const int64_t target = 1024;
   int64_t parts = (target + base - 1) / base;
-  const int64_t min_blocks = (256 + bs - 1) / bs;
-  const int64_t max_parts = (nblk + min_blocks - 1) / min_blocks;
+  const int64_t min_units = (256 + unit - 1) / unit;
+  const int64_t max_parts = (nunits + min_units - 1) / min_units;
   if (parts > max_parts) parts = max_parts;
   if (parts < 1) parts = 1;
-  return static_cast<int32_t>((nblk + parts - 1) / parts);
+  return static_cast<int32_t>((nunits + parts - 1) / parts) * unit;
+}
+
+int32_t num_partitions(int32_t max_context, int32_t ptokens) {
+  return max_context <= 0 ? 1 : (max_context + ptokens - 1) / ptokens;
+}
+
+bool bad_partition(const pa_pool* p, int32_t partition_tokens) {
+  return partition_tokens < 0 || partition_tokens % partition_unit(p) != 0;
 }
 
 }  // namespace
@@ -121,7 +132,7 @@ pa_status pa_create_pool(const pa_pool_desc* desc, void* d_k_cache, void* d_v_ca
   g.elt = elt_bytes(desc->kv_dtype);
   g.block_size = desc->block_size;
   g.paged = desc->layout == PA_PAGED ? 1 : 0;
-  g.unit = g.paged ? desc->block_size : desc->max_seq_len;
+  g.blocks_per_seq = g.paged ? 0 : desc->max_seq_len / desc->block_size;
   pa_pool* p = new (std::nothrow) pa_pool(*desc, g);
   if (p == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool: out of host memory");
   *out = p;
@@ -224,21 +235,16 @@ pa_status pa_append_kv(pa_pool* pool, int32_t layer, const void* d_k, const void
 
 int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t max_context,
                                    int32_t partition_tokens) {
-  if (pool == nullptr || num_seqs < 0 || max_context < 0 || partition_tokens < 0) return 0;
-  if (partition_tokens % pool->desc.block_size != 0) return 0;
-  return choose_partition_blocks(pool, num_seqs, max_context, partition_tokens) *
-         pool->desc.block_size;
+  if (pool == nullptr || num_seqs < 0 || max_context < 0 || bad_partition(pool, partition_tokens)) return 0;
+  return choose_partition_tokens(pool, num_seqs, max_context, partition_tokens);
 }
 
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t num_q_heads,
                                  int32_t max_context, int32_t partition_tokens) {
-  if (pool == nullptr || num_seqs < 0 || max_context < 0 || partition_tokens < 0) return 0;
-  if (partition_tokens % pool->desc.block_size != 0) return 0;
-  const int32_t bs = pool->desc.block_size;
-  const int32_t pb = choose_partition_blocks(pool, num_seqs, max_context, partition_tokens);
-  const int32_t nblk = (max_context + bs - 1) / bs;
-  const int32_t parts = nblk <= 0 ? 1 : (nblk + pb - 1) / pb;
-  return pa::decode_workspace_bytes(num_seqs, num_q_heads, pool->desc.head_dim, parts);
+  if (pool == nullptr || num_seqs < 0 || max_context < 0 || bad_partition(pool, partition_tokens)) return 0;
+  const int32_t pt = choose_partition_tokens(pool, num_seqs, max_context, partition_tokens);
+  return pa::decode_workspace_bytes(num_seqs, num_q_heads, pool->desc.head_dim,
+                                    num_partitions(max_context, pt));
 }
 
 pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
@@ -256,12 +262,13 @@ pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dt
     return fail(PA_ERR_INVALID_ARG, "decode: num_q_heads must be a positive multiple of num_kv_heads");
   if (q_dtype != d.kv_dtype)
     return fail(PA_ERR_UNSUPPORTED, "decode: q_dtype must equal the cache's kv_dtype");
-  if (num_q_heads / d.num_kv_heads > 8)
-    return fail(PA_ERR_UNSUPPORTED, "decode: GQA groups of more than 8 query heads");
+  if (num_q_heads / d.num_kv_heads > 16)
+    return fail(PA_ERR_UNSUPPORTED, "decode: GQA groups of more than 16 query heads");
   if (max_context < 0 || max_context > d.max_seq_len)
     return fail(PA_ERR_INVALID_ARG, "decode: max_context must be in [0, max_seq_len]");
-  if (partition_tokens < 0 || partition_tokens % d.block_size != 0)
-    return fail(PA_ERR_INVALID_ARG, "decode: partition_tokens must be 0 or a positive multiple of block_size");
+  if (bad_partition(pool, partition_tokens))
+    return fail(PA_ERR_INVALID_ARG,
+                "decode: partition_tokens must be 0 or a positive multiple of 16 and of block_size");
   if (d_q == nullptr || d_context_lens == nullptr || d_out == nullptr)
     return fail(PA_ERR_INVALID_ARG, "decode: null device pointer");
   if (reinterpret_cast<uintptr_t>(d_q) & 15) return fail(PA_ERR_INVALID_ARG, "decode: q must be 16-byte aligned");
@@ -284,8 +291,9 @@ pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dt
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.table_stride = table_stride;
-  a.partition_blocks = choose_partition_blocks(pool, num_seqs, max_context, partition_tokens);
-  a.num_partitions = nblk <= 0 ? 1 : (nblk + a.partition_blocks - 1) / a.partition_blocks;
+  const int32_t pt = choose_partition_tokens(pool, num_seqs, max_context, partition_tokens);
+  a.partition_chunks = pt / 16;
+  a.num_partitions = num_partitions(max_context, pt);
   a.scale = scale;
   if (grid * a.num_partitions > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "decode: launch too large");
   const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, d.head_dim, a.num_partitions);

@@ -33,9 +33,12 @@ def _stream_handle(stream):
 class Pool:
     """K and V caches for ``num_layers`` layers plus the host block allocator.
 
-    Cache tensors (``k_cache``, ``v_cache``) have shape
-    ``[num_layers][units][num_kv_heads][U][head_dim]`` with ``units, U`` =
-    ``num_blocks, block_size`` (paged) or ``max_seqs, max_seq_len`` (contiguous).
+    Cache tensors hold one tile per (block, KV head), as include/pa.h lays out:
+      ``k_cache``: ``[num_layers][units][num_kv_heads][head_dim/VE][block_size][VE]``
+      ``v_cache``: ``[num_layers][units][num_kv_heads][head_dim][block_size]``
+    with ``VE = 16 / element bytes`` and ``units = num_blocks`` (paged) or
+    ``max_seqs * max_seq_len / block_size`` (contiguous: request r owns the
+    ``max_seq_len / block_size`` consecutive blocks from ``r * max_seq_len / block_size``).
     """
 
     def __init__(self, num_layers: int, num_blocks: int, block_size: int, num_kv_heads: int,
@@ -57,17 +60,19 @@ class Pool:
         if nbytes == 0:
             raise capi.PaError(capi.PA_ERR_INVALID_ARG, "Pool", "invalid pool description")
         tdt = torch.bfloat16 if kv_dtype == "bf16" else torch.float32
-        units, unit = ((num_blocks, block_size) if layout == "paged" else (max_seqs, max_seq_len))
-        shape = (num_layers, units, num_kv_heads, unit, head_dim)
+        units = num_blocks if layout == "paged" else max_seqs * (max_seq_len // block_size)
+        ve = 16 // (2 if kv_dtype == "bf16" else 4)
+        k_shape = (num_layers, units, num_kv_heads, head_dim // ve, block_size, ve)
+        v_shape = (num_layers, units, num_kv_heads, head_dim, block_size)
         if host_only:
             self.k_cache = self.v_cache = None
             self._fake = torch.empty(16, dtype=torch.uint8)
         elif fill is None:
-            self.k_cache = torch.empty(shape, dtype=tdt, device=device)
-            self.v_cache = torch.empty(shape, dtype=tdt, device=device)
+            self.k_cache = torch.empty(k_shape, dtype=tdt, device=device)
+            self.v_cache = torch.empty(v_shape, dtype=tdt, device=device)
         else:
-            self.k_cache = torch.full(shape, fill, dtype=tdt, device=device)
-            self.v_cache = torch.full(shape, fill, dtype=tdt, device=device)
+            self.k_cache = torch.full(k_shape, fill, dtype=tdt, device=device)
+            self.v_cache = torch.full(v_shape, fill, dtype=tdt, device=device)
         if host_only:
             # any 16-byte aligned address: allocator calls never dereference it
             kp = vp = (self._fake.data_ptr() + 15) // 16 * 16

@@ -152,18 +152,21 @@ class Case:
         """Oracle gather of sequence s's K and V out of the device cache."""
         layer = self.layers[0] if layer is None else layer
         n = int(self.pl.lengths[s])
+        bs = self.cfg.block_size
         if self.layout == "paged":
-            t = self.tables_np[s][: -(-n // self.cfg.block_size)]
+            t = self.tables_np[s][: -(-n // bs)]
             tt = torch.from_numpy(np.ascontiguousarray(t)).long().to(self.pool.k_cache.device)
-            kb = to_f64(self.pool.k_cache[layer].index_select(0, tt))
-            vb = to_f64(self.pool.v_cache[layer].index_select(0, tt))
+            kb = A.k_rows(to_f64(self.pool.k_cache[layer].index_select(0, tt)))
+            vb = A.v_rows(to_f64(self.pool.v_cache[layer].index_select(0, tt)))
             local = list(range(len(t)))
-            return (A.gather_paged(kb, local, n, self.cfg.block_size),
-                    A.gather_paged(vb, local, n, self.cfg.block_size))
+            return A.gather_paged(kb, local, n, bs), A.gather_paged(vb, local, n, bs)
         r = self.batch_rids[s]
-        kb = to_f64(self.pool.k_cache[layer][r: r + 1])
-        vb = to_f64(self.pool.v_cache[layer][r: r + 1])
-        return A.gather_contiguous(kb, 0, n), A.gather_contiguous(vb, 0, n)
+        per = self.cfg.max_seq_len // bs
+        kb = A.k_rows(to_f64(self.pool.k_cache[layer][r * per:(r + 1) * per]))
+        vb = A.v_rows(to_f64(self.pool.v_cache[layer][r * per:(r + 1) * per]))
+        kc = A.contiguous_rows(kb, 1, self.cfg.max_seq_len)
+        vc = A.contiguous_rows(np.ascontiguousarray(vb), 1, self.cfg.max_seq_len)
+        return A.gather_contiguous(kc, 0, n), A.gather_contiguous(vc, 0, n)
 
     def replay_on_oracle(self):
         """The oracle allocator on the same plan.

@@ -214,3 +214,23 @@ def test_bf16_decoding_matches_torch():
     ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(got, ref)
     assert got[0] == 1.0 and got[1] == -2.0 and got[4] == 2.0 ** -133
+
+
+def test_tile_readers_worked_example():
+    # d = 4, VE = 2, BS = 3: K tile [2][3][2], V tile [4][3]; token row o is
+    # (K) chunks 0 and 1 of row o, (V) column o.
+    k = np.arange(12).reshape(1, 1, 2, 3, 2)
+    rows = A.k_rows(k)
+    assert rows.shape == (1, 1, 3, 4)
+    assert rows[0, 0].tolist() == [[0, 1, 6, 7], [2, 3, 8, 9], [4, 5, 10, 11]]
+    v = np.arange(12).reshape(1, 1, 4, 3)
+    assert A.v_rows(v)[0, 0].tolist() == [[0, 3, 6, 9], [1, 4, 7, 10], [2, 5, 8, 11]]
+
+
+def test_contiguous_rows_follow_reqid_times_s():
+    # 2 requests, S = 4, BS = 2: request r's blocks are 2r and 2r+1
+    rows = np.arange(4 * 1 * 2 * 1).reshape(4, 1, 2, 1)
+    per_req = A.contiguous_rows(rows, 2, 4)
+    assert per_req[:, 0, :, 0].tolist() == [[0, 1, 2, 3], [4, 5, 6, 7]]
+    # flat offset of request r's sub-tensor is r x S x Hkv x d
+    assert per_req.reshape(-1).tolist() == rows.reshape(-1).tolist()
