@@ -44,9 +44,52 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="layer pools rotated (0: workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm-probe", action="store_true",
+                    help="skip the achievable-read-bandwidth probe (bench_read_probe)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized buffer 3 times (calibrates byte counters)")
+    ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
+                    help="only time plain reductions over a MIB-sized buffer (achievable read rate)")
     return ap.parse_args()
+
+
+def hbm_probe() -> dict | None:
+    """Best read rate of bench_read_probe (plain stream and 4 KiB tiles), GB/s."""
+    import subprocess
+
+    exe = os.path.join(ROOT, "bench_read_probe")
+    if not os.path.exists(exe):
+        return None
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    if res.returncode != 0:
+        return None
+    best = {}
+    for line in res.stdout.splitlines():
+        parts = line.split()
+        if len(parts) == 3:
+            best[parts[0]] = max(best.get(parts[0], 0.0), float(parts[2]))
+    return best
+
+
+def read_probe(mib: int) -> None:
+    """Achievable HBM read rate: plain device reductions over a large buffer."""
+    import torch
+
+    n = mib * (1 << 20) // 2
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for name, fn in (("sum", lambda: x.sum(dtype=torch.float32)), ("amax", lambda: x.amax())):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = round(n * 2 * 10 / (a.elapsed_time(b) / 1e3) / 1e9, 1)
+    print(json.dumps({"read_probe_bytes": n * 2, "gbs": res}), flush=True)
 
 
 def copy_probe(mib: int) -> None:
@@ -199,6 +242,35 @@ class Bench:
         return lens.astype(np.int64)
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "pa_decode_llama3-8b_b64_ctx1024_hbm_counters.md")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter summary, or None.
+
+    The rocprofv3 FETCH_SIZE / WRITE_SIZE runs of that summary were taken for
+    one workload and one kernel source; the figure is used only while both
+    still match (the kernel source's SHA-256 is compared).
+    """
+    import hashlib
+
+    try:
+        text = open(COUNTERS_FILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if "traffic_bytes_per_launch=" in line:
+            fields = dict(kv.split("=", 1) for kv in line.split())
+    if not fields or fields.get("workload") != workload:
+        return None
+    src = os.path.join(ROOT, "paged_kv_cache_241_amd", "csrc", "kernels.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if digest != fields.get("kernels_hip_sha256_16"):
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def kv_bytes(cfg, lens) -> int:
     elt = 2 if cfg.kv_dtype == "bf16" else 4
     return int(lens.sum()) * cfg.num_kv_heads * cfg.head_dim * elt * 2
@@ -274,6 +346,9 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
+    if args.read_probe:
+        read_probe(args.read_probe)
+        return
     import torch
 
     import workloads as W
@@ -347,10 +422,18 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
         },
     }
+    if args.config == 2 and args.layout == "paged" and args.partition_tokens == 0:
+        res["roofline"]["traffic"] = measured_traffic("cfg2-paged")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(bench, args.cpu_seconds)
+    if not args.no_hbm_probe:
+        probe = hbm_probe()
+        if probe:
+            res["hbm_read_probe_gbs"] = probe
+            res["roofline"]["frac_of_probe_best"] = round(achieved / max(probe.values()), 4)
     print(json.dumps(res), flush=True)
 
 

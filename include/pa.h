@@ -16,25 +16,34 @@
  * ---------------------------------------------------------------------------
  * Cache layout (device memory owned by the caller)
  * ---------------------------------------------------------------------------
- * The K cache and the V cache are two separate device arrays of identical
- * shape, element type kv_dtype, for all layers:
+ * The K cache and the V cache are two separate device arrays, element type
+ * kv_dtype, for all layers.  Each layer is an array of tiles, one per (block,
+ * KV head); VE = 16 / sizeof(element) (8 for bf16, 4 for fp32):
  *
- *   PA_PAGED:      [num_layers][num_blocks][num_kv_heads][block_size][head_dim]
- *   PA_CONTIGUOUS: [num_layers][max_seqs][num_kv_heads][max_seq_len][head_dim]
+ *   K: [num_layers][units][num_kv_heads][head_dim/VE][block_size][VE]
+ *   V: [num_layers][units][num_kv_heads][head_dim][block_size]
  *
- * Paged: block b of a layer holds, for every KV head, block_size consecutive
- * token rows; a sequence's blocks need not be adjacent and its block table maps
- * logical block j (tokens j*BS .. j*BS+BS-1) to a physical block ([ROC] paging
- * paragraph and Terms; [PAS] Summary).  One block id names the same block in
- * every layer, in K and in V.
- * Contiguous: request r owns the sub-tensor at offset r x (max K-cache size of
- * one request) of each layer's tensor ([VAC] 5.2.3); the library hands out r.
+ * The K tile keeps each token row in 16-byte chunks (chunk-major); the V tile
+ * is dimension-major.  Both make the decode kernel's matrix-core operand
+ * loads contiguous wave accesses.
  *
- * A "slot" names one token row:  slot = u*U + o, with U = block_size (paged:
- * u = physical block, o = row in the block) or U = max_seq_len (contiguous:
- * u = reqId, o = position).  Element (slot, head h, dim e) of layer l is at
- *   ((l*units + u)*num_kv_heads + h)*U*head_dim + o*head_dim + e
- * with units = num_blocks (paged) or max_seqs (contiguous).
+ * PA_PAGED: units = num_blocks.  Block b holds, for every KV head,
+ * block_size consecutive tokens; a sequence's blocks need not be adjacent and
+ * its block table maps logical block j (tokens j*BS .. j*BS+BS-1) to a
+ * physical block ([ROC] paging paragraph and Terms; [PAS] Summary).  One block
+ * id names the same block in every layer, in K and in V.
+ * PA_CONTIGUOUS: units = max_seqs * max_seq_len / block_size.  Request r owns
+ * the max_seq_len / block_size consecutive blocks starting at block
+ * r * max_seq_len / block_size, i.e. the sub-tensor at offset r x (max K-cache
+ * size of one request) of each layer's tensor ([VAC] 5.2.3); the library
+ * hands out r.
+ *
+ * A "slot" names one token row: slot = u*block_size + o, u the block, o the
+ * row in it (contiguous: slot = reqId*max_seq_len + position).  Element
+ * (slot, head h, dim e) of layer l is, with tile = ((l*units + u)*num_kv_heads
+ * + h) * head_dim * block_size:
+ *   K: tile + ((e / VE) * block_size + o) * VE + e % VE
+ *   V: tile + e * block_size + o
  *
  * ---------------------------------------------------------------------------
  * Conventions
@@ -98,6 +107,7 @@ typedef struct pa_stats {
   int64_t reserved_tokens;  /* paged: used_blocks*block_size; contiguous: live*S */
   int64_t live_seqs;
   int64_t cow_copies;       /* copy-on-write copies made since creation */
+  int64_t shared_blocks;    /* blocks currently held by more than one request */
   double utilisation;       /* tokens / reserved_tokens: share of reserved cache
                                holding real tokens ([ROC] readouts, [PAS] Key points) */
 } pa_stats;
@@ -195,7 +205,8 @@ pa_status pa_append_kv(pa_pool* pool, int32_t layer, const void* d_k, const void
                        const int32_t* d_slots, int32_t n, void* stream);
 
 /* Context partition pa_decode uses for these sizes (partition_tokens 0 =
- * the library's choice), in tokens: a multiple of block_size. */
+ * the library's choice), in tokens: a multiple of 16 and of block_size.
+ * Returns 0 for invalid arguments. */
 int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t max_context,
                                    int32_t partition_tokens);
 
@@ -220,9 +231,16 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t 
  *   d_out:          device fp32 [num_seqs][num_q_heads][head_dim].
  *   d_workspace:    device scratch of >= pa_decode_workspace_bytes(...) bytes
  *                   (may be NULL when that is 0).
+ *   partition_tokens: context tokens per workgroup, 0 = the library's choice,
+ *                   else a multiple of 16 and of block_size; contexts longer
+ *                   than one partition are split and merged (split-K).
  * Softmax is computed online in fp32 per context partition; partitions are
  * merged in a fixed order, so results depend only on logical positions, never
- * on which physical blocks hold them.  Supported: G <= 8, head_dim 64/128. */
+ * on which physical blocks hold them.  bf16 caches weight V with each softmax
+ * weight split into two bf16 parts (relative error below 2^-16 per weight).
+ * K and V are read with non-temporal loads while no block of the pool is
+ * shared, with cached loads otherwise.  Supported: G <= 16, head_dim 64/128.
+ * The workspace serves one call at a time. */
 pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
                     int32_t num_q_heads, float scale, const int32_t* d_block_tables,
                     int32_t table_stride, const int32_t* d_req_ids,

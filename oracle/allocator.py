@@ -237,6 +237,7 @@ class RefAllocator:
             "reserved_tokens": reserved,
             "live_seqs": len(self.seqs),
             "cow_copies": self.cow_copies,
+            "shared_blocks": sum(1 for rc in self.refcount if rc > 1),
             "utilisation": (tokens / reserved) if reserved else 0.0,
         }
 

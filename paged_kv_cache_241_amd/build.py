@@ -68,6 +68,11 @@ def build(verbose: bool = False) -> str:
           os.path.join(BUILD, "kernels.o"), os.path.join(BUILD, "pa_api.o"),
           os.path.join(BUILD, "block_allocator.o")], verbose)
     os.replace(tmp, LIB)
+    # the benchmark's achievable-bandwidth probe (not part of the library)
+    probe_src = os.path.join(ROOT, "bench_read_probe.hip")
+    if os.path.exists(probe_src):
+        _run([hipcc, "-O3", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
+              "-packed-fp32-ops", probe_src, "-o", os.path.join(ROOT, "bench_read_probe")], verbose)
     return LIB
 
 

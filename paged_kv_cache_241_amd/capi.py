@@ -60,7 +60,8 @@ class pa_stats(ctypes.Structure):
         ("free_blocks", ctypes.c_int64), ("used_blocks", ctypes.c_int64),
         ("tokens", ctypes.c_int64), ("logical_tokens", ctypes.c_int64),
         ("reserved_tokens", ctypes.c_int64), ("live_seqs", ctypes.c_int64),
-        ("cow_copies", ctypes.c_int64), ("utilisation", ctypes.c_double),
+        ("cow_copies", ctypes.c_int64), ("shared_blocks", ctypes.c_int64),
+        ("utilisation", ctypes.c_double),
     ]
 
 

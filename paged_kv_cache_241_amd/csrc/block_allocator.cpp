@@ -100,7 +100,8 @@ Status BlockAllocator::fork(int32_t parent, int32_t* child, std::string* err) {
   c.live = true;
   c.len = p.len;
   c.table = p.table;
-  for (int32_t b : c.table) ++refcount_[b];
+  for (int32_t b : c.table)
+    if (++refcount_[b] == 2) ++shared_blocks_;
   *child = r;
   return kOk;
 }
@@ -110,7 +111,9 @@ Status BlockAllocator::free_seq(int32_t rid, std::string* err) {
   if (st != kOk) return st;
   Seq& s = seqs_[rid];
   for (int32_t b : s.table) {
-    if (--refcount_[b] == 0) {
+    const int32_t rc = --refcount_[b];
+    if (rc == 1) --shared_blocks_;
+    if (rc == 0) {
       fill_[b] = 0;
       free_.push_back(b);
     }
@@ -233,7 +236,7 @@ Status BlockAllocator::reserve(const int32_t* rids, int32_t n, const int32_t* co
           const int32_t nb = pop_block();
           refcount_[nb] = 1;
           fill_[nb] = fill_[b];
-          --refcount_[b];
+          if (--refcount_[b] == 1) --shared_blocks_;
           s.table.back() = nb;
           pairs[2 * np] = b;
           pairs[2 * np + 1] = nb;
@@ -288,6 +291,7 @@ AllocStats BlockAllocator::stats() const {
     st.logical_tokens += s.len;
   }
   st.cow_copies = cow_copies_;
+  st.shared_blocks = shared_blocks_;
   if (paged_) {
     st.free_blocks = static_cast<int64_t>(free_.size());
     st.used_blocks = num_blocks_ - st.free_blocks;

@@ -34,7 +34,7 @@ enum Status : int {
 
 struct AllocStats {
   int64_t free_blocks = 0, used_blocks = 0, tokens = 0, logical_tokens = 0;
-  int64_t reserved_tokens = 0, live_seqs = 0, cow_copies = 0;
+  int64_t reserved_tokens = 0, live_seqs = 0, cow_copies = 0, shared_blocks = 0;
   double utilisation = 0.0;
 };
 
@@ -55,6 +55,8 @@ class BlockAllocator {
                 std::string* err) const;
   AllocStats stats() const;
 
+  // Blocks currently held by more than one request.
+  int64_t shared_blocks() const { return shared_blocks_; }
   bool paged() const { return paged_; }
   int32_t block_size() const { return block_size_; }
   int32_t num_blocks() const { return num_blocks_; }
@@ -79,6 +81,7 @@ class BlockAllocator {
   std::vector<int32_t> free_ids_;  // stack of free reqIds
   std::vector<Seq> seqs_;          // indexed by reqId
   int64_t cow_copies_ = 0;
+  int64_t shared_blocks_ = 0;      // blocks with refcount > 1
   // per-call scratch (kept to avoid reallocating on every reserve)
   std::vector<uint32_t> mark_;
   uint32_t epoch_ = 0;

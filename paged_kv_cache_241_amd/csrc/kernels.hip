@@ -48,11 +48,14 @@ namespace pa {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWave * kWaves;
 constexpr int kMergeThreads = 64;
 constexpr int kChunk = 16;        // tokens per MFMA tile
 constexpr int kMaxGroup = 16;     // query heads per KV head the tile can hold
+constexpr int kMaxMergeLds = 64 * 1024;
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 0
+#endif
+constexpr int kDepth = PA_DECODE_DEPTH;  // chunks in flight per wave while one is processed
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -60,10 +63,14 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-// Workgroups of a launch are dealt to the 8 XCDs round-robin by id.  Give
-// each XCD one contiguous range of work items so that neighbours (partitions
-// of one sequence, samples sharing a prompt's blocks) meet in the same L2.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
+// Workgroups of a launch are dealt to the 8 XCDs round-robin by id.  With
+// shared blocks (samples of one prompt), give each XCD one contiguous range
+// of work items so that the sharers meet in the same L2.  Without sharing,
+// keep the round-robin order: the KV heads of one sequence then spread over
+// all XCDs, which balances ragged batches (measured on MI355X: 4% faster on a
+// ragged mix, 2% slower with shared prompts).
+__device__ __forceinline__ int work_item(int bid, int n, bool group) {
+  if (!group) return bid;
   constexpr int kXcd = 8;
   const int q = n / kXcd, rem = n % kXcd;
   const int x = bid % kXcd, local = bid / kXcd;
@@ -80,6 +87,31 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
 __device__ __forceinline__ uint4 ld16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ld8(const char* p) { return *reinterpret_cast<const uint2*>(p); }
+
+// K/V cache reads.  When no block is shared, every byte is read once per
+// decode and the loads are marked non-temporal (streamed past the caches'
+// retention); shared blocks (several samples of one prompt) are read with
+// ordinary loads so that the repeats hit in L2 / Infinity Cache.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+template <bool NT>
+__device__ __forceinline__ uint4 kv16(const char* p) {
+  if constexpr (NT) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return ld16(p);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ uint2 kv8(const char* p) {
+  if constexpr (NT) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(v.x, v.y);
+  } else {
+    return ld8(p);
+  }
+}
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
@@ -100,21 +132,32 @@ struct Geo {
 // ---------------------------------------------------------------------------
 // decode: one workgroup per (sequence, KV head, partition)
 // ---------------------------------------------------------------------------
-template <int KIND, int D, int BS>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
+#ifndef PA_DECODE_WAVES_PER_EU
+#define PA_DECODE_WAVES_PER_EU 0
+#endif
+// LDS bytes of the wave merge: per wave, G maxima, G sums and G x D partial
+// outputs.
+__host__ __device__ constexpr int merge_lds_bytes(int waves, int G, int D) {
+  return waves * G * (D + 2) * 4;
+}
+
+template <int KIND, int D, int BS, int W, bool NT>
+__global__ __launch_bounds__(W * kWave)
+#if PA_DECODE_WAVES_PER_EU > 0
+__attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU, PA_DECODE_WAVES_PER_EU)))
+#endif
+void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
   using GG = Geo<KIND, D, BS>;
   constexpr int NX = GG::NX, NN = GG::NN, TILE = GG::TILE, ELT = GG::ELT;
+  constexpr int kWaves = W;
+  constexpr int kThreads = W * kWave;
   // V operand per lane per output tile: 4 consecutive tokens of one dim
   using VOp = typename std::conditional<KIND == kBF16, uint2, uint4>::type;
-
-  __shared__ float sm_m[kWaves][kMaxGroup];
-  __shared__ float sm_l[kWaves][kMaxGroup];
-  __shared__ float sm_acc[kWaves][kMaxGroup][D];
 
   const int P = a.num_partitions;
   const int hkv = geo.num_kv_heads;
   const int G = a.num_q_heads / hkv;
-  const int work = xcd_remap(blockIdx.x, gridDim.x);
+  const int work = work_item(blockIdx.x, gridDim.x, !NT);
   const int part = work % P;
   const int sk = work / P;
   const int kvh = sk % hkv;
@@ -178,8 +221,6 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(CacheGeom ge
 #pragma unroll
   for (int nb = 0; nb < NN; ++nb) acc[nb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  uint4 kop[NX];
-  VOp vop[NN];
   auto load = [&](int c, uint4 (&kk)[NX], VOp (&vv)[NN]) {
     if constexpr (BS >= kChunk) {
       // the chunk lies in one block: a wave-uniform tile base plus a 32-bit
@@ -193,41 +234,42 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(CacheGeom ge
       const int row0 = (c * kChunk) % BS;
       const uint32_t ko = static_cast<uint32_t>((j4 * BS + row0 + n) * 16);
 #pragma unroll
-      for (int x = 0; x < NX; ++x) kk[x] = ld16(kt + ko + x * 4 * BS * 16);
+      for (int x = 0; x < NX; ++x) kk[x] = kv16<NT>(kt + ko + x * 4 * BS * 16);
       const uint32_t vo = static_cast<uint32_t>((n * BS + row0 + 4 * j4) * ELT);
 #pragma unroll
       for (int nb = 0; nb < NN; ++nb) {
-        if constexpr (KIND == kBF16) vv[nb] = ld8(vt + vo + nb * 16 * BS * ELT);
-        else vv[nb] = ld16(vt + vo + nb * 16 * BS * ELT);
+        if constexpr (KIND == kBF16) vv[nb] = kv8<NT>(vt + vo + nb * 16 * BS * ELT);
+        else vv[nb] = kv16<NT>(vt + vo + nb * 16 * BS * ELT);
       }
     } else {
       // blocks shorter than a chunk: each lane finds its own block
       const int tk = c * kChunk + n;
       const char* kt = kl + tile_of(tk) + (tk % BS) * 16;
 #pragma unroll
-      for (int x = 0; x < NX; ++x) kk[x] = ld16(kt + (x * 4 + j4) * BS * 16);
+      for (int x = 0; x < NX; ++x) kk[x] = kv16<NT>(kt + (x * 4 + j4) * BS * 16);
       int tv = c * kChunk + 4 * j4;
       tv = min(tv, ((L - 1) / 4) * 4);
       const char* vt = vl + tile_of(tv) + (tv % BS) * ELT;
 #pragma unroll
       for (int nb = 0; nb < NN; ++nb) {
-        if constexpr (KIND == kBF16) vv[nb] = ld8(vt + (nb * 16 + n) * BS * ELT);
-        else vv[nb] = ld16(vt + (nb * 16 + n) * BS * ELT);
+        if constexpr (KIND == kBF16) vv[nb] = kv8<NT>(vt + (nb * 16 + n) * BS * ELT);
+        else vv[nb] = kv16<NT>(vt + (nb * 16 + n) * BS * ELT);
       }
     }
   };
 
+  // The chunk being processed plus DEPTH chunks whose loads are in flight,
+  // in a ring of register buffers; the rotation is unrolled so that every
+  // buffer index is a constant.  Loads past the partition re-read its last
+  // chunk (an L2 hit) instead of branching: a branch around loads makes the
+  // wait for the current chunk also wait for the newer loads.
+  constexpr int DEPTH = kDepth;
+  uint4 kbuf[DEPTH + 1][NX];
+  VOp vbuf[DEPTH + 1][NN];
   int c = cb + wave;
-  if (c < ce) load(c, kop, vop);
-  while (c < ce) {
-    const int cn = c + kWaves;
-    uint4 kn[NX];
-    VOp vn[NN];
-    // always issue the next chunk's loads (the last iteration re-reads a chunk
-    // of this partition): a branch here would make the wait for the current
-    // chunk also wait for these
-    load(min(cn, ce - 1), kn, vn);
-
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) load(min(c + d * kWaves, ce - 1), kbuf[d], vbuf[d]);
+  auto process = [&](int c, uint4 (&kop)[NX], VOp (&vop)[NN]) {
     // S[token 4*j4+i][head n]
     floatx4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -315,38 +357,48 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(CacheGeom ge
         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[3], __uint_as_float(vop[nb].w), acc[nb], 0, 0, 0);
       }
     }
-    c = cn;
+  };
+  while (c < ce) {
 #pragma unroll
-    for (int x = 0; x < NX; ++x) kop[x] = kn[x];
-#pragma unroll
-    for (int nb = 0; nb < NN; ++nb) vop[nb] = vn[nb];
+    for (int d = 0; d <= DEPTH; ++d) {
+      if (c >= ce) break;
+      load(min(c + DEPTH * kWaves, ce - 1), kbuf[(d + DEPTH) % (DEPTH + 1)],
+           vbuf[(d + DEPTH) % (DEPTH + 1)]);
+      process(c, kbuf[d], vbuf[d]);
+      c += kWaves;
+    }
   }
 
-  // weight sum of head n over the wave's tokens, then merge the waves
+  // weight sum of head n over the wave's tokens, then merge the waves:
+  // LDS holds m[W][G], l[W][G], acc[W][G][D]
+  extern __shared__ float lds[];
+  float* sm_m = lds;
+  float* sm_l = lds + kWaves * G;
+  float* sm_acc = lds + 2 * kWaves * G;
   lsum += xor16(lsum);
   lsum += xor32(lsum);
   if (j4 == 0 && n < G) {
-    sm_m[wave][n] = m;
-    sm_l[wave][n] = lsum;
+    sm_m[wave * G + n] = m;
+    sm_l[wave * G + n] = lsum;
   }
 #pragma unroll
   for (int nb = 0; nb < NN; ++nb)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (4 * j4 + i < G) sm_acc[wave][4 * j4 + i][nb * 16 + n] = acc[nb][i];
+      if (4 * j4 + i < G) sm_acc[(wave * G + 4 * j4 + i) * D + nb * 16 + n] = acc[nb][i];
   __syncthreads();
   const int64_t row0 = static_cast<int64_t>(s) * a.num_q_heads + h0;
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int g = idx / D, e = idx % D;
-    float mx = sm_m[0][g];
+    float mx = sm_m[g];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm_m[w][g]);
+    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm_m[w * G + g]);
     float A = 0.0f, Lt = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float wt = fexp2(sm_m[w][g] - mx);
-      A = fmaf(wt, sm_acc[w][g][e], A);
-      Lt = fmaf(wt, sm_l[w][g], Lt);
+      const float wt = fexp2(sm_m[w * G + g] - mx);
+      A = fmaf(wt, sm_acc[(w * G + g) * D + e], A);
+      Lt = fmaf(wt, sm_l[w * G + g], Lt);
     }
     if (P == 1) {
       a.out[(row0 + g) * D + e] = A / Lt;
@@ -454,16 +506,29 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CacheGeom g,
   }
 }
 
-template <int KIND, int D, int BS>
-hipError_t launch_decode_t(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
+template <int KIND, int D, int BS, int W>
+hipError_t launch_decode_w(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
   const int64_t nwork = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
-  hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS>), dim3(static_cast<uint32_t>(nwork)),
-                     dim3(kThreads), 0, st, g, a);
+  const int G = a.num_q_heads / g.num_kv_heads;
+  if (a.streaming)
+    hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, true>), dim3(static_cast<uint32_t>(nwork)),
+                       dim3(W * kWave), merge_lds_bytes(W, G, D), st, g, a);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, false>), dim3(static_cast<uint32_t>(nwork)),
+                       dim3(W * kWave), merge_lds_bytes(W, G, D), st, g, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_partitions == 1) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(static_cast<uint32_t>(a.num_seqs) * a.num_q_heads),
                      dim3(kMergeThreads), 0, st, a);
   return hipGetLastError();
+}
+
+template <int KIND, int D, int BS>
+hipError_t launch_decode_t(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
+  const int G = a.num_q_heads / g.num_kv_heads;
+  if (a.waves == 8 && merge_lds_bytes(8, G, D) <= kMaxMergeLds)
+    return launch_decode_w<KIND, D, BS, 8>(g, a, st);
+  return launch_decode_w<KIND, D, BS, 4>(g, a, st);
 }
 
 template <int KIND, int D>

@@ -50,6 +50,8 @@ struct DecodeArgs {
   int32_t table_stride = 0;
   int32_t partition_chunks = 0;      // 16-token chunks per partition
   int32_t num_partitions = 1;
+  int32_t waves = 4;                 // waves per workgroup: 4 or 8
+  int32_t streaming = 1;             // non-temporal K/V loads (no block is shared)
   float scale = 1.0f;
 };
 

@@ -86,7 +86,7 @@ def _same_state(ref, lib):
     got = lib.p.stats()
     want = ref.stats()
     for key in ("free_blocks", "used_blocks", "tokens", "logical_tokens", "reserved_tokens",
-                "live_seqs", "cow_copies"):
+                "live_seqs", "cow_copies", "shared_blocks"):
         assert got[key] == want[key], key
     assert got["utilisation"] == pytest.approx(want["utilisation"], rel=0, abs=1e-15)
 
