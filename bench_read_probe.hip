@@ -30,6 +30,32 @@ __global__ void tile_read(const u32x4* __restrict__ b, const int* __restrict__ p
   }
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
+// The decode's own read pattern without its arithmetic: 512 workgroups x 4
+// waves, each wave walks 16 random blocks and reads, per block, a 4 KiB K
+// tile (4 x 16 B per lane) and a 4 KiB V tile (8 x 8 B per lane) from two
+// arrays.  ids[] holds block ids < nblocks.
+__global__ void kv_pattern(const char* __restrict__ K, const char* __restrict__ V,
+                           const int* __restrict__ ids, int per_wave, unsigned* out) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & 63;
+  const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  u32x4 acc = {0, 0, 0, 0};
+  for (int i = 0; i < per_wave; ++i) {
+    const long tile = (long)ids[gw * per_wave + i] * 4096;
+    u32x4 k[4];
+    u32x2 v[8];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) k[x] = __builtin_nontemporal_load((const u32x4*)(K + tile + x * 1024 + lane * 16));
+#pragma unroll
+    for (int x = 0; x < 8; ++x) v[x] = __builtin_nontemporal_load((const u32x2*)(V + tile + x * 512 + lane * 8));
+#pragma unroll
+    for (int x = 0; x < 4; ++x) acc ^= k[x];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) { acc.x ^= v[x].x; acc.y ^= v[x].y; }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 int main() {
   const size_t bytes = (size_t)4 << 30, n = bytes / 16;
   const int ntiles = (int)(bytes / 4096);
@@ -59,6 +85,28 @@ int main() {
       float ms; CK(hipEventElapsedTime(&ms, ev0, ev1));
       printf("tiles_%s %d %.0f\n", shuffle ? "random" : "in_order", wg, 5.0 * bytes / (ms / 1e3) / 1e9);
     }
+  }
+  {
+    // decode-shaped pattern: K and V tiles from the two halves of the buffer
+    const char* Kp = reinterpret_cast<const char*>(b);
+    const char* Vp = Kp + bytes / 2;
+    const int nblocks = (int)(bytes / 2 / 4096), per_wave = 16, wg = 512, waves = wg * 4;
+    std::vector<int> ids((size_t)waves * per_wave);
+    std::mt19937 g(7);
+    std::uniform_int_distribution<int> U(0, nblocks - 1);
+    for (auto& x : ids) x = U(g);
+    int* dids;
+    CK(hipMalloc(&dids, ids.size() * 4));
+    CK(hipMemcpy(dids, ids.data(), ids.size() * 4, hipMemcpyHostToDevice));
+    hipLaunchKernelGGL(kv_pattern, dim3(wg), dim3(256), 0, 0, Kp, Vp, dids, per_wave, out);
+    CK(hipGetLastError());
+    CK(hipEventRecord(ev0));
+    for (int r = 0; r < 20; ++r) hipLaunchKernelGGL(kv_pattern, dim3(wg), dim3(256), 0, 0, Kp, Vp, dids, per_wave, out);
+    CK(hipEventRecord(ev1)); CK(hipEventSynchronize(ev1));
+    float ms; CK(hipEventElapsedTime(&ms, ev0, ev1));
+    const double moved = (double)waves * per_wave * 8192;
+    printf("decode_pattern %d %.0f\n", wg, moved * 20 / (ms / 1e3) / 1e9);
+    printf("decode_pattern_us %d %.2f\n", wg, ms * 1e3 / 20);
   }
   return 0;
 }
