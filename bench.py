@@ -2,10 +2,12 @@
 
 One step = one decode iteration of the whole batch over every layer pool:
   host  pa_reserve: one new token per sequence (allocate-on-fill, copy-on-write)
-  H2D   slots, block tables and context lengths (pinned, asynchronous)
+  H2D   slots, context lengths, and block tables when a block was handed out
+        (pinned, asynchronous)
   GPU   pa_copy_blocks for any copy-on-write pairs
-        pa_append_kv for each layer (the new token's K/V)
-        pa_decode for each layer (paged attention; split-K merge if needed)
+        pa_append_decode for each layer: the new token's K/V stored into its
+        slot and paged attention over the context, in one launch (split-K
+        merge if needed); --separate-append uses pa_append_kv + pa_decode
 NL distinct layer pools are rotated so that the 256 MB Infinity Cache cannot
 serve repeated reads.  Contexts grow by one token per step; the workload's
 prefill is set so that the timed steps are centred on the nominal context.
@@ -42,6 +44,8 @@ def parse():
     ap.add_argument("--prompt-len", type=int, default=0, help="workload 5: prompt length")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--block-size", type=int, default=0, help="tokens per block (0: workload's, 16)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="pa_append_kv then pa_decode per layer instead of one pa_append_decode")
     ap.add_argument("--layers", type=int, default=0, help="layer pools rotated (0: workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -210,7 +214,7 @@ class Bench:
             self.pool.append_kv(layer, kr.index_select(0, it).contiguous(),
                                 vr.index_select(0, it).contiguous(), st)
 
-    def prepare(self, max_steps: int):
+    def prepare(self, max_steps: int, separate_append: bool = False):
         """Fixed device buffers, double-buffered pinned staging, ctypes arguments."""
         import ctypes
 
@@ -249,6 +253,7 @@ class Bench:
         self.ws_bytes = self.ws.numel()
         self.dtype_code = capi.PA_BF16 if self.cfg.kv_dtype == "bf16" else capi.PA_F32
         self.check = capi.check
+        self.separate_append = separate_append
         self.nstep = 0
         # the tables only change when a block is handed out: upload on demand
         self.tables_dirty = True
@@ -286,20 +291,25 @@ class Bench:
         st["event"].record(self.stream)
         lens = st["lens"].numpy().astype(np.int64)
         max_context = int(lens.max())
-        for layer in range(self.nl):
-            self.check(lib.pa_append_kv(pool.handle, layer, self.k_new[layer].data_ptr(),
-                                        self.v_new[layer].data_ptr(), self.slots_d.data_ptr(), b,
-                                        self.sh), "pa_append_kv")
-        if ev is not None:
-            ev[0].record(self.stream)
         tables = self.tables_d.data_ptr() if self.layout == "paged" else None
         req = self.req_ids.data_ptr() if self.layout != "paged" else None
+        if self.separate_append:
+            for layer in range(self.nl):
+                self.check(lib.pa_append_kv(pool.handle, layer, self.k_new[layer].data_ptr(),
+                                            self.v_new[layer].data_ptr(), self.slots_d.data_ptr(),
+                                            b, self.sh), "pa_append_kv")
+        if ev is not None:
+            ev[0].record(self.stream)
         for layer in range(self.nl):
-            self.check(lib.pa_decode(pool.handle, layer, self.q[layer].data_ptr(), self.dtype_code,
-                                     cfg.num_q_heads, self.scale, tables, self.stride, req,
-                                     self.lens_d.data_ptr(), b, max_context, self.pt,
-                                     self.out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, self.sh),
-                       "pa_decode")
+            tail = (self.q[layer].data_ptr(), self.dtype_code, cfg.num_q_heads, self.scale, tables,
+                    self.stride, req, self.lens_d.data_ptr(), b, max_context, self.pt,
+                    self.out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, self.sh)
+            if self.separate_append:
+                self.check(lib.pa_decode(pool.handle, layer, *tail), "pa_decode")
+            else:
+                self.check(lib.pa_append_decode(pool.handle, layer, self.k_new[layer].data_ptr(),
+                                                self.v_new[layer].data_ptr(), self.slots_d.data_ptr(),
+                                                *tail), "pa_append_decode")
         if ev is not None:
             ev[1].record(self.stream)
         return lens
@@ -324,8 +334,10 @@ def measured_traffic(workload: str):
     fields = {}
     for line in text.splitlines():
         if "traffic_bytes_per_launch=" in line:
-            fields = dict(kv.split("=", 1) for kv in line.split())
-    if not fields or fields.get("workload") != workload:
+            kv = dict(item.split("=", 1) for item in line.split())
+            if kv.get("workload") == workload:
+                fields = kv
+    if not fields:
         return None
     src = os.path.join(ROOT, "paged_kv_cache_241_amd", "csrc", "kernels.hip")
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
@@ -339,12 +351,40 @@ def kv_bytes(cfg, lens) -> int:
     return int(lens.sum()) * cfg.num_kv_heads * cfg.head_dim * elt * 2
 
 
-def algorithmic_bytes(cfg, lens) -> int:
-    """Bytes a decode launch must move: K/V, q, out, block-table entries, lengths."""
+def unique_kv_fraction(bench) -> float:
+    """Share of the batch's logical K/V bytes that lie in distinct blocks.
+
+    Samples of one prompt share its full blocks, and a shared block has to come
+    from HBM only once per launch, so the roofline counts every distinct block
+    (with the most rows any sharer uses) once.  1.0 when nothing is shared."""
+    if bench.layout != "paged":
+        return 1.0
+    tables, lens = bench.pool.block_tables(bench.rids_np)
+    bs = bench.cfg.block_size
+    rows_of = {}
+    logical = 0
+    for row, n in zip(tables, lens):
+        n = int(n)
+        for j in range(-(-n // bs)):
+            rows = min(bs, n - j * bs)
+            blk = int(row[j])
+            rows_of[blk] = max(rows_of.get(blk, 0), rows)
+            logical += rows
+    return sum(rows_of.values()) / logical if logical else 1.0
+
+
+def algorithmic_bytes(cfg, lens, fused_append: bool, kv_fraction: float = 1.0) -> int:
+    """Bytes a decode launch must move: K/V (times the share in distinct blocks),
+    q, out, block-table entries, lengths; with the fused append also the new
+    rows (read once, written once) and slots."""
     elt = 2 if cfg.kv_dtype == "bf16" else 4
     b = len(lens)
     tables = int(sum(-(-int(n) // cfg.block_size) for n in lens)) * 4
-    return (kv_bytes(cfg, lens) + b * cfg.num_q_heads * cfg.head_dim * (elt + 4) + tables + b * 4)
+    total = (int(round(kv_bytes(cfg, lens) * kv_fraction)) +
+             b * cfg.num_q_heads * cfg.head_dim * (elt + 4) + tables + b * 4)
+    if fused_append:
+        total += b * cfg.num_kv_heads * cfg.head_dim * elt * 2 * 2 + b * 4
+    return total
 
 
 def cpu_baseline(bench, seconds: float) -> dict:
@@ -432,27 +472,29 @@ def main():
     cfg = W.get(args.config, **over)
     nl = args.layers or cfg.num_layers
     bench = Bench(cfg, args.layout, nl, args.warmup + args.steps + 1, args.partition_tokens)
-    bench.prepare(args.warmup + args.steps)
+    bench.prepare(args.warmup + args.steps, args.separate_append)
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     total_kv = 0
-    total_alg = 0
     lens_seen = []
+    lens_all = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         lens = bench.step(evs[i])
         total_kv += kv_bytes(cfg, lens) * nl
-        total_alg += algorithmic_bytes(cfg, lens) * nl
+        lens_all.append(lens)
         lens_seen.append(float(lens.mean()))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dt = t1 - t0
     decode_ms = sum(a.elapsed_time(b) for a, b in evs)
     per_launch_s = decode_ms / 1e3 / (args.steps * nl)
+    kv_frac = unique_kv_fraction(bench)
+    total_alg = sum(algorithmic_bytes(cfg, ln, not args.separate_append, kv_frac) for ln in lens_all) * nl
     achieved = total_alg / (args.steps * nl) / per_launch_s / 1e9
     value = total_kv / dt / 1e9
     b = len(bench.batch)
@@ -485,17 +527,20 @@ def main():
         "pool_utilisation": round(stats["utilisation"], 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode (decode_partition_kernel + decode_merge_kernel when split)",
+            "kernel": ("pa_decode" if args.separate_append else "pa_append_decode") +
+                      " (decode_partition_kernel, + decode_merge_kernel when contexts are split)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "kv_unique_fraction": round(kv_frac, 4),
             "traffic": None,
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
         },
     }
     if args.config == 2 and args.layout == "paged" and args.partition_tokens == 0:
-        res["roofline"]["traffic"] = measured_traffic("cfg2-paged")
+        res["roofline"]["traffic"] = measured_traffic(
+            "cfg2-paged" + ("" if args.separate_append else "-fused"))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(bench, args.cpu_seconds)
     if not args.no_hbm_probe:

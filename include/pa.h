@@ -248,6 +248,25 @@ pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dt
                     int32_t partition_tokens, float* d_out, void* d_workspace,
                     size_t workspace_bytes, void* stream);
 
+/* One decode step of a layer in one launch: pa_append_kv of each sequence's
+ * new token, then pa_decode over contexts that end with it ([KVP]
+ * Observation-1: every running request grows by one token per iteration).
+ *   d_k, d_v:   device [num_seqs][num_kv_heads][head_dim], kv_dtype, 16-byte
+ *               aligned: the new token of sequence s.
+ *   d_slots:    device int32 [num_seqs]: slot of sequence s's new token, as
+ *               pa_reserve handed it out, i.e. the slot of position L_s - 1;
+ *               < 0: sequence s appends nothing (its cache is read as is).
+ * The other arguments, the result and the errors are those of pa_decode.  The
+ * cache afterwards equals pa_append_kv's; the output equals pa_decode's after
+ * that append, bit for bit. */
+pa_status pa_append_decode(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                           const int32_t* d_slots, const void* d_q, pa_dtype q_dtype,
+                           int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                           int32_t table_stride, const int32_t* d_req_ids,
+                           const int32_t* d_context_lens, int32_t num_seqs, int32_t max_context,
+                           int32_t partition_tokens, float* d_out, void* d_workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Message of the calling thread's last error ("" if none). */
 const char* pa_last_error(void);
 

@@ -41,7 +41,8 @@ EXPORTS = (
     "pa_cache_bytes", "pa_bytes_per_token", "pa_create_pool", "pa_destroy_pool",
     "pa_set_free_order", "pa_seq_add", "pa_seq_fork", "pa_seq_free", "pa_reserve",
     "pa_get_block_tables", "pa_get_stats", "pa_copy_blocks", "pa_append_kv",
-    "pa_decode_partition_tokens", "pa_decode_workspace_bytes", "pa_decode", "pa_last_error",
+    "pa_decode_partition_tokens", "pa_decode_workspace_bytes", "pa_decode", "pa_append_decode",
+    "pa_last_error",
 )
 
 
@@ -106,6 +107,9 @@ def load() -> ctypes.CDLL:
         "pa_decode_workspace_bytes": (ctypes.c_size_t, [_vp, _i32, _i32, _i32, _i32]),
         "pa_decode": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _i32, ctypes.c_float, _vp, _i32,
                                      _vp, _vp, _i32, _i32, _i32, _vp, _vp, ctypes.c_size_t, _vp]),
+        "pa_append_decode": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
+                                            ctypes.c_float, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
+                                            _vp, _vp, ctypes.c_size_t, _vp]),
         "pa_last_error": (ctypes.c_char_p, []),
     }
     assert set(sig) == set(EXPORTS)

@@ -19,7 +19,9 @@
 // Decode design (the pages give no kernel; this one is built for gfx950):
 //   * one 256-thread workgroup (4 waves of 64) per (sequence, KV head, context
 //     partition); the G <= 16 query heads of the GQA group share every K/V
-//     load; waves take the partition's 16-token chunks round-robin;
+//     load; waves take the partition's 16-token chunks round-robin from its
+//     end, so that the context's last chunk (the one that may be partly
+//     filled, and the one the fused append patches) is a wave's first;
 //   * per chunk, S = K q^T is one 16x16 MFMA tile (16 tokens x 16 head
 //     columns, the unused columns hold zero queries): bf16 caches use
 //     v_mfma_f32_16x16x32_bf16 over head_dim/32 steps, fp32 caches
@@ -52,10 +54,6 @@ constexpr int kMergeThreads = 64;
 constexpr int kChunk = 16;        // tokens per MFMA tile
 constexpr int kMaxGroup = 16;     // query heads per KV head the tile can hold
 constexpr int kMaxMergeLds = 64 * 1024;
-#ifndef PA_DECODE_DEPTH
-#define PA_DECODE_DEPTH 0
-#endif
-constexpr int kDepth = PA_DECODE_DEPTH;  // chunks in flight per wave while one is processed
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -92,6 +90,10 @@ __device__ __forceinline__ uint2 ld8(const char* p) { return *reinterpret_cast<c
 // decode and the loads are marked non-temporal (streamed past the caches'
 // retention); shared blocks (several samples of one prompt) are read with
 // ordinary loads so that the repeats hit in L2 / Infinity Cache.
+// Read-only during a launch: a uniform read through the constant address
+// space is always a scalar (SMEM) load, whatever else the kernel stores.
+typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 template <bool NT>
@@ -132,9 +134,10 @@ struct Geo {
 // ---------------------------------------------------------------------------
 // decode: one workgroup per (sequence, KV head, partition)
 // ---------------------------------------------------------------------------
-#ifndef PA_DECODE_WAVES_PER_EU
-#define PA_DECODE_WAVES_PER_EU 0
-#endif
+// bf16 caches with blocks of at least a chunk fit 128 VGPRs, i.e. four waves
+// per SIMD (the occupancy the HBM stream needs); the others would spill.
+template <int KIND, int BS>
+constexpr int decode_min_waves_per_eu() { return KIND == kBF16 && BS >= kChunk ? 4 : 1; }
 // LDS bytes of the wave merge: per wave, G maxima, G sums and G x D partial
 // outputs.
 __host__ __device__ constexpr int merge_lds_bytes(int waves, int G, int D) {
@@ -143,9 +146,7 @@ __host__ __device__ constexpr int merge_lds_bytes(int waves, int G, int D) {
 
 template <int KIND, int D, int BS, int W, bool NT>
 __global__ __launch_bounds__(W * kWave)
-#if PA_DECODE_WAVES_PER_EU > 0
-__attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU, PA_DECODE_WAVES_PER_EU)))
-#endif
+__attribute__((amdgpu_waves_per_eu(decode_min_waves_per_eu<KIND, BS>())))
 void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
   using GG = Geo<KIND, D, BS>;
   constexpr int NX = GG::NX, NN = GG::NN, TILE = GG::TILE, ELT = GG::ELT;
@@ -181,6 +182,34 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n = lane & 15;   // head column of S / row of the K tile
   const int j4 = lane >> 4;  // lane group: tokens 4*j4 .. 4*j4+3
+
+  // Wave w takes chunks ce-1-w, ce-1-w-W, ... down to cb.  The last chunk of
+  // the context, the only one that may be partly filled and the one that
+  // holds the appended token, is then the first chunk of wave 0.
+  //
+  // Fused append: token L-1 arrives in new_k / new_v.  Wave 0 loads the row
+  // into registers next to q, so its latency overlaps everything up to the
+  // first chunk, where selects put it into the operand registers; it keeps a
+  // copy in LDS and stores the row into the cache after its loop.  (Narrow
+  // row stores at the end cost less than writing the whole chunk back from
+  // the operand registers, whose writes would interleave with the reads.)
+  constexpr int kRowVec = D * ELT / 16;  // 16-byte pieces of one row
+  __shared__ uint4 sm_new[2 * kRowVec];  // K pieces, then V pieces
+  const bool own_new = a.new_k != nullptr && wave == 0 && ce == nch && a.new_slots[s] >= 0;
+  uint4 nk[NX];      // lane (n, j4): K pieces x*4+j4 of the new row
+  uint32_t nv[NN];   // lane (n, j4): V element nb*16+n of the new row
+  if (own_new) {
+    const int64_t src = (static_cast<int64_t>(s) * hkv + kvh) * D * ELT;
+    const char* nk_row = static_cast<const char*>(a.new_k) + src;
+    const char* nv_row = static_cast<const char*>(a.new_v) + src;
+#pragma unroll
+    for (int x = 0; x < NX; ++x) nk[x] = ld16(nk_row + (x * 4 + j4) * 16);
+#pragma unroll
+    for (int nb = 0; nb < NN; ++nb) {
+      if constexpr (KIND == kBF16) nv[nb] = *reinterpret_cast<const uint16_t*>(nv_row + (nb * 16 + n) * 2);
+      else nv[nb] = *reinterpret_cast<const uint32_t*>(nv_row + (nb * 16 + n) * 4);
+    }
+  }
 
   // q operand: head n of the group, zero beyond G (the row address is
   // clamped to a head of this group so that it always exists)
@@ -221,21 +250,33 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NN; ++nb) acc[nb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto load = [&](int c, uint4 (&kk)[NX], VOp (&vv)[NN]) {
+  // Wave-uniform block of chunk c (blocks of at least a chunk): a scalar load
+  // of the table entry through the constant address space.  readfirstlane
+  // keeps the index scalar even where the compiler cannot prove it uniform.
+  auto block_of_chunk = [&](int c) -> int64_t {
+    const int blk = __builtin_amdgcn_readfirstlane((c * kChunk) / BS);
+    return geo.paged ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(
+                           reinterpret_cast<const_i32_ptr>(reinterpret_cast<uintptr_t>(table))[blk]))
+                     : first_block + blk;
+  };
+  // u: the chunk's block when BS >= kChunk (from block_of_chunk)
+  auto load = [&](int c, int64_t u, uint4 (&kk)[NX], VOp (&vv)[NN]) {
     if constexpr (BS >= kChunk) {
       // the chunk lies in one block: a wave-uniform tile base plus a 32-bit
       // lane offset (rows past the context stay inside the tile)
-      const int blk = (c * kChunk) / BS;
-      const int64_t u = geo.paged ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(table[blk]))
-                                  : first_block + blk;
       const int64_t tile = (u * hkv + kvh) * TILE;
       const char* kt = kl + tile;
       const char* vt = vl + tile;
       const int row0 = (c * kChunk) % BS;
-      const uint32_t ko = static_cast<uint32_t>((j4 * BS + row0 + n) * 16);
+      // the empty asm keeps each lane offset a 32-bit value inside the loop,
+      // so that the loads use a scalar base plus a 32-bit vector offset
+      // instead of a 64-bit vector address per lane
+      uint32_t ko = static_cast<uint32_t>((j4 * BS + row0 + n) * 16);
+      asm volatile("" : "+v"(ko));
 #pragma unroll
       for (int x = 0; x < NX; ++x) kk[x] = kv16<NT>(kt + ko + x * 4 * BS * 16);
-      const uint32_t vo = static_cast<uint32_t>((n * BS + row0 + 4 * j4) * ELT);
+      uint32_t vo = static_cast<uint32_t>((n * BS + row0 + 4 * j4) * ELT);
+      asm volatile("" : "+v"(vo));
 #pragma unroll
       for (int nb = 0; nb < NN; ++nb) {
         if constexpr (KIND == kBF16) vv[nb] = kv8<NT>(vt + vo + nb * 16 * BS * ELT);
@@ -258,18 +299,52 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
     }
   };
 
-  // The chunk being processed plus DEPTH chunks whose loads are in flight,
-  // in a ring of register buffers; the rotation is unrolled so that every
-  // buffer index is a constant.  Loads past the partition re-read its last
-  // chunk (an L2 hit) instead of branching: a branch around loads makes the
-  // wait for the current chunk also wait for the newer loads.
-  constexpr int DEPTH = kDepth;
-  uint4 kbuf[DEPTH + 1][NX];
-  VOp vbuf[DEPTH + 1][NN];
-  int c = cb + wave;
+  // the new token's K and V replace what the cache holds at position L-1
+  // (selects only: a reference to a runtime-chosen component would send the
+  // operand registers to scratch memory); the lanes holding them copy them
+  // to LDS for the store after the loop
+  auto patch_new = [&](int c, uint4 (&kk)[NX], VOp (&vv)[NN]) {
+    const bool krow = c * kChunk + n == L - 1;
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load(min(c + d * kWaves, ce - 1), kbuf[d], vbuf[d]);
-  auto process = [&](int c, uint4 (&kop)[NX], VOp (&vop)[NN]) {
+    for (int x = 0; x < NX; ++x) {
+      kk[x].x = krow ? nk[x].x : kk[x].x;
+      kk[x].y = krow ? nk[x].y : kk[x].y;
+      kk[x].z = krow ? nk[x].z : kk[x].z;
+      kk[x].w = krow ? nk[x].w : kk[x].w;
+    }
+    if (krow) {
+#pragma unroll
+      for (int x = 0; x < NX; ++x) sm_new[x * 4 + j4] = nk[x];
+    }
+    const int e = L - 1 - (c * kChunk + 4 * j4);
+#pragma unroll
+    for (int nb = 0; nb < NN; ++nb) {
+      const uint32_t h = nv[nb];
+      if constexpr (KIND == kBF16) {
+        const uint32_t x = vv[nb].x, y = vv[nb].y;
+        vv[nb].x = e == 0 ? ((x & 0xFFFF0000u) | h) : (e == 1 ? ((x & 0x0000FFFFu) | (h << 16)) : x);
+        vv[nb].y = e == 2 ? ((y & 0xFFFF0000u) | h) : (e == 3 ? ((y & 0x0000FFFFu) | (h << 16)) : y);
+      } else {
+        vv[nb].x = e == 0 ? h : vv[nb].x;
+        vv[nb].y = e == 1 ? h : vv[nb].y;
+        vv[nb].z = e == 2 ? h : vv[nb].z;
+        vv[nb].w = e == 3 ? h : vv[nb].w;
+      }
+    }
+    if (e >= 0 && e < 4) {
+      char* nv_lds = reinterpret_cast<char*>(sm_new + kRowVec);
+#pragma unroll
+      for (int nb = 0; nb < NN; ++nb) {
+        if constexpr (KIND == kBF16) reinterpret_cast<uint16_t*>(nv_lds)[nb * 16 + n] = static_cast<uint16_t>(nv[nb]);
+        else reinterpret_cast<uint32_t*>(nv_lds)[nb * 16 + n] = nv[nb];
+      }
+    }
+  };
+
+  // one chunk: S = K q^T on the MFMA, online softmax, O += P V.  FIRST marks
+  // a wave's first chunk, the only one that can be partly filled.
+  auto process = [&](auto first, int c, uint4 (&kop)[NX], VOp (&vop)[NN]) {
+    constexpr bool kFirst = decltype(first)::value;
     // S[token 4*j4+i][head n]
     floatx4_t S = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -288,7 +363,7 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = S[i] * c2;
     const int t0 = c * kChunk + 4 * j4;
-    if ((c + 1) * kChunk > L) {
+    if (kFirst && (c + 1) * kChunk > L) {
       // last, partly filled chunk: rows past the context hold whatever the
       // cache held (possibly NaN or Inf patterns): zero weight and zero V
 #pragma unroll
@@ -314,12 +389,14 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
     mx = fmaxf(mx, xor16(mx));
     mx = fmaxf(mx, xor32(mx));
     const float mn = fmaxf(m, mx);
-    const float alpha = fexp2(m - mn);
+    // a wave's first chunk starts from m = -inf, acc = 0 and lsum = 0, so
+    // there is nothing to rescale (and acc need not be live yet)
+    const float alpha = kFirst ? 0.0f : fexp2(m - mn);
     m = mn;
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = fexp2(sc[i] - mn);
-    if (__any(alpha != 1.0f)) {
+    if (!kFirst && __any(alpha != 1.0f)) {
       // rows of acc belong to heads 4*j4+i: fetch their factors
       float ai[4];
 #pragma unroll
@@ -358,15 +435,27 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
       }
     }
   };
-  while (c < ce) {
-#pragma unroll
-    for (int d = 0; d <= DEPTH; ++d) {
-      if (c >= ce) break;
-      load(min(c + DEPTH * kWaves, ce - 1), kbuf[(d + DEPTH) % (DEPTH + 1)],
-           vbuf[(d + DEPTH) % (DEPTH + 1)]);
-      process(c, kbuf[d], vbuf[d]);
-      c += kWaves;
-    }
+  // The block of the next chunk is fetched one chunk ahead of its loads (an
+  // index clamped into the partition rather than a branch).
+  uint4 kbuf[NX];
+  VOp vbuf[NN];
+  int c = ce - 1 - wave;
+  int64_t u_next = 0;
+  if constexpr (BS >= kChunk) u_next = block_of_chunk(max(c, cb));
+  if (c >= cb) {
+    const int64_t u = u_next;
+    if constexpr (BS >= kChunk) u_next = block_of_chunk(max(c - kWaves, cb));
+    load(c, u, kbuf, vbuf);
+    if (own_new) patch_new(c, kbuf, vbuf);
+    process(std::true_type{}, c, kbuf, vbuf);
+    c -= kWaves;
+  }
+  while (c >= cb) {
+    const int64_t u = u_next;
+    if constexpr (BS >= kChunk) u_next = block_of_chunk(max(c - kWaves, cb));
+    load(c, u, kbuf, vbuf);
+    process(std::false_type{}, c, kbuf, vbuf);
+    c -= kWaves;
   }
 
   // weight sum of head n over the wave's tokens, then merge the waves:
@@ -410,6 +499,30 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
         a.ws[prow * 2] = mx;
         a.ws[prow * 2 + 1] = Lt;
       }
+    }
+  }
+  // the appended row into the cache: K as 16-byte pieces, V element by
+  // element ([D][BS] tiles)
+  if (own_new && lane < kRowVec) {
+    constexpr int VE = GG::VE;
+    const int slot = a.new_slots[s];
+    const int q = lane;
+    const int64_t u = slot / BS;
+    const int o = slot % BS;
+    const int64_t tile = static_cast<int64_t>(a.layer) * geo.layer_bytes + (u * hkv + kvh) * TILE;
+    *reinterpret_cast<uint4*>(geo.k_base + tile + (q * BS + o) * 16) = sm_new[q];
+    const uint4 vw = sm_new[kRowVec + q];
+    char* vt = geo.v_base + tile;
+    const uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
+    if constexpr (KIND == kBF16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<uint16_t*>(vt + ((q * VE + 2 * e) * BS + o) * 2) = static_cast<uint16_t>(w[e] & 0xFFFFu);
+        *reinterpret_cast<uint16_t*>(vt + ((q * VE + 2 * e + 1) * BS + o) * 2) = static_cast<uint16_t>(w[e] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *reinterpret_cast<uint32_t*>(vt + ((q * VE + e) * BS + o) * 4) = w[e];
     }
   }
 }

@@ -50,6 +50,11 @@ struct DecodeArgs {
   int32_t table_stride = 0;
   int32_t partition_chunks = 0;      // 16-token chunks per partition
   int32_t num_partitions = 1;
+  // fused append (pa_append_decode): token L_s - 1 of sequence s is
+  // new_k[s] / new_v[s] ([B][Hkv][D]), stored to slot new_slots[s] (< 0: none)
+  const void* new_k = nullptr;
+  const void* new_v = nullptr;
+  const int32_t* new_slots = nullptr;
   int32_t waves = 4;                 // waves per workgroup: 4 or 8
   int32_t streaming = 1;             // non-temporal K/V loads (no block is shared)
   float scale = 1.0f;

@@ -261,39 +261,44 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t 
                                     num_partitions(max_context, pt));
 }
 
-pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
-                    int32_t num_q_heads, float scale, const int32_t* d_block_tables,
-                    int32_t table_stride, const int32_t* d_req_ids,
-                    const int32_t* d_context_lens, int32_t num_seqs, int32_t max_context,
-                    int32_t partition_tokens, float* d_out, void* d_workspace,
-                    size_t workspace_bytes, void* stream) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "decode: null pool");
+}  // extern "C"
+
+namespace {
+pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void* d_k_new,
+                      const void* d_v_new, const int32_t* d_slots, const void* d_q,
+                      pa_dtype q_dtype, int32_t num_q_heads, float scale,
+                      const int32_t* d_block_tables, int32_t table_stride,
+                      const int32_t* d_req_ids, const int32_t* d_context_lens, int32_t num_seqs,
+                      int32_t max_context, int32_t partition_tokens, float* d_out,
+                      void* d_workspace, size_t workspace_bytes, void* stream) {
+  const std::string w(who);
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null pool");
   const pa_pool_desc& d = pool->desc;
-  if (layer < 0 || layer >= d.num_layers) return fail(PA_ERR_INVALID_ARG, "decode: layer out of range");
-  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "decode: negative num_seqs");
+  if (layer < 0 || layer >= d.num_layers) return fail(PA_ERR_INVALID_ARG, w + ": layer out of range");
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, w + ": negative num_seqs");
   if (num_seqs == 0) return PA_OK;
   if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
-    return fail(PA_ERR_INVALID_ARG, "decode: num_q_heads must be a positive multiple of num_kv_heads");
+    return fail(PA_ERR_INVALID_ARG, w + ": num_q_heads must be a positive multiple of num_kv_heads");
   if (q_dtype != d.kv_dtype)
-    return fail(PA_ERR_UNSUPPORTED, "decode: q_dtype must equal the cache's kv_dtype");
+    return fail(PA_ERR_UNSUPPORTED, w + ": q_dtype must equal the cache's kv_dtype");
   if (num_q_heads / d.num_kv_heads > 16)
-    return fail(PA_ERR_UNSUPPORTED, "decode: GQA groups of more than 16 query heads");
+    return fail(PA_ERR_UNSUPPORTED, w + ": GQA groups of more than 16 query heads");
   if (max_context < 0 || max_context > d.max_seq_len)
-    return fail(PA_ERR_INVALID_ARG, "decode: max_context must be in [0, max_seq_len]");
+    return fail(PA_ERR_INVALID_ARG, w + ": max_context must be in [0, max_seq_len]");
   if (bad_partition(pool, partition_tokens))
     return fail(PA_ERR_INVALID_ARG,
-                "decode: partition_tokens must be 0 or a positive multiple of 16 and of block_size");
+                w + ": partition_tokens must be 0 or a positive multiple of 16 and of block_size");
   if (d_q == nullptr || d_context_lens == nullptr || d_out == nullptr)
-    return fail(PA_ERR_INVALID_ARG, "decode: null device pointer");
-  if (reinterpret_cast<uintptr_t>(d_q) & 15) return fail(PA_ERR_INVALID_ARG, "decode: q must be 16-byte aligned");
+    return fail(PA_ERR_INVALID_ARG, w + ": null device pointer");
+  if (reinterpret_cast<uintptr_t>(d_q) & 15) return fail(PA_ERR_INVALID_ARG, w + ": q must be 16-byte aligned");
   const int32_t bs = d.block_size;
   const int32_t nblk = (max_context + bs - 1) / bs;
   if (d.layout == PA_PAGED) {
-    if (d_block_tables == nullptr) return fail(PA_ERR_INVALID_ARG, "decode: null block tables");
+    if (d_block_tables == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null block tables");
     if (table_stride < nblk)
-      return fail(PA_ERR_INVALID_ARG, "decode: table_stride is shorter than ceil(max_context / block_size)");
+      return fail(PA_ERR_INVALID_ARG, w + ": table_stride is shorter than ceil(max_context / block_size)");
   }
-  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "decode: scale is NaN");
+  if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, w + ": scale is NaN");
   const int64_t grid = static_cast<int64_t>(num_seqs) * d.num_kv_heads;
   pa::DecodeArgs a;
   a.q = d_q;
@@ -309,24 +314,59 @@ pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dt
   a.partition_chunks = pt / 16;
   a.num_partitions = num_partitions(max_context, pt);
   a.waves = PA_DECODE_WAVES;
+  if (d_k_new != nullptr) {
+    a.new_k = d_k_new;
+    a.new_v = d_v_new;
+    a.new_slots = d_slots;
+  }
   a.streaming = pool->alloc.shared_blocks() == 0 ? 1 : 0;
   a.scale = scale;
-  if (grid * a.num_partitions > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "decode: launch too large");
+  if (grid * a.num_partitions > INT32_MAX) return fail(PA_ERR_INVALID_ARG, w + ": launch too large");
   const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, d.head_dim, a.num_partitions);
   if (need > 0) {
     if (d_workspace == nullptr || workspace_bytes < need)
-      return fail(PA_ERR_WORKSPACE, "decode: workspace needs " + std::to_string(need) + " bytes, got " +
+      return fail(PA_ERR_WORKSPACE, w + ": workspace needs " + std::to_string(need) + " bytes, got " +
                                         std::to_string(d_workspace ? workspace_bytes : 0));
     if (reinterpret_cast<uintptr_t>(d_workspace) & 15)
-      return fail(PA_ERR_INVALID_ARG, "decode: workspace must be 16-byte aligned");
+      return fail(PA_ERR_INVALID_ARG, w + ": workspace must be 16-byte aligned");
     a.ws = static_cast<float*>(d_workspace);
   }
   bool supported = true;
   const int kind = d.kv_dtype == PA_BF16 ? pa::kBF16 : pa::kF32;
   hipError_t e = pa::launch_decode(pool->geom, kind, a, &supported, static_cast<hipStream_t>(stream));
-  if (!supported) return fail(PA_ERR_UNSUPPORTED, "decode: no kernel for this shape");
-  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("decode: ") + hipGetErrorString(e));
+  if (!supported) return fail(PA_ERR_UNSUPPORTED, w + ": no kernel for this shape");
+  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string(w + ": ") + hipGetErrorString(e));
   return PA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
+                    int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                    int32_t table_stride, const int32_t* d_req_ids,
+                    const int32_t* d_context_lens, int32_t num_seqs, int32_t max_context,
+                    int32_t partition_tokens, float* d_out, void* d_workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode_impl("decode", pool, layer, nullptr, nullptr, nullptr, d_q, q_dtype, num_q_heads,
+                     scale, d_block_tables, table_stride, d_req_ids, d_context_lens, num_seqs,
+                     max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream);
+}
+
+pa_status pa_append_decode(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                           const int32_t* d_slots, const void* d_q, pa_dtype q_dtype,
+                           int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                           int32_t table_stride, const int32_t* d_req_ids,
+                           const int32_t* d_context_lens, int32_t num_seqs, int32_t max_context,
+                           int32_t partition_tokens, float* d_out, void* d_workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (d_k == nullptr || d_v == nullptr || d_slots == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "append_decode: null k, v or slots");
+  if ((reinterpret_cast<uintptr_t>(d_k) | reinterpret_cast<uintptr_t>(d_v)) & 15)
+    return fail(PA_ERR_INVALID_ARG, "append_decode: k and v must be 16-byte aligned");
+  return decode_impl("append_decode", pool, layer, d_k, d_v, d_slots, d_q, q_dtype, num_q_heads,
+                     scale, d_block_tables, table_stride, d_req_ids, d_context_lens, num_seqs,
+                     max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream);
 }
 
 const char* pa_last_error(void) { return g_err.c_str(); }

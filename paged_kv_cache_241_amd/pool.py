@@ -195,8 +195,13 @@ class Pool:
                                                       max_context, partition_tokens))
 
     def decode(self, layer: int, q, scale: float, block_tables, context_lens, max_context: int,
-               out=None, partition_tokens: int = 0, req_ids=None, workspace=None, stream=None):
-        """Decode attention for q [B][Hq][D]; returns out fp32 [B][Hq][D]."""
+               out=None, partition_tokens: int = 0, req_ids=None, workspace=None, stream=None,
+               append=None):
+        """Decode attention for q [B][Hq][D]; returns out fp32 [B][Hq][D].
+
+        ``append=(k, v, slots)`` stores each sequence's new token first, in the
+        same launch (pa_append_decode); k, v are [B][Hkv][D], slots int32 [B].
+        """
         import torch
 
         assert self.k_cache is not None, "host-only pool"
@@ -218,10 +223,19 @@ class Pool:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        capi.check(self.lib.pa_decode(
-            self.handle, layer, q.data_ptr(), _DTYPES[self.kv_dtype], hq, float(scale),
-            block_tables.data_ptr() if self.layout == "paged" else None, stride,
-            req_ids.data_ptr() if req_ids is not None else None, context_lens.data_ptr(), b,
-            int(max_context), int(partition_tokens), out.data_ptr(), ws_ptr, ws_bytes,
-            _stream_handle(stream)), "pa_decode")
+        args = (q.data_ptr(), _DTYPES[self.kv_dtype], hq, float(scale),
+                block_tables.data_ptr() if self.layout == "paged" else None, stride,
+                req_ids.data_ptr() if req_ids is not None else None, context_lens.data_ptr(), b,
+                int(max_context), int(partition_tokens), out.data_ptr(), ws_ptr, ws_bytes,
+                _stream_handle(stream))
+        if append is None:
+            capi.check(self.lib.pa_decode(self.handle, layer, *args), "pa_decode")
+        else:
+            k, v, slots = append
+            for t in (k, v):
+                assert t.is_cuda and t.is_contiguous() and t.dtype == self.torch_dtype
+                assert tuple(t.shape) == (b, self.num_kv_heads, self.head_dim)
+            assert slots.is_cuda and slots.dtype == torch.int32 and tuple(slots.shape) == (b,)
+            capi.check(self.lib.pa_append_decode(self.handle, layer, k.data_ptr(), v.data_ptr(),
+                                                 slots.data_ptr(), *args), "pa_append_decode")
         return out

@@ -57,7 +57,8 @@ class Case:
     """One workload built on the GPU: pool, tables, lengths, q, and values."""
 
     def __init__(self, cfg: W.Config, layout: str = "paged", layers=(0,), num_layers=None,
-                 free_seed=None, fill=None, values=None, init=None, device="cuda"):
+                 free_seed=None, fill=None, values=None, init=None, step_append=True,
+                 device="cuda"):
         self.cfg = cfg
         self.pl = pl = W.plan(cfg)
         self.layers = tuple(layers)
@@ -80,8 +81,13 @@ class Case:
         self.alloc = _Tracked(self.pool)
         self.rids = {}
         self.log = []
+        self._append = True
         W.run_ops(pl.ops, self.alloc, self.rids, on_reserve=self._on_reserve)
+        # the decode step's reserve; its appends may be left to the caller
+        # (step_slots / step_rows then say what to append)
+        self._append = step_append
         W.run_ops([pl.step], self.alloc, self.rids, on_reserve=self._on_reserve)
+        self._append = True
         torch.cuda.synchronize()
         self.batch_rids = [self.rids[h] for h in pl.batch_handles]
         if layout == "paged":
@@ -113,6 +119,10 @@ class Case:
                 idx.extend(self.pl.rows[h][p0:p0 + c])
                 sl.extend(int(x) for x in slots[k:k + c])
             k += c
+        if not self._append:
+            self.step_slots = torch.tensor(sl, dtype=torch.int32, device=dev)
+            self.step_rows = torch.tensor(idx, dtype=torch.int64, device=dev)
+            return
         if not idx:
             return
         idx_t = torch.tensor(idx, dtype=torch.int64, device=dev)
@@ -122,14 +132,22 @@ class Case:
             self.pool.append_kv(l, kr.index_select(0, idx_t).contiguous(),
                                 vr.index_select(0, idx_t).contiguous(), sl_t)
 
-    def decode(self, layer=None, partition_tokens=0, q=None, req_ids=True):
+    def decode(self, layer=None, partition_tokens=0, q=None, req_ids=True, append=None):
         layer = self.layers[0] if layer is None else layer
         q = self.vals[layer][0] if q is None else q
         out = self.pool.decode(layer, q, self.scale, self.tables, self.lens, self.max_context,
                                partition_tokens=partition_tokens,
-                               req_ids=self.req_ids if (self.layout != "paged" and req_ids) else None)
+                               req_ids=self.req_ids if (self.layout != "paged" and req_ids) else None,
+                               append=append)
         torch.cuda.synchronize()
         return out
+
+    def step_kv(self, layer=None):
+        """The decode step's new K and V rows, [B][Hkv][D], batch order."""
+        layer = self.layers[0] if layer is None else layer
+        _, kr, vr = self.vals[layer]
+        return (kr.index_select(0, self.step_rows).contiguous(),
+                vr.index_select(0, self.step_rows).contiguous())
 
     def logical(self, s: int, layer=None):
         """fp64 (q, K, V) of batch sequence s straight from the generator."""

@@ -1,0 +1,52 @@
+"""bench.py's byte accounting (CPU only: a host-only pool, no device calls)."""
+
+import os
+import sys
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+import bench  # noqa: E402
+from workloads import get  # noqa: E402
+
+
+def _pool(bs):
+    from paged_kv_cache_241_amd.pool import Pool
+    return Pool(num_layers=1, num_blocks=64, block_size=bs, num_kv_heads=2, head_dim=64,
+                kv_dtype="bf16", layout="paged", max_seqs=8, max_seq_len=256, host_only=True)
+
+
+def test_unique_fraction_counts_shared_blocks_once():
+    pool = _pool(8)
+    a = pool.add()
+    pool.reserve([a], [20])          # blocks of 8 + 8 + 4 rows
+    b = pool.fork(a)                 # shares all three
+    pool.reserve([b], [1])           # the partly filled last block is copied: 8 + 8 + 5
+    fake = SimpleNamespace(layout="paged", pool=pool, rids_np=np.array([a, b], np.int32),
+                           cfg=SimpleNamespace(block_size=8))
+    # logical rows 20 + 21; distinct: two shared full blocks, a's 4 rows, b's 5
+    assert bench.unique_kv_fraction(fake) == pytest.approx((8 + 8 + 4 + 5) / 41)
+
+
+def test_unique_fraction_is_one_without_sharing():
+    pool = _pool(16)
+    rids = [pool.add() for _ in range(3)]
+    pool.reserve(rids, [17, 40, 1])
+    fake = SimpleNamespace(layout="paged", pool=pool, rids_np=np.array(rids, np.int32),
+                           cfg=SimpleNamespace(block_size=16))
+    assert bench.unique_kv_fraction(fake) == 1.0
+    assert bench.unique_kv_fraction(SimpleNamespace(layout="contiguous")) == 1.0
+
+
+def test_algorithmic_bytes_of_the_llama_decode_launch():
+    cfg = get(2)
+    lens = np.full(64, 1024)
+    kv = 64 * 1024 * 8 * 128 * 2 * 2
+    other = 64 * 32 * 128 * (2 + 4) + 64 * 64 * 4 + 64 * 4
+    assert bench.algorithmic_bytes(cfg, lens, False) == kv + other
+    # fused: the new K and V rows read and written, plus the slots
+    assert bench.algorithmic_bytes(cfg, lens, True) == kv + other + 64 * 8 * 128 * 2 * 2 * 2 + 64 * 4
+    assert bench.algorithmic_bytes(cfg, lens, False, 0.5) == kv // 2 + other

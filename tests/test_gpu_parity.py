@@ -300,3 +300,47 @@ def test_append_and_decode_over_several_layers():
     case = Case(cfg, layers=(0, 3), num_layers=4)
     for layer in (0, 3):
         _check(case, case.decode(layer=layer), range(cfg.batch), layer=layer)
+
+
+# --------------------------------------------------------------------------
+# fused append + decode (one launch per layer)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid,over,layout,pt", [
+    (2, {"batch": 6, "num_blocks": 6 * 64 + 9}, "paged", 0),
+    (3, {"batch": 8}, "paged", 64),
+    (4, {"batch": 5, "num_blocks": 400}, "contiguous", 0),
+    (5, {"batch": 16, "prompt_len": 300, "private_len": 1, "num_blocks": 300}, "paged", 128),
+    (1, {"kv_dtype": "f32"}, "paged", 0),
+])
+def test_fused_append_decode_equals_separate_calls(cid, over, layout, pt):
+    cfg = W.get(cid, **over)
+    # zero-filled pools, so that rows nobody writes compare equal too
+    sep = Case(cfg, layout=layout, step_append=False, fill=0.0)
+    fus = Case(cfg, layout=layout, step_append=False, fill=0.0)
+    assert torch.equal(sep.step_slots, fus.step_slots)
+    k, v = sep.step_kv()
+    sep.pool.append_kv(0, k, v, sep.step_slots)
+    a = sep.decode(partition_tokens=pt)
+    b = fus.decode(partition_tokens=pt, append=(k, v, fus.step_slots))
+    assert torch.equal(a, b)
+    assert torch.equal(sep.pool.k_cache, fus.pool.k_cache)
+    assert torch.equal(sep.pool.v_cache, fus.pool.v_cache)
+    _check(fus, b, range(cfg.batch))
+    if cid == 5:
+        # the step's first private write copied each prompt's shared last block
+        assert fus.pool.stats()["cow_copies"] == (cfg.batch // cfg.samples) * (cfg.samples - 1)
+
+
+def test_fused_append_skips_negative_slots():
+    cfg = W.get(2, batch=5, num_blocks=5 * 64 + 5)
+    case = Case(cfg, step_append=False)
+    k, v = case.step_kv()
+    slots = case.step_slots.clone()
+    # sequences 1 and 3 get their token through a separate append first
+    sub = torch.tensor([1, 3], device="cuda")
+    case.pool.append_kv(0, k[sub].contiguous(), v[sub].contiguous(), slots[sub].contiguous())
+    slots[1] = -1
+    slots[3] = -1
+    out = case.decode(append=(k, v, slots))
+    _check(case, out, range(cfg.batch))
