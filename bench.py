@@ -48,6 +48,9 @@ def parse():
                     help="pa_append_kv then pa_decode per layer instead of one pa_append_decode")
     ap.add_argument("--layers", type=int, default=0, help="layer pools rotated (0: workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget")
+    ap.add_argument("--swap-seqs", type=int, default=0, metavar="N",
+                    help="after the timed steps, swap N requests out to pinned host memory "
+                         "and back in, and report the rates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-probe", action="store_true",
                     help="skip the achievable-read-bandwidth probe (bench_read_probe)")
@@ -315,6 +318,34 @@ class Bench:
         return lens
 
 
+def swap_probe(bench, n: int) -> dict:
+    """Swap the first n requests of the batch out to pinned host images and
+    back in (pa_swap_out / pa_swap_in), timed with HIP events on the stream
+    the calls are queued on.  The images hold every rotated layer's blocks."""
+    import torch
+
+    pool = bench.pool
+    rids = bench.batch[:n]
+    images = [torch.empty(pool.swap_bytes(r), dtype=torch.uint8, pin_memory=True) for r in rids]
+    total = sum(im.numel() for im in images)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record(bench.stream)
+    for r, im in zip(rids, images):
+        pool.swap_out(r, im, bench.stream)
+    ev[1].record(bench.stream)
+    for r, im in zip(rids, images):
+        pool.swap_in(r, im, bench.stream)
+    ev[2].record(bench.stream)
+    torch.cuda.synchronize()
+    bench.tables_dirty = True
+    t_out = ev[0].elapsed_time(ev[1]) / 1e3
+    t_in = ev[1].elapsed_time(ev[2]) / 1e3
+    return {"seqs": n, "bytes": total, "out_ms": round(t_out * 1e3, 3), "in_ms": round(t_in * 1e3, 3),
+            "out_gbs": round(total / t_out / 1e9, 2), "in_gbs": round(total / t_in / 1e9, 2),
+            "image": "pinned host memory"}
+
+
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "pa_decode_llama3-8b_b64_ctx1024_hbm_counters.md")
 
 
@@ -543,6 +574,8 @@ def main():
             "cfg2-paged" + ("" if args.separate_append else "-fused"))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(bench, args.cpu_seconds)
+    if args.swap_seqs:
+        res["swap"] = swap_probe(bench, args.swap_seqs)
     if not args.no_hbm_probe:
         probe = hbm_probe()
         if probe:

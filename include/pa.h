@@ -103,13 +103,15 @@ typedef struct pa_stats {
   int64_t free_blocks;      /* paged: blocks on the free list */
   int64_t used_blocks;      /* paged: blocks held by at least one request */
   int64_t tokens;           /* token rows physically held (a shared row counts once) */
-  int64_t logical_tokens;   /* sum of live requests' lengths */
+  int64_t logical_tokens;   /* sum of resident requests' lengths */
   int64_t reserved_tokens;  /* paged: used_blocks*block_size; contiguous: live*S */
-  int64_t live_seqs;
+  int64_t live_seqs;        /* resident requests (swapped-out ones not counted) */
   int64_t cow_copies;       /* copy-on-write copies made since creation */
   int64_t shared_blocks;    /* blocks currently held by more than one request */
   double utilisation;       /* tokens / reserved_tokens: share of reserved cache
                                holding real tokens ([ROC] readouts, [PAS] Key points) */
+  int64_t swapped_seqs;     /* requests swapped out (pa_swap_out) */
+  int64_t swapped_tokens;   /* sum of their lengths */
 } pa_stats;
 
 typedef struct pa_pool pa_pool; /* opaque, host memory */
@@ -187,6 +189,50 @@ pa_status pa_get_block_tables(const pa_pool* pool, const int32_t* req_ids, int32
                               int32_t stride, int32_t* tables_out, int32_t* lens_out);
 
 pa_status pa_get_stats(const pa_pool* pool, pa_stats* out);
+
+/* ---- pre-emption by swapping ([ROC] "Fragmentation is lost users" and the
+ * Pre-emption term: when paging runs out, a request's cache is evicted and
+ * swapped back in later; [PAS] Summary: the scheduler pre-empts requests) ----
+ *
+ * A swapped-out request keeps its id and length but holds no blocks: it cannot
+ * grow (pa_reserve), fork, or have its table read (PA_ERR_INVALID_ARG) until
+ * it is swapped in; pa_seq_free drops it.  Its image, in memory the caller
+ * owns, holds every layer's copy of its blocks:
+ *     image[layer][j][0 = K, 1 = V][num_kv_heads][tile]
+ * for j < ceil(L / block_size) in logical order, each tile as the pool lays it
+ * out (K [head_dim/VE][block_size][VE], V [head_dim][block_size]), i.e.
+ * num_layers * ceil(L/BS) * 2 * num_kv_heads * head_dim * BS * elt bytes.
+ * Whole blocks are copied, rows past L included.  Sharing is not kept: blocks
+ * the request shared are copied out in full and come back as its own.
+ * Paged only. */
+
+/* Bytes of req_id's image (a resident or swapped-out request). */
+pa_status pa_swap_bytes(const pa_pool* pool, int32_t req_id, size_t* bytes_out);
+
+/* Copy resident request req_id's blocks into the image at d_image (capacity
+ * image_bytes; pinned host memory from hipHostMalloc, or device memory; 16-byte
+ * aligned), then give the blocks back as pa_seq_free does (table order, a
+ * block is free once no other request holds it).  Asynchronous on stream: the
+ * image is complete when the stream reaches this point, and the released
+ * blocks may be handed out again at once, so work that writes them must be
+ * ordered after this call (same stream, or an event).  d_image NULL with
+ * image_bytes 0: no copy, the contents are dropped (pre-emption by
+ * recomputation; no device work, no stream use).  PA_ERR_INVALID_ARG
+ * (contiguous pool, swapped-out request, image too small, unaligned, or memory
+ * the device cannot address) and PA_ERR_UNKNOWN_SEQ change nothing. */
+pa_status pa_swap_out(pa_pool* pool, int32_t req_id, void* d_image, size_t image_bytes,
+                      void* stream);
+
+/* Take ceil(L / block_size) fresh blocks for swapped-out request req_id (off
+ * the free list, all or nothing: PA_ERR_NO_BLOCKS changes nothing) and copy
+ * its image back into them.  Asynchronous on stream; the image must stay
+ * unchanged until the stream passes this point.  Afterwards the request is
+ * resident with a new block table and the same contents.  d_image NULL with
+ * image_bytes 0: no copy; the blocks' rows are undefined until the caller
+ * rewrites them (pa_append_kv into the slots of positions 0..L-1, which the
+ * new table gives), as after a recomputation. */
+pa_status pa_swap_in(pa_pool* pool, int32_t req_id, const void* d_image, size_t image_bytes,
+                     void* stream);
 
 /* ---- device calls: enqueue on stream, asynchronous ------------------------ */
 

@@ -16,6 +16,9 @@ What the pages fix:
   [ROC] "Fragmentation is lost users").
 * A finished or pre-empted request's cache is given back ([ROC]
   "Fragmentation is lost users" and the "Pre-emption" term).
+* A pre-empted request's cache can be evicted and swapped back in later
+  ([ROC] "Fragmentation is lost users"; [PAS] Summary: the scheduler
+  pre-empts requests).
 * Utilisation is the share of reserved cache that holds real tokens ([ROC]
   readouts; [PAS] Key points).
 * In the contiguous per-request layout the library hands out a reqId in
@@ -33,6 +36,12 @@ Readings where the pages are silent (the C library documents the same rules):
   (share count > 1) first copies that block to a fresh one and drops its share
   of the old one; the last remaining holder writes in place.  Full shared
   blocks are never written, hence never copied.
+* Swapping (paged only): ``swap_out`` gives a request's blocks back exactly as
+  ``free_seq`` does but keeps its id and length; its contents leave as whole
+  blocks.  ``swap_in`` takes ``ceil(L / BS)`` blocks off the free stack, all
+  or nothing, in the order they come off, and fills them with those contents,
+  so sharing is not restored.  A swapped-out request cannot grow, fork or be
+  read until it is swapped in; it can be freed.
 * Stats: ``tokens`` counts token rows physically held (a shared row once),
   ``reserved_tokens`` is ``used_blocks x BS`` (paged) or ``live requests x S``
   (contiguous), ``utilisation = tokens / reserved_tokens``.
@@ -62,6 +71,7 @@ class AllocError(Exception):
 class _Seq:
     table: list = field(default_factory=list)
     length: int = 0
+    swapped: bool = False
 
 
 def ceil_div(a: int, b: int) -> int:
@@ -115,10 +125,16 @@ class RefAllocator:
             raise AllocError(ERR_UNKNOWN_SEQ, f"request {rid} is not live")
         return self.seqs[rid]
 
+    def _resident(self, rid: int) -> _Seq:
+        s = self._get(rid)
+        if s.swapped:
+            raise AllocError(ERR_INVALID_ARG, f"request {rid} is swapped out")
+        return s
+
     def fork(self, parent: int) -> int:
         if self.layout != PAGED:
             raise AllocError(ERR_INVALID_ARG, "sharing needs the paged layout")
-        p = self._get(parent)
+        p = self._resident(parent)
         if not self.free_ids:
             raise AllocError(ERR_NO_REQ_ID, "all request ids are in use")
         rid = self.free_ids.pop()
@@ -127,15 +143,48 @@ class RefAllocator:
             self.refcount[b] += 1
         return rid
 
-    def free_seq(self, rid: int) -> None:
-        s = self._get(rid)
+    def _give_back(self, s: _Seq) -> None:
         for b in s.table:
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
                 self.fill[b] = 0
                 self.free.append(b)
+        s.table = []
+
+    def free_seq(self, rid: int) -> None:
+        s = self._get(rid)
+        self._give_back(s)
         del self.seqs[rid]
         self.free_ids.append(rid)
+
+    # -- pre-emption by swapping -----------------------------------------------
+    def swap_out(self, rid: int) -> list:
+        """Evict rid's cache; return the blocks whose contents leave, in order."""
+        if self.layout != PAGED:
+            raise AllocError(ERR_INVALID_ARG, "swapping needs the paged layout")
+        s = self._resident(rid)
+        blocks = list(s.table)
+        self._give_back(s)
+        s.swapped = True
+        return blocks
+
+    def swap_in(self, rid: int) -> list:
+        """Bring rid back into fresh blocks; return its new table."""
+        if self.layout != PAGED:
+            raise AllocError(ERR_INVALID_ARG, "swapping needs the paged layout")
+        s = self._get(rid)
+        if not s.swapped:
+            raise AllocError(ERR_INVALID_ARG, f"request {rid} is not swapped out")
+        n = ceil_div(s.length, self.block_size)
+        if n > len(self.free):
+            raise AllocError(ERR_NO_BLOCKS, f"need {n} blocks, {len(self.free)} free")
+        for j in range(n):
+            b = self.free.pop()
+            self.refcount[b] = 1
+            self.fill[b] = min(self.block_size, s.length - j * self.block_size)
+            s.table.append(b)
+        s.swapped = False
+        return list(s.table)
 
     # -- growth --------------------------------------------------------------
     def blocks_needed(self, req_ids, counts) -> tuple[int, int]:
@@ -170,7 +219,7 @@ class RefAllocator:
         if len(set(req_ids)) != len(req_ids):
             raise AllocError(ERR_INVALID_ARG, "a request may appear once per call")
         for rid, c in zip(req_ids, counts):
-            s = self._get(rid)
+            s = self._resident(rid)
             if c < 0:
                 raise AllocError(ERR_INVALID_ARG, "negative token count")
             if s.length + c > self.max_seq_len:
@@ -215,30 +264,34 @@ class RefAllocator:
 
     # -- readouts ------------------------------------------------------------
     def table(self, rid: int) -> list:
-        return list(self._get(rid).table)
+        return list(self._resident(rid).table)
 
     def length(self, rid: int) -> int:
         return self._get(rid).length
 
     def stats(self) -> dict:
+        resident = [s for s in self.seqs.values() if not s.swapped]
+        swapped = [s for s in self.seqs.values() if s.swapped]
         if self.layout == PAGED:
             used = self.num_blocks - len(self.free)
             tokens = sum(self.fill[b] for b in range(self.num_blocks) if self.refcount[b] > 0)
             reserved = used * self.block_size
         else:
             used = 0
-            tokens = sum(s.length for s in self.seqs.values())
-            reserved = len(self.seqs) * self.max_seq_len
+            tokens = sum(s.length for s in resident)
+            reserved = len(resident) * self.max_seq_len
         return {
             "free_blocks": len(self.free),
             "used_blocks": used,
             "tokens": tokens,
-            "logical_tokens": sum(s.length for s in self.seqs.values()),
+            "logical_tokens": sum(s.length for s in resident),
             "reserved_tokens": reserved,
-            "live_seqs": len(self.seqs),
+            "live_seqs": len(resident),
             "cow_copies": self.cow_copies,
             "shared_blocks": sum(1 for rc in self.refcount if rc > 1),
             "utilisation": (tokens / reserved) if reserved else 0.0,
+            "swapped_seqs": len(swapped),
+            "swapped_tokens": sum(s.length for s in swapped),
         }
 
 
@@ -261,6 +314,9 @@ def check_invariants(a: RefAllocator) -> None:
     bs = a.block_size
     held = [0] * a.num_blocks
     for s in a.seqs.values():
+        if s.swapped:
+            assert s.table == [], "a swapped-out request holds blocks"
+            continue
         assert len(s.table) == ceil_div(s.length, bs), "table length != ceil(L/BS)"
         waste = len(s.table) * bs - s.length
         assert 0 <= waste < bs, "waste must be under one block"
@@ -291,6 +347,7 @@ class ContentModel:
         self.a = alloc
         self.rows: dict[int, object] = {}
         self.history: dict[int, list] = {rid: [] for rid in alloc.seqs}
+        self.images: dict[int, list] = {}   # swapped-out request -> its rows, whole blocks
         self.serial = 0
 
     def add(self) -> int:
@@ -306,6 +363,25 @@ class ContentModel:
     def free_seq(self, rid: int) -> None:
         self.a.free_seq(rid)
         del self.history[rid]
+        self.images.pop(rid, None)
+
+    def swap_out(self, rid: int) -> None:
+        """Whole blocks leave, rows past the request's length included."""
+        blocks = self.a.swap_out(rid)
+        bs = self.a.block_size
+        self.images[rid] = [self.rows.get(b * bs + o) for b in blocks for o in range(bs)]
+
+    def swap_in(self, rid: int) -> None:
+        table = self.a.swap_in(rid)
+        bs = self.a.block_size
+        image = self.images.pop(rid)
+        for j, b in enumerate(table):
+            for o in range(bs):
+                label = image[j * bs + o]
+                if label is None:
+                    self.rows.pop(b * bs + o, None)
+                else:
+                    self.rows[b * bs + o] = label
 
     def reserve(self, req_ids, counts=None):
         slots, pairs = self.a.reserve(req_ids, counts)
@@ -330,6 +406,10 @@ class ContentModel:
     def check(self) -> None:
         bs = self.a.block_size
         for rid, hist in self.history.items():
+            if rid in self.images:
+                image = self.images[rid]
+                assert image[:len(hist)] == hist, f"request {rid}'s image holds other tokens"
+                continue
             table = self.a.table(rid)
             seen = [self.rows.get(table[t // bs] * bs + t % bs) for t in range(len(hist))]
             assert seen == hist, f"request {rid} sees other tokens than it wrote"

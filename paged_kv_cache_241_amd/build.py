@@ -55,6 +55,8 @@ def build(verbose: bool = False) -> str:
     jobs = [
         [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "kernels.hip"),
          "-o", os.path.join(BUILD, "kernels.o")],
+        [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "swap.hip"),
+         "-o", os.path.join(BUILD, "swap.o")],
         [hipcc, *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "pa_api.cpp"),
          "-o", os.path.join(BUILD, "pa_api.o")],
         [hipcc, *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "block_allocator.cpp"),
@@ -65,7 +67,7 @@ def build(verbose: bool = False) -> str:
             f.result()
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp,
-          os.path.join(BUILD, "kernels.o"), os.path.join(BUILD, "pa_api.o"),
+          os.path.join(BUILD, "kernels.o"), os.path.join(BUILD, "swap.o"), os.path.join(BUILD, "pa_api.o"),
           os.path.join(BUILD, "block_allocator.o")], verbose)
     os.replace(tmp, LIB)
     # the benchmark's achievable-bandwidth probe (not part of the library)

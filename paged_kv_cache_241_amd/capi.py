@@ -42,7 +42,7 @@ EXPORTS = (
     "pa_set_free_order", "pa_seq_add", "pa_seq_fork", "pa_seq_free", "pa_reserve",
     "pa_get_block_tables", "pa_get_stats", "pa_copy_blocks", "pa_append_kv",
     "pa_decode_partition_tokens", "pa_decode_workspace_bytes", "pa_decode", "pa_append_decode",
-    "pa_last_error",
+    "pa_swap_bytes", "pa_swap_out", "pa_swap_in", "pa_last_error",
 )
 
 
@@ -63,6 +63,7 @@ class pa_stats(ctypes.Structure):
         ("reserved_tokens", ctypes.c_int64), ("live_seqs", ctypes.c_int64),
         ("cow_copies", ctypes.c_int64), ("shared_blocks", ctypes.c_int64),
         ("utilisation", ctypes.c_double),
+        ("swapped_seqs", ctypes.c_int64), ("swapped_tokens", ctypes.c_int64),
     ]
 
 
@@ -102,6 +103,9 @@ def load() -> ctypes.CDLL:
         "pa_get_block_tables": (ctypes.c_int, [_vp, _p32, _i32, _i32, _p32, _p32]),
         "pa_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(pa_stats)]),
         "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _i32, _vp]),
+        "pa_swap_bytes": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(ctypes.c_size_t)]),
+        "pa_swap_out": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_size_t, _vp]),
+        "pa_swap_in": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_size_t, _vp]),
         "pa_append_kv": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i32, _vp]),
         "pa_decode_partition_tokens": (ctypes.c_int32, [_vp, _i32, _i32, _i32]),
         "pa_decode_workspace_bytes": (ctypes.c_size_t, [_vp, _i32, _i32, _i32, _i32]),

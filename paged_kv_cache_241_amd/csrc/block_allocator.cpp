@@ -59,6 +59,30 @@ Status BlockAllocator::check_live(int32_t rid, std::string* err) const {
   return kOk;
 }
 
+Status BlockAllocator::check_resident(int32_t rid, std::string* err) const {
+  Status st = check_live(rid, err);
+  if (st != kOk) return st;
+  if (seqs_[rid].swapped) {
+    *err = "request id " + std::to_string(rid) + " is swapped out";
+    return kInvalidArg;
+  }
+  return kOk;
+}
+
+// Gives a request's blocks back in table order (a block is free once no table
+// holds it) and empties its table.
+void BlockAllocator::release(Seq& s) {
+  for (int32_t b : s.table) {
+    const int32_t rc = --refcount_[b];
+    if (rc == 1) --shared_blocks_;
+    if (rc == 0) {
+      fill_[b] = 0;
+      free_.push_back(b);
+    }
+  }
+  s.table.clear();
+}
+
 Status BlockAllocator::add(int32_t* rid, std::string* err) {
   if (rid == nullptr) {
     *err = "seq_add: null output";
@@ -72,6 +96,7 @@ Status BlockAllocator::add(int32_t* rid, std::string* err) {
   free_ids_.pop_back();
   Seq& s = seqs_[r];
   s.live = true;
+  s.swapped = false;
   s.len = 0;
   s.table.clear();
   *rid = r;
@@ -87,7 +112,7 @@ Status BlockAllocator::fork(int32_t parent, int32_t* child, std::string* err) {
     *err = "seq_fork: null output";
     return kInvalidArg;
   }
-  Status st = check_live(parent, err);
+  Status st = check_resident(parent, err);
   if (st != kOk) return st;
   if (free_ids_.empty()) {
     *err = "seq_fork: all request ids are live";
@@ -98,6 +123,7 @@ Status BlockAllocator::fork(int32_t parent, int32_t* child, std::string* err) {
   Seq& c = seqs_[r];
   const Seq& p = seqs_[parent];
   c.live = true;
+  c.swapped = false;
   c.len = p.len;
   c.table = p.table;
   for (int32_t b : c.table)
@@ -110,17 +136,10 @@ Status BlockAllocator::free_seq(int32_t rid, std::string* err) {
   Status st = check_live(rid, err);
   if (st != kOk) return st;
   Seq& s = seqs_[rid];
-  for (int32_t b : s.table) {
-    const int32_t rc = --refcount_[b];
-    if (rc == 1) --shared_blocks_;
-    if (rc == 0) {
-      fill_[b] = 0;
-      free_.push_back(b);
-    }
-  }
+  release(s);
   s.live = false;
+  s.swapped = false;
   s.len = 0;
-  s.table.clear();
   free_ids_.push_back(rid);
   return kOk;
 }
@@ -146,7 +165,7 @@ Status BlockAllocator::reserve(const int32_t* rids, int32_t n, const int32_t* co
   }
   int64_t total = 0;
   for (int32_t i = 0; i < n; ++i) {
-    Status st = check_live(rids[i], err);
+    Status st = check_resident(rids[i], err);
     if (st != kOk) return st;
     if (mark_[rids[i]] == epoch_) {
       *err = "reserve: request " + std::to_string(rids[i]) + " listed twice";
@@ -261,7 +280,7 @@ Status BlockAllocator::tables(const int32_t* rids, int32_t n, int32_t stride, in
     return kInvalidArg;
   }
   for (int32_t i = 0; i < n; ++i) {
-    Status st = check_live(rids[i], err);
+    Status st = check_resident(rids[i], err);
     if (st != kOk) return st;
     if (out && static_cast<int64_t>(seqs_[rids[i]].table.size()) > stride) {
       *err = "get_block_tables: request " + std::to_string(rids[i]) + " has " +
@@ -287,6 +306,11 @@ AllocStats BlockAllocator::stats() const {
   AllocStats st;
   for (const Seq& s : seqs_) {
     if (!s.live) continue;
+    if (s.swapped) {
+      ++st.swapped_seqs;
+      st.swapped_tokens += s.len;
+      continue;
+    }
     ++st.live_seqs;
     st.logical_tokens += s.len;
   }
@@ -306,6 +330,71 @@ AllocStats BlockAllocator::stats() const {
                        ? static_cast<double>(st.tokens) / static_cast<double>(st.reserved_tokens)
                        : 0.0;
   return st;
+}
+
+Status BlockAllocator::swap_out_blocks(int32_t rid, std::vector<int32_t>* blocks, int32_t* len,
+                                       std::string* err) const {
+  if (!paged_) {
+    *err = "swap_out: swapping needs the paged layout";
+    return kInvalidArg;
+  }
+  Status st = check_resident(rid, err);
+  if (st != kOk) return st;
+  *blocks = seqs_[rid].table;
+  *len = seqs_[rid].len;
+  return kOk;
+}
+
+Status BlockAllocator::swap_out(int32_t rid, std::string* err) {
+  std::vector<int32_t> blocks;
+  int32_t len = 0;
+  Status st = swap_out_blocks(rid, &blocks, &len, err);
+  if (st != kOk) return st;
+  Seq& s = seqs_[rid];
+  release(s);
+  s.swapped = true;
+  return kOk;
+}
+
+Status BlockAllocator::swap_in(int32_t rid, std::vector<int32_t>* blocks, std::string* err) {
+  if (!paged_) {
+    *err = "swap_in: swapping needs the paged layout";
+    return kInvalidArg;
+  }
+  Status st = check_live(rid, err);
+  if (st != kOk) return st;
+  Seq& s = seqs_[rid];
+  if (!s.swapped) {
+    *err = "swap_in: request " + std::to_string(rid) + " is not swapped out";
+    return kInvalidArg;
+  }
+  const int64_t n = ceil_div(s.len, block_size_);
+  if (n > static_cast<int64_t>(free_.size())) {
+    *err = "swap_in: need " + std::to_string(n) + " blocks, " + std::to_string(free_.size()) +
+           " free";
+    return kNoBlocks;
+  }
+  s.table.clear();
+  for (int64_t j = 0; j < n; ++j) {
+    const int32_t b = pop_block();
+    refcount_[b] = 1;
+    fill_[b] = static_cast<int32_t>(std::min<int64_t>(block_size_, s.len - j * block_size_));
+    s.table.push_back(b);
+  }
+  s.swapped = false;
+  *blocks = s.table;
+  return kOk;
+}
+
+void BlockAllocator::swap_in_undo(int32_t rid) {
+  Seq& s = seqs_[rid];
+  for (auto it = s.table.rbegin(); it != s.table.rend(); ++it) {
+    refcount_[*it] = 0;
+    fill_[*it] = 0;
+    free_.push_back(*it);
+  }
+  s.table.clear();
+  s.swapped = true;
 }
 
 }  // namespace pa

@@ -12,10 +12,16 @@
 //     copied when a sharer first writes into it, the last holder writes in
 //     place;
 //   * finishing or pre-empting a request returns its unshared blocks;
+//   * a pre-empted request can instead be swapped out: its blocks are given
+//     back but it keeps its reqId and length, and swapping it in later takes
+//     fresh blocks for its whole context;
 //   * reqIds in [0, max_seqs) are handed out by the allocator.
 // Choices where the pages are silent: the free list and the reqId list are
 // stacks (last returned, first reused); reserve is all-or-nothing and handles
-// requests in the order given.
+// requests in the order given.  Swap-out gives blocks back in table order, as
+// freeing does; swap-in takes ceil(L / block_size) blocks off the free stack,
+// all or nothing.  A swapped-out request cannot grow, fork or be read until it
+// is swapped in; it can be freed.
 #pragma once
 
 #include <cstdint>
@@ -36,6 +42,7 @@ struct AllocStats {
   int64_t free_blocks = 0, used_blocks = 0, tokens = 0, logical_tokens = 0;
   int64_t reserved_tokens = 0, live_seqs = 0, cow_copies = 0, shared_blocks = 0;
   double utilisation = 0.0;
+  int64_t swapped_seqs = 0, swapped_tokens = 0;
 };
 
 class BlockAllocator {
@@ -55,6 +62,27 @@ class BlockAllocator {
                 std::string* err) const;
   AllocStats stats() const;
 
+  // Swap-out, in two steps so that the caller can copy the blocks out first:
+  // swap_out_blocks reads the resident request's table (its blocks in logical
+  // order) and changes nothing; swap_out releases the blocks.
+  Status swap_out_blocks(int32_t rid, std::vector<int32_t>* blocks, int32_t* len,
+                         std::string* err) const;
+  Status swap_out(int32_t rid, std::string* err);
+  // Swap-in: fresh blocks for the swapped-out request's whole context, in
+  // logical order.  swap_in_undo gives them back, restoring the free stack.
+  Status swap_in(int32_t rid, std::vector<int32_t>* blocks, std::string* err);
+  void swap_in_undo(int32_t rid);
+
+  // Length of a live request (resident or swapped out); false if not live.
+  bool length(int32_t rid, int32_t* len) const {
+    if (rid < 0 || rid >= max_seqs_ || !seqs_[rid].live) return false;
+    *len = seqs_[rid].len;
+    return true;
+  }
+  bool swapped(int32_t rid) const {
+    return rid >= 0 && rid < max_seqs_ && seqs_[rid].live && seqs_[rid].swapped;
+  }
+
   // Blocks currently held by more than one request.
   int64_t shared_blocks() const { return shared_blocks_; }
   bool paged() const { return paged_; }
@@ -66,11 +94,14 @@ class BlockAllocator {
  private:
   struct Seq {
     bool live = false;
+    bool swapped = false;  // live but holding no blocks
     int32_t len = 0;
     std::vector<int32_t> table;
   };
 
   Status check_live(int32_t rid, std::string* err) const;
+  Status check_resident(int32_t rid, std::string* err) const;
+  void release(Seq& s);
   int32_t pop_block();
 
   bool paged_;

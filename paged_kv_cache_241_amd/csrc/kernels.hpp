@@ -37,6 +37,11 @@ hipError_t launch_append(const CacheGeom& g, int32_t layer, const void* k, const
 hipError_t launch_copy_blocks(const CacheGeom& g, const int32_t* pairs, int32_t n,
                               hipStream_t stream);
 
+// Swap image <-> blocks: blocks[j] (host array, n ids) in every layer, K and V,
+// to or from image[layer][j][K|V][num_kv_heads][tile] (device-addressable).
+hipError_t launch_swap(const CacheGeom& g, const int32_t* blocks, int32_t n, char* image,
+                       bool to_image, hipStream_t stream);
+
 struct DecodeArgs {
   const void* q = nullptr;           // [B][Hq][D]
   const int32_t* tables = nullptr;   // paged: [B][stride]

@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "../../include/pa.h"
 #include "block_allocator.hpp"
@@ -108,6 +109,56 @@ int32_t num_partitions(int32_t max_context, int32_t ptokens) {
 
 bool bad_partition(const pa_pool* p, int32_t partition_tokens) {
   return partition_tokens < 0 || partition_tokens % partition_unit(p) != 0;
+}
+
+
+// Length of a live request of a paged pool (resident or swapped out).
+pa_status swap_length(const pa_pool* pool, int32_t req_id, const char* who, int32_t* len) {
+  if (!pool->geom.paged)
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": swapping needs the paged layout");
+  if (!pool->alloc.length(req_id, len))
+    return fail(PA_ERR_UNKNOWN_SEQ, std::string(who) + ": request id " + std::to_string(req_id) +
+                                        " is not live");
+  return PA_OK;
+}
+
+size_t image_bytes(const pa_pool* pool, int32_t len) {
+  const pa_pool_desc& d = pool->desc;
+  const int64_t blocks = (static_cast<int64_t>(len) + d.block_size - 1) / d.block_size;
+  return static_cast<size_t>(static_cast<int64_t>(d.num_layers) * blocks * 2 * d.num_kv_heads *
+                             d.head_dim * d.block_size * elt_bytes(d.kv_dtype));
+}
+
+// The image must hold the request's blocks and be reachable by the kernels:
+// device memory as it is, pinned host memory through its device mapping.
+// Anything else (pageable host memory) is refused here rather than faulted on.
+// No image at all (NULL with capacity 0) means no copy: *dev stays NULL.
+pa_status check_image(const pa_pool* pool, const void* image, size_t cap, int32_t len,
+                      const char* who, char** dev) {
+  const std::string w(who);
+  const size_t need = image_bytes(pool, len);
+  *dev = nullptr;
+  if (image == nullptr && cap == 0) return PA_OK;
+  if (need == 0) return PA_OK;
+  if (image == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null image with a nonzero capacity");
+  if (cap < need)
+    return fail(PA_ERR_INVALID_ARG, w + ": image holds " + std::to_string(cap) + " bytes, " +
+                                        std::to_string(need) + " needed");
+  if (reinterpret_cast<uintptr_t>(image) & 15) return fail(PA_ERR_INVALID_ARG, w + ": image must be 16-byte aligned");
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, image) != hipSuccess) {
+    (void)hipGetLastError();  // leave no error behind for the next launch
+    return fail(PA_ERR_INVALID_ARG, w + ": image is neither device nor pinned host memory");
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+    *dev = static_cast<char*>(const_cast<void*>(image));
+  } else if (attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr) {
+    const char* hp = static_cast<const char*>(attr.hostPointer ? attr.hostPointer : image);
+    *dev = static_cast<char*>(attr.devicePointer) + (static_cast<const char*>(image) - hp);
+  } else {
+    return fail(PA_ERR_INVALID_ARG, w + ": image is neither device nor pinned host memory");
+  }
+  return PA_OK;
 }
 
 }  // namespace
@@ -216,6 +267,64 @@ pa_status pa_get_stats(const pa_pool* pool, pa_stats* out) {
   out->cow_copies = s.cow_copies;
   out->shared_blocks = s.shared_blocks;
   out->utilisation = s.utilisation;
+  out->swapped_seqs = s.swapped_seqs;
+  out->swapped_tokens = s.swapped_tokens;
+  return PA_OK;
+}
+
+pa_status pa_swap_bytes(const pa_pool* pool, int32_t req_id, size_t* bytes_out) {
+  if (pool == nullptr || bytes_out == nullptr) return fail(PA_ERR_INVALID_ARG, "swap_bytes: null argument");
+  int32_t len = 0;
+  pa_status st = swap_length(pool, req_id, "swap_bytes", &len);
+  if (st != PA_OK) return st;
+  *bytes_out = image_bytes(pool, len);
+  return PA_OK;
+}
+
+pa_status pa_swap_out(pa_pool* pool, int32_t req_id, void* d_image, size_t image_bytes_cap,
+                      void* stream) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "swap_out: null pool");
+  std::vector<int32_t> blocks;
+  int32_t len = 0;
+  std::string err;
+  pa::Status s = pool->alloc.swap_out_blocks(req_id, &blocks, &len, &err);
+  if (s != pa::kOk) return fail(static_cast<pa_status>(s), "swap_out: " + err);
+  char* dev = nullptr;
+  pa_status st = check_image(pool, d_image, image_bytes_cap, len, "swap_out", &dev);
+  if (st != PA_OK) return st;
+  if (dev != nullptr) {
+    hipError_t e = pa::launch_swap(pool->geom, blocks.data(), static_cast<int32_t>(blocks.size()),
+                                   dev, true, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("swap_out: ") + hipGetErrorString(e));
+  }
+  s = pool->alloc.swap_out(req_id, &err);
+  if (s != pa::kOk) return fail(static_cast<pa_status>(s), "swap_out: " + err);
+  return PA_OK;
+}
+
+pa_status pa_swap_in(pa_pool* pool, int32_t req_id, const void* d_image, size_t image_bytes_cap,
+                     void* stream) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "swap_in: null pool");
+  int32_t len = 0;
+  pa_status st = swap_length(pool, req_id, "swap_in", &len);
+  if (st != PA_OK) return st;
+  if (!pool->alloc.swapped(req_id))
+    return fail(PA_ERR_INVALID_ARG, "swap_in: request " + std::to_string(req_id) + " is not swapped out");
+  char* dev = nullptr;
+  st = check_image(pool, d_image, image_bytes_cap, len, "swap_in", &dev);
+  if (st != PA_OK) return st;
+  std::vector<int32_t> blocks;
+  std::string err;
+  pa::Status s = pool->alloc.swap_in(req_id, &blocks, &err);
+  if (s != pa::kOk) return fail(static_cast<pa_status>(s), "swap_in: " + err);
+  if (dev != nullptr) {
+    hipError_t e = pa::launch_swap(pool->geom, blocks.data(), static_cast<int32_t>(blocks.size()),
+                                   dev, false, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+      pool->alloc.swap_in_undo(req_id);
+      return fail(PA_ERR_HIP, std::string("swap_in: ") + hipGetErrorString(e));
+    }
+  }
   return PA_OK;
 }
 

@@ -155,6 +155,32 @@ class Pool:
                                                 _ptr32(tables), _ptr32(lens)), "pa_get_block_tables")
         return tables[:n], lens[:n]
 
+    # -- pre-emption by swapping ---------------------------------------------
+    def swap_bytes(self, rid: int) -> int:
+        """Bytes of request rid's swap image (include/pa.h lays it out)."""
+        n = ctypes.c_size_t()
+        capi.check(self.lib.pa_swap_bytes(self.handle, rid, ctypes.byref(n)), "pa_swap_bytes")
+        return n.value
+
+    def _image(self, image, stream):
+        if image is None:  # no copy: nothing touches the device
+            return ctypes.c_void_p(None), 0, ctypes.c_void_p(None)
+        return (ctypes.c_void_p(image.data_ptr()), image.numel() * image.element_size(),
+                _stream_handle(stream))
+
+    def swap_out(self, rid: int, image=None, stream=None) -> None:
+        """Copy rid's blocks into ``image`` (a pinned host or device uint8
+        tensor of at least swap_bytes(rid) bytes) and give the blocks back;
+        ``image=None`` drops the contents (pre-emption by recomputation)."""
+        ptr, cap, st = self._image(image, stream)
+        capi.check(self.lib.pa_swap_out(self.handle, rid, ptr, cap, st), "pa_swap_out")
+
+    def swap_in(self, rid: int, image=None, stream=None) -> None:
+        """Give swapped-out rid fresh blocks and copy ``image`` back into them
+        (``image=None``: no copy, the caller rewrites the rows)."""
+        ptr, cap, st = self._image(image, stream)
+        capi.check(self.lib.pa_swap_in(self.handle, rid, ptr, cap, st), "pa_swap_in")
+
     def stats(self) -> dict:
         st = capi.pa_stats()
         capi.check(self.lib.pa_get_stats(self.handle, ctypes.byref(st)), "pa_get_stats")

@@ -64,6 +64,22 @@ class _Lib:
     def table_len(self, rids, stride):
         return self._wrap(self.p.block_tables, rids, stride)
 
+    # no image: the allocator side of a swap (no device work on a host-only pool);
+    # like the oracle, return the blocks that leave / the new table
+    def swap_out(self, rid):
+        try:
+            tables, lens = self.p.block_tables([rid])
+            blocks = [int(b) for b in tables[0] if b >= 0]
+        except capi.PaError:
+            blocks = None
+        self._wrap(self.p.swap_out, rid, None)
+        return blocks
+
+    def swap_in(self, rid):
+        self._wrap(self.p.swap_in, rid, None)
+        tables, _ = self.p.block_tables([rid])
+        return [int(b) for b in tables[0] if b >= 0]
+
 
 def _make(nb, bs, max_seqs, max_len, layout=AL.PAGED):
     lay = "paged" if layout == AL.PAGED else "contiguous"
@@ -74,7 +90,7 @@ def _make(nb, bs, max_seqs, max_len, layout=AL.PAGED):
 
 
 def _same_state(ref, lib):
-    live = sorted(ref.seqs)
+    live = sorted(r for r, s in ref.seqs.items() if not s.swapped)
     stride = max([len(ref.seqs[r].table) for r in live] + [1])
     tables, lens = lib.table_len(live, stride)
     for i, r in enumerate(live):
@@ -86,7 +102,7 @@ def _same_state(ref, lib):
     got = lib.p.stats()
     want = ref.stats()
     for key in ("free_blocks", "used_blocks", "tokens", "logical_tokens", "reserved_tokens",
-                "live_seqs", "cow_copies", "shared_blocks"):
+                "live_seqs", "cow_copies", "shared_blocks", "swapped_seqs", "swapped_tokens"):
         assert got[key] == want[key], key
     assert got["utilisation"] == pytest.approx(want["utilisation"], rel=0, abs=1e-15)
 
@@ -103,7 +119,8 @@ def _both(ref, lib, fn):
     return out[0]
 
 
-_ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "grow", "free", "grow1"]),
+_ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "grow", "free", "grow1", "swapout",
+                                           "swapin"]),
                           st.integers(0, 1 << 30), st.integers(0, 40)), max_size=60)
 
 
@@ -118,10 +135,14 @@ def test_random_operations_bit_exact(ops, bs, nb, seed):
         if kind == "add":
             _both(ref, lib, lambda a: a.add())
         elif kind == "fork" and live:
+            # a swapped-out parent is an error on both sides
             _both(ref, lib, lambda a: a.fork(live[pick % len(live)]))
         elif kind == "free":
             rid = live[pick % len(live)] if live and pick % 5 else pick % 9 - 1
             _both(ref, lib, lambda a: a.free_seq(rid))
+        elif kind in ("swapout", "swapin"):
+            rid = live[pick % len(live)] if live and pick % 7 else pick % 9 - 1
+            _both(ref, lib, lambda a: getattr(a, "swap_out" if kind == "swapout" else "swap_in")(rid))
         elif kind in ("grow", "grow1") and live:
             chosen = [r for i, r in enumerate(live) if (pick >> i) & 1] or live[:1]
             chosen = chosen[::-1] if pick & 64 else chosen
@@ -148,6 +169,36 @@ def test_error_codes_and_argument_checks():
         Pool(host_only=True, num_layers=1, num_blocks=4, block_size=12, num_kv_heads=1,
              head_dim=64, kv_dtype="f32")
     assert ei.value.status == capi.PA_ERR_INVALID_ARG
+
+
+def test_swap_refuses_bad_images_and_changes_nothing():
+    """Checked before any device work: a short, unaligned or pageable image,
+    a contiguous pool, a swapped-out or unknown request."""
+    import ctypes
+
+    import torch
+
+    p = Pool(num_layers=2, num_blocks=16, block_size=8, num_kv_heads=2, head_dim=64,
+             kv_dtype="bf16", max_seqs=4, max_seq_len=64, host_only=True)
+    r = p.add()
+    p.reserve([r], [10])
+    n = p.swap_bytes(r)
+    assert n == 2 * 2 * 2 * (2 * 64 * 8 * 2)            # layers x blocks x K,V x block bytes
+    buf = torch.empty(n + 16, dtype=torch.uint8)         # pageable host memory
+    ptr = (buf.data_ptr() + 15) // 16 * 16
+    lib = p.lib
+    for args in ((ptr, n), (ptr, n - 16), (ptr + 8, n), (None, 16)):
+        st = lib.pa_swap_out(p.handle, r, ctypes.c_void_p(args[0]), args[1], None)
+        assert st == capi.PA_ERR_INVALID_ARG, lib.pa_last_error()
+        tables, lens = p.block_tables([r])
+        assert tables.tolist() == [[0, 1]] and lens.tolist() == [10]
+    assert lib.pa_swap_in(p.handle, r, None, 0, None) == capi.PA_ERR_INVALID_ARG   # resident
+    assert lib.pa_swap_out(p.handle, 3, None, 0, None) == capi.PA_ERR_UNKNOWN_SEQ
+    assert p.stats()["swapped_seqs"] == 0
+    c = Pool(num_layers=1, num_blocks=0, block_size=16, num_kv_heads=1, head_dim=64,
+             kv_dtype="f32", layout="contiguous", max_seqs=2, max_seq_len=64, host_only=True)
+    q = c.add()
+    assert lib.pa_swap_out(c.handle, q, None, 0, None) == capi.PA_ERR_INVALID_ARG
 
 
 def test_contiguous_mode_bit_exact():

@@ -201,7 +201,96 @@ def test_contiguous_slots_follow_reqid_times_s():
         a.fork(r0)
 
 
-_ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "grow", "free"]),
+def test_swap_round_trip_restores_contents_and_takes_blocks_off_the_stack():
+    m = AL.ContentModel(AL.RefAllocator(10, 4, 4, 64))
+    r = m.add()
+    m.reserve([r], [10])                 # blocks 0, 1, 2 (ascending free order)
+    assert m.a.table(r) == [0, 1, 2]
+    m.swap_out(r)
+    # given back in table order onto the free stack, block 2 on top
+    assert m.a.free[-3:] == [0, 1, 2]
+    st_out = m.a.stats()
+    assert st_out["used_blocks"] == 0 and st_out["live_seqs"] == 0
+    assert st_out["swapped_seqs"] == 1 and st_out["swapped_tokens"] == 10
+    m.check()
+    m.swap_in(r)
+    # ceil(10 / 4) = 3 blocks off the top of the stack: the table comes back reversed
+    assert m.a.table(r) == [2, 1, 0]
+    assert m.a.length(r) == 10 and m.a.stats()["swapped_seqs"] == 0
+    m.check()
+    AL.check_invariants(m.a)
+    m.reserve([r], [3])                  # 2 rows fill block 0, then a new block
+    m.check()
+    assert m.a.table(r) == [2, 1, 0, 3]
+
+
+def test_swapping_out_one_sharer_leaves_the_others_their_blocks():
+    m = AL.ContentModel(AL.RefAllocator(12, 4, 4, 64))
+    p = m.add()
+    m.reserve([p], [6])
+    c = m.fork(p)
+    shared = m.a.table(p)
+    m.swap_out(p)
+    assert m.a.table(c) == shared and all(m.a.refcount[b] == 1 for b in shared)
+    assert m.a.stats()["shared_blocks"] == 0
+    m.reserve([c], [3])                  # c is now the only holder: writes in place
+    m.check()
+    m.swap_in(p)                         # p comes back into private blocks
+    assert set(m.a.table(p)).isdisjoint(m.a.table(c))
+    m.reserve([p], [2])
+    m.check()
+    AL.check_invariants(m.a)
+
+
+def test_preemption_by_swapping_frees_room_and_the_request_resumes():
+    # 6 blocks of 4: two requests of 11 tokens fill the pool (one row left in
+    # each last block)
+    m = AL.ContentModel(AL.RefAllocator(6, 4, 4, 64))
+    a, b = m.add(), m.add()
+    m.reserve([a, b], [11, 11])
+    c = m.add()
+    with pytest.raises(AL.AllocError) as e:
+        m.reserve([c], [5])
+    assert e.value.status == AL.ERR_NO_BLOCKS
+    m.swap_out(b)                        # the pre-empted request
+    m.reserve([c], [5])
+    with pytest.raises(AL.AllocError) as e:
+        m.swap_in(b)                     # needs 3 blocks, 1 free: nothing changes
+    assert e.value.status == AL.ERR_NO_BLOCKS and m.a.seqs[b].swapped
+    m.free_seq(c)
+    m.swap_in(b)
+    m.reserve([a, b])                    # both write their last free row in place
+    assert m.a.stats()["free_blocks"] == 0
+    m.check()
+    AL.check_invariants(m.a)
+
+
+def test_swap_errors():
+    a = AL.RefAllocator(8, 4, 4, 64)
+    r = a.add()
+    a.reserve([r], [5])
+    with pytest.raises(AL.AllocError) as e:
+        a.swap_in(r)                     # resident
+    assert e.value.status == AL.ERR_INVALID_ARG
+    a.swap_out(r)
+    for call in (lambda: a.reserve([r]), lambda: a.fork(r), lambda: a.table(r),
+                 lambda: a.swap_out(r)):
+        with pytest.raises(AL.AllocError) as e:
+            call()
+        assert e.value.status == AL.ERR_INVALID_ARG
+    with pytest.raises(AL.AllocError) as e:
+        a.swap_out(7)
+    assert e.value.status == AL.ERR_UNKNOWN_SEQ
+    a.free_seq(r)                        # a swapped-out request can be dropped
+    assert a.stats()["swapped_seqs"] == 0 and a.stats()["free_blocks"] == 8
+    c = AL.RefAllocator(0, 16, 4, 64, layout=AL.CONTIGUOUS)
+    q = c.add()
+    with pytest.raises(AL.AllocError) as e:
+        c.swap_out(q)
+    assert e.value.status == AL.ERR_INVALID_ARG
+
+
+_ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "grow", "free", "swapout", "swapin"]),
                           st.integers(0, 1 << 30), st.integers(0, 40)), max_size=60)
 
 
@@ -211,15 +300,25 @@ def test_random_operation_sequences_keep_every_invariant(ops, bs, nb):
     m = AL.ContentModel(AL.RefAllocator(nb, bs, 6, 120))
     for kind, pick, count in ops:
         live = sorted(m.history)
+        resident = [r for r in live if r not in m.images]
         try:
             if kind == "add":
                 m.add()
-            elif kind == "fork" and live:
-                m.fork(live[pick % len(live)])
+            elif kind == "fork" and resident:
+                m.fork(resident[pick % len(resident)])
             elif kind == "free" and live:
                 m.free_seq(live[pick % len(live)])
-            elif kind == "grow" and live:
-                chosen = [r for i, r in enumerate(live) if (pick >> i) & 1] or live[:1]
+            elif kind == "swapout" and resident:
+                m.swap_out(resident[pick % len(resident)])
+            elif kind == "swapin" and m.images:
+                out = sorted(m.images)
+                before = copy.deepcopy(m.a.__dict__)
+                try:
+                    m.swap_in(out[pick % len(out)])
+                except AL.AllocError as e:
+                    assert e.status == AL.ERR_NO_BLOCKS and m.a.__dict__ == before
+            elif kind == "grow" and resident:
+                chosen = [r for i, r in enumerate(resident) if (pick >> i) & 1] or resident[:1]
                 before = copy.deepcopy(m.a.__dict__)
                 try:
                     m.reserve(chosen, [count % 7] * len(chosen))
@@ -257,5 +356,13 @@ def test_invariant_checker_catches_planted_mistakes():
     m.a.refcount[m.a.table(p)[0]] = 1   # plant: forget the share
     m.reserve([p])
     m.reserve([c])                        # overwrites p's third token in place
+    with pytest.raises(AssertionError):
+        m.check()
+    # a swap-in that brings back the wrong rows is caught too
+    m = AL.ContentModel(AL.RefAllocator(8, 4, 4, 64))
+    r = m.add()
+    m.reserve([r], [6])
+    m.swap_out(r)
+    m.images[r][1], m.images[r][4] = m.images[r][4], m.images[r][1]   # plant: two rows swapped
     with pytest.raises(AssertionError):
         m.check()
