@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (2 = the metric's)")
-    ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"])
+    ap.add_argument("--layout", default="paged", choices=["paged", "contiguous", "vmm"],
+                    help="vmm: the contiguous layout with caches mapped on demand (ROCm VMM)")
     ap.add_argument("--prompt-len", type=int, default=0, help="workload 5: prompt length")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--block-size", type=int, default=0, help="tokens per block (0: workload's, 16)")
@@ -125,6 +126,9 @@ class Bench:
 
         self.torch = torch
         self.cfg = cfg
+        # "vmm": the contiguous layout with its caches mapped on demand
+        self.vmm = layout == "vmm"
+        layout = "contiguous" if self.vmm else layout
         self.layout = layout
         self.nl = num_layers
         self.pt = partition_tokens
@@ -136,8 +140,14 @@ class Bench:
         headroom = len(pl.batch_handles) * (-(-extra_steps // bs) + 1)
         nb = pl.num_blocks + headroom
         self.max_seqs = 4096 if layout == "paged" else cfg.batch
+        elt = 2 if cfg.kv_dtype == "bf16" else 4
+        # demand paging may map at most what the plain contiguous pool reserves
+        full = 2 * num_layers * self.max_seqs * cfg.max_seq_len * cfg.num_kv_heads * cfg.head_dim * elt
         self.pool = Pool(num_layers, nb, bs, cfg.num_kv_heads, cfg.head_dim, cfg.kv_dtype, layout,
-                         max_seqs=self.max_seqs, max_seq_len=cfg.max_seq_len, device=dev)
+                         max_seqs=self.max_seqs, max_seq_len=cfg.max_seq_len, device=dev,
+                         vmm_bytes=full if self.vmm else None)
+        self.full_bytes = full
+        self.reserve_s = 0.0   # host time inside pa_reserve during the prefill
         if layout == "paged":
             order = np.concatenate([W.free_order(pl.num_blocks, cfg.seed),
                                     np.arange(pl.num_blocks, nb, dtype=np.int32)])
@@ -169,7 +179,9 @@ class Bench:
                 del self.length[rid]
 
             def reserve(_, rids, counts):
+                t0 = time.perf_counter()
                 out = pool.reserve(rids, counts)
+                self.reserve_s += time.perf_counter() - t0
                 for r, c in zip(rids, counts):
                     self.length[r] += c
                 return out
@@ -576,6 +588,15 @@ def main():
         res["cpu_baseline"] = cpu_baseline(bench, args.cpu_seconds)
     if args.swap_seqs:
         res["swap"] = swap_probe(bench, args.swap_seqs)
+    if bench.vmm:
+        v = bench.pool.vmm_stats()
+        res["vmm"] = {
+            "page_bytes": v["page_bytes"], "mapped_bytes": v["mapped_bytes"],
+            "contiguous_reservation_bytes": bench.full_bytes,
+            "mapped_share": round(v["mapped_bytes"] / bench.full_bytes, 4),
+            "prefill_reserve_s": round(bench.reserve_s, 4),
+            "map_rate_gbs": round(v["mapped_bytes"] / bench.reserve_s / 1e9, 2) if bench.reserve_s else None,
+        }
     if not args.no_hbm_probe:
         probe = hbm_probe()
         if probe:

@@ -51,7 +51,8 @@
  * Ownership: the caller owns all device memory (caches, q, out, tables, slots,
  *   workspace) and keeps it alive while the pool uses it.  The library owns
  *   only the opaque host-side pa_pool and frees it in pa_destroy_pool.  No
- *   function allocates device memory.
+ *   function allocates device memory, except that a demand-paged pool
+ *   (pa_create_pool_vmm) maps its own cache pages in pa_reserve.
  * Errors: every call returns a pa_status; PA_OK is 0, errors are negative.
  *   Nothing throws across the ABI.  On error no state changes (pa_reserve is
  *   all-or-nothing) and pa_last_error() gives a message for the calling thread.
@@ -133,8 +134,43 @@ size_t pa_bytes_per_token(const pa_pool_desc* desc);
 pa_status pa_create_pool(const pa_pool_desc* desc, void* d_k_cache, void* d_v_cache,
                          pa_pool** out);
 
-/* Free the host handle.  The caches are the caller's. */
+/* Free the host handle.  The caches are the caller's (a demand-paged pool's
+ * are the library's: they are unmapped and freed here, so no queued or
+ * running work may still use them). */
 pa_status pa_destroy_pool(pa_pool* pool);
+
+/* ---- demand-paged contiguous caches ([VAC] 5.2.1-5.2.3) -------------------
+ * The contiguous layout with its K and V caches backed on demand: the library
+ * reserves the virtual range of both caches (num_layers x max_seqs x S each,
+ * request reqId's sub-range at reqId x S, as pa_create_pool lays them out)
+ * without physical memory, and pa_reserve maps physical pages into a
+ * request's sub-range of every layer, K and V, before it hands out slots
+ * past the pages already there.  Pages are 2 MiB where one request's
+ * sub-range, S x num_kv_heads x head_dim x elt bytes, is a multiple of that,
+ * else the device's allocation granularity (which it must then be a multiple
+ * of); each page is its own physical allocation.  physical_bytes caps the memory mapped: a pa_reserve that would pass
+ * it fails with PA_ERR_NO_BLOCKS and changes nothing (PA_ERR_HIP from the
+ * mapping calls may leave pages mapped but changes no length).  A freed
+ * request's pages stay mapped for the next request given its id (ids are
+ * reused last-freed first) until pa_vmm_trim.  Everything else is the
+ * contiguous pool's.  PA_ERR_UNSUPPORTED: the device or the sizes do not
+ * allow it. */
+typedef struct pa_vmm_stats {
+  int64_t page_bytes;    /* physical page (allocation granularity) */
+  int64_t mapped_bytes;  /* physical memory mapped, all layers, K and V */
+  int64_t budget_bytes;  /* physical_bytes rounded down to whole pages */
+  int64_t region_bytes;  /* one request's sub-range of one layer's K (or V) */
+} pa_vmm_stats;
+
+pa_status pa_create_pool_vmm(const pa_pool_desc* desc, size_t physical_bytes, pa_pool** out);
+
+pa_status pa_vmm_info(const pa_pool* pool, pa_vmm_stats* out);
+
+/* Unmap the pages of every request id that is not live; *freed_bytes_out (may
+ * be NULL) gets the bytes given back.  No queued or running work may still
+ * touch those requests' caches: synchronise the streams that used them
+ * first. */
+pa_status pa_vmm_trim(pa_pool* pool, int64_t* freed_bytes_out);
 
 /* Replace the order in which free blocks are handed out: block_ids[0] first.
  * block_ids must be a permutation of 0..num_blocks-1 and no block may be in

@@ -61,6 +61,8 @@ def build(verbose: bool = False) -> str:
          "-o", os.path.join(BUILD, "pa_api.o")],
         [hipcc, *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "block_allocator.cpp"),
          "-o", os.path.join(BUILD, "block_allocator.o")],
+        [hipcc, *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "vmm.cpp"),
+         "-o", os.path.join(BUILD, "vmm.o")],
     ]
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         for f in [ex.submit(_run, j, verbose) for j in jobs]:
@@ -68,7 +70,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp,
           os.path.join(BUILD, "kernels.o"), os.path.join(BUILD, "swap.o"), os.path.join(BUILD, "pa_api.o"),
-          os.path.join(BUILD, "block_allocator.o")], verbose)
+          os.path.join(BUILD, "block_allocator.o"), os.path.join(BUILD, "vmm.o")], verbose)
     os.replace(tmp, LIB)
     # the benchmark's achievable-bandwidth probe (not part of the library)
     probe_src = os.path.join(ROOT, "bench_read_probe.hip")

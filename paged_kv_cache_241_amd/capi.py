@@ -42,7 +42,8 @@ EXPORTS = (
     "pa_set_free_order", "pa_seq_add", "pa_seq_fork", "pa_seq_free", "pa_reserve",
     "pa_get_block_tables", "pa_get_stats", "pa_copy_blocks", "pa_append_kv",
     "pa_decode_partition_tokens", "pa_decode_workspace_bytes", "pa_decode", "pa_append_decode",
-    "pa_swap_bytes", "pa_swap_out", "pa_swap_in", "pa_last_error",
+    "pa_swap_bytes", "pa_swap_out", "pa_swap_in", "pa_create_pool_vmm", "pa_vmm_info",
+    "pa_vmm_trim", "pa_last_error",
 )
 
 
@@ -64,6 +65,13 @@ class pa_stats(ctypes.Structure):
         ("cow_copies", ctypes.c_int64), ("shared_blocks", ctypes.c_int64),
         ("utilisation", ctypes.c_double),
         ("swapped_seqs", ctypes.c_int64), ("swapped_tokens", ctypes.c_int64),
+    ]
+
+
+class pa_vmm_stats(ctypes.Structure):
+    _fields_ = [
+        ("page_bytes", ctypes.c_int64), ("mapped_bytes", ctypes.c_int64),
+        ("budget_bytes", ctypes.c_int64), ("region_bytes", ctypes.c_int64),
     ]
 
 
@@ -106,6 +114,10 @@ def load() -> ctypes.CDLL:
         "pa_swap_bytes": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(ctypes.c_size_t)]),
         "pa_swap_out": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_size_t, _vp]),
         "pa_swap_in": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_size_t, _vp]),
+        "pa_create_pool_vmm": (ctypes.c_int, [ctypes.POINTER(pa_pool_desc), ctypes.c_size_t,
+                                              ctypes.POINTER(_vp)]),
+        "pa_vmm_info": (ctypes.c_int, [_vp, ctypes.POINTER(pa_vmm_stats)]),
+        "pa_vmm_trim": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_int64)]),
         "pa_append_kv": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i32, _vp]),
         "pa_decode_partition_tokens": (ctypes.c_int32, [_vp, _i32, _i32, _i32]),
         "pa_decode_workspace_bytes": (ctypes.c_size_t, [_vp, _i32, _i32, _i32, _i32]),

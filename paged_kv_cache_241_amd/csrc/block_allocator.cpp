@@ -150,20 +150,17 @@ int32_t BlockAllocator::pop_block() {
   return b;
 }
 
-Status BlockAllocator::reserve(const int32_t* rids, int32_t n, const int32_t* counts,
-                               int32_t* slots, int64_t slots_cap, int32_t* pairs,
-                               int32_t pair_cap, int32_t* n_pairs, std::string* err) {
-  if (n < 0 || (n > 0 && rids == nullptr) || pair_cap < 0) {
+Status BlockAllocator::check_growth(const int32_t* rids, int32_t n, const int32_t* counts,
+                                    int64_t* total, std::string* err) const {
+  if (n < 0 || (n > 0 && rids == nullptr)) {
     *err = "reserve: bad request list";
     return kInvalidArg;
   }
-  if (n_pairs) *n_pairs = 0;
-  // validate everything before touching state
   if (++epoch_ == 0) {
     std::fill(mark_.begin(), mark_.end(), 0);
     epoch_ = 1;
   }
-  int64_t total = 0;
+  int64_t sum = 0;
   for (int32_t i = 0; i < n; ++i) {
     Status st = check_resident(rids[i], err);
     if (st != kOk) return st;
@@ -181,7 +178,25 @@ Status BlockAllocator::reserve(const int32_t* rids, int32_t n, const int32_t* co
       *err = "reserve: request " + std::to_string(rids[i]) + " would exceed max_seq_len";
       return kInvalidArg;
     }
-    total += c;
+    sum += c;
+  }
+  *total = sum;
+  return kOk;
+}
+
+Status BlockAllocator::reserve(const int32_t* rids, int32_t n, const int32_t* counts,
+                               int32_t* slots, int64_t slots_cap, int32_t* pairs,
+                               int32_t pair_cap, int32_t* n_pairs, std::string* err) {
+  if (n < 0 || (n > 0 && rids == nullptr) || pair_cap < 0) {
+    *err = "reserve: bad request list";
+    return kInvalidArg;
+  }
+  if (n_pairs) *n_pairs = 0;
+  // validate everything before touching state
+  int64_t total = 0;
+  {
+    Status st = check_growth(rids, n, counts, &total, err);
+    if (st != kOk) return st;
   }
   if (total > slots_cap || (total > 0 && slots == nullptr)) {
     *err = "reserve: slots_out holds " + std::to_string(slots_cap) + " slots, " +

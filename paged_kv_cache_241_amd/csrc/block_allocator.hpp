@@ -58,6 +58,11 @@ class BlockAllocator {
   Status reserve(const int32_t* rids, int32_t n, const int32_t* counts, int32_t* slots,
                  int64_t slots_cap, int32_t* pairs, int32_t pair_cap, int32_t* n_pairs,
                  std::string* err);
+  // The checks reserve makes before it changes anything (ids live and
+  // resident, each listed once, counts >= 0, lengths within max_seq_len);
+  // *total receives the number of slots the call would hand out.
+  Status check_growth(const int32_t* rids, int32_t n, const int32_t* counts, int64_t* total,
+                      std::string* err) const;
   Status tables(const int32_t* rids, int32_t n, int32_t stride, int32_t* out, int32_t* lens,
                 std::string* err) const;
   AllocStats stats() const;
@@ -114,8 +119,8 @@ class BlockAllocator {
   int64_t cow_copies_ = 0;
   int64_t shared_blocks_ = 0;      // blocks with refcount > 1
   // per-call scratch (kept to avoid reallocating on every reserve)
-  std::vector<uint32_t> mark_;
-  uint32_t epoch_ = 0;
+  mutable std::vector<uint32_t> mark_;
+  mutable uint32_t epoch_ = 0;
   std::vector<int32_t> touched_;   // last blocks whose share count a dry run lowered
   std::vector<int32_t> share_;     // dry-run share count of touched blocks
 };

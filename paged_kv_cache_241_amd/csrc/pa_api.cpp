@@ -10,15 +10,20 @@
 #include "../../include/pa.h"
 #include "block_allocator.hpp"
 #include "kernels.hpp"
+#include "vmm.hpp"
 
 struct pa_pool {
   pa_pool_desc desc;
   pa::CacheGeom geom;
   pa::BlockAllocator alloc;
+  pa::VirtualCache* vmm = nullptr;  // demand-paged contiguous caches (owned), or null
   pa_pool(const pa_pool_desc& d, const pa::CacheGeom& g)
       : desc(d),
         geom(g),
         alloc(d.num_blocks, d.block_size, d.max_seqs, d.max_seq_len, d.layout == PA_PAGED) {}
+  ~pa_pool() { delete vmm; }
+  pa_pool(const pa_pool&) = delete;
+  pa_pool& operator=(const pa_pool&) = delete;
 };
 
 namespace {
@@ -112,6 +117,21 @@ bool bad_partition(const pa_pool* p, int32_t partition_tokens) {
 }
 
 
+pa::CacheGeom make_geom(const pa_pool_desc* desc, void* k, void* v) {
+  pa::CacheGeom g;
+  g.k_base = static_cast<char*>(k);
+  g.v_base = static_cast<char*>(v);
+  g.layer_bytes = layer_bytes(desc);
+  g.num_layers = desc->num_layers;
+  g.num_kv_heads = desc->num_kv_heads;
+  g.head_dim = desc->head_dim;
+  g.elt = elt_bytes(desc->kv_dtype);
+  g.block_size = desc->block_size;
+  g.paged = desc->layout == PA_PAGED ? 1 : 0;
+  g.blocks_per_seq = g.paged ? 0 : desc->max_seq_len / desc->block_size;
+  return g;
+}
+
 // Length of a live request of a paged pool (resident or swapped out).
 pa_status swap_length(const pa_pool* pool, int32_t req_id, const char* who, int32_t* len) {
   if (!pool->geom.paged)
@@ -186,20 +206,59 @@ pa_status pa_create_pool(const pa_pool_desc* desc, void* d_k_cache, void* d_v_ca
     return fail(PA_ERR_INVALID_ARG, "create_pool: null cache pointer");
   if ((reinterpret_cast<uintptr_t>(d_k_cache) | reinterpret_cast<uintptr_t>(d_v_cache)) & 15)
     return fail(PA_ERR_INVALID_ARG, "create_pool: caches must be 16-byte aligned");
-  pa::CacheGeom g;
-  g.k_base = static_cast<char*>(d_k_cache);
-  g.v_base = static_cast<char*>(d_v_cache);
-  g.layer_bytes = layer_bytes(desc);
-  g.num_layers = desc->num_layers;
-  g.num_kv_heads = desc->num_kv_heads;
-  g.head_dim = desc->head_dim;
-  g.elt = elt_bytes(desc->kv_dtype);
-  g.block_size = desc->block_size;
-  g.paged = desc->layout == PA_PAGED ? 1 : 0;
-  g.blocks_per_seq = g.paged ? 0 : desc->max_seq_len / desc->block_size;
-  pa_pool* p = new (std::nothrow) pa_pool(*desc, g);
+  pa_pool* p = new (std::nothrow) pa_pool(*desc, make_geom(desc, d_k_cache, d_v_cache));
   if (p == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool: out of host memory");
   *out = p;
+  return PA_OK;
+}
+
+pa_status pa_create_pool_vmm(const pa_pool_desc* desc, size_t physical_bytes, pa_pool** out) {
+  if (out == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool_vmm: null output");
+  *out = nullptr;
+  const std::string why = check_desc(desc);
+  if (!why.empty()) return fail(PA_ERR_INVALID_ARG, "create_pool_vmm: " + why);
+  if (desc->layout != PA_CONTIGUOUS)
+    return fail(PA_ERR_INVALID_ARG, "create_pool_vmm: demand paging backs the contiguous layout");
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_HIP, std::string("create_pool_vmm: ") + hipGetErrorString(e));
+  }
+  const int64_t region = layer_bytes(desc) / desc->max_seqs;
+  pa::VirtualCache* vc = nullptr;
+  const std::string err =
+      pa::VirtualCache::create(desc->num_layers, desc->max_seqs, region, physical_bytes, device, &vc);
+  if (!err.empty()) return fail(PA_ERR_UNSUPPORTED, "create_pool_vmm: " + err);
+  pa_pool* p = new (std::nothrow) pa_pool(*desc, make_geom(desc, vc->k_base(), vc->v_base()));
+  if (p == nullptr) {
+    delete vc;
+    return fail(PA_ERR_INVALID_ARG, "create_pool_vmm: out of host memory");
+  }
+  p->vmm = vc;
+  *out = p;
+  return PA_OK;
+}
+
+pa_status pa_vmm_info(const pa_pool* pool, pa_vmm_stats* out) {
+  if (pool == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_info: null argument");
+  if (pool->vmm == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_info: not a demand-paged pool");
+  out->page_bytes = pool->vmm->page_bytes();
+  out->mapped_bytes = pool->vmm->bytes_mapped();
+  out->budget_bytes = pool->vmm->bytes_budget();
+  out->region_bytes = pool->vmm->region_bytes();
+  return PA_OK;
+}
+
+pa_status pa_vmm_trim(pa_pool* pool, int64_t* freed_bytes_out) {
+  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_trim: null pool");
+  if (pool->vmm == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_trim: not a demand-paged pool");
+  const int64_t before = pool->vmm->bytes_mapped();
+  for (int32_t r = 0; r < pool->desc.max_seqs; ++r) {
+    int32_t len = 0;
+    if (!pool->alloc.length(r, &len)) pool->vmm->trim(r);
+  }
+  if (freed_bytes_out) *freed_bytes_out = before - pool->vmm->bytes_mapped();
   return PA_OK;
 }
 
@@ -242,6 +301,35 @@ pa_status pa_reserve(pa_pool* pool, const int32_t* req_ids, int32_t n, const int
                      int32_t cow_cap, int32_t* n_cow_out) {
   if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "reserve: null pool");
   std::string err;
+  if (pool->vmm != nullptr) {
+    // demand paging: back every listed request's grown prefix first, all or
+    // nothing against the physical budget
+    int64_t total = 0;
+    pa::Status st = pool->alloc.check_growth(req_ids, n, counts, &total, &err);
+    if (st != pa::kOk) return from_alloc(st, err);
+    if (total > slots_cap || (total > 0 && slots_out == nullptr))
+      return fail(PA_ERR_INVALID_ARG, "reserve: slots_out holds " + std::to_string(slots_cap) +
+                                          " slots, " + std::to_string(total) + " needed");
+    const int64_t unit = static_cast<int64_t>(pool->desc.num_kv_heads) * pool->desc.head_dim *
+                         pool->desc.block_size * elt_bytes(pool->desc.kv_dtype);
+    std::vector<int64_t> bytes(n);
+    int64_t more = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      int32_t len = 0;
+      pool->alloc.length(req_ids[i], &len);
+      const int64_t grown = static_cast<int64_t>(len) + (counts ? counts[i] : 1);
+      bytes[i] = (grown + pool->desc.block_size - 1) / pool->desc.block_size * unit;
+      more += pool->vmm->bytes_short(req_ids[i], bytes[i]);
+    }
+    if (more > pool->vmm->bytes_free())
+      return fail(PA_ERR_NO_BLOCKS, "reserve: needs " + std::to_string(more) +
+                                        " more bytes of physical memory, " +
+                                        std::to_string(pool->vmm->bytes_free()) + " left");
+    for (int32_t i = 0; i < n; ++i) {
+      const std::string e = pool->vmm->grow(req_ids[i], bytes[i]);
+      if (!e.empty()) return fail(PA_ERR_HIP, "reserve: " + e);
+    }
+  }
   pa::Status st = pool->alloc.reserve(req_ids, n, counts, slots_out, slots_cap, cow_pairs_out,
                                       cow_cap, n_cow_out, &err);
   return from_alloc(st, err);

@@ -44,10 +44,15 @@ class Pool:
     def __init__(self, num_layers: int, num_blocks: int, block_size: int, num_kv_heads: int,
                  head_dim: int, kv_dtype: str = "bf16", layout: str = "paged",
                  max_seqs: int = 256, max_seq_len: int = 8192, device="cuda", fill=None,
-                 host_only: bool = False):
+                 host_only: bool = False, vmm_bytes: int | None = None):
         """``host_only``: no cache memory is allocated and only the host
         allocator calls may be used (the library never touches the caches in
-        those calls); device calls then fail."""
+        those calls); device calls then fail.
+
+        ``vmm_bytes``: a demand-paged contiguous pool (pa_create_pool_vmm) whose
+        caches the library backs with up to that many bytes of physical pages
+        as requests grow; ``k_cache`` / ``v_cache`` are then None (the library
+        owns the memory and unbacked ranges must not be read)."""
         import torch
 
         self.lib = capi.load()
@@ -64,6 +69,17 @@ class Pool:
         ve = 16 // (2 if kv_dtype == "bf16" else 4)
         k_shape = (num_layers, units, num_kv_heads, head_dim // ve, block_size, ve)
         v_shape = (num_layers, units, num_kv_heads, head_dim, block_size)
+        self.vmm = vmm_bytes is not None
+        if self.vmm:
+            if layout != "contiguous":
+                raise ValueError("demand paging backs the contiguous layout")
+            self.k_cache = self.v_cache = None
+            h = ctypes.c_void_p()
+            capi.check(self.lib.pa_create_pool_vmm(ctypes.byref(self.desc), int(vmm_bytes),
+                                                   ctypes.byref(h)), "pa_create_pool_vmm")
+            self._finish(h, num_layers, num_blocks, block_size, num_kv_heads, head_dim, max_seqs,
+                         max_seq_len, tdt)
+            return
         if host_only:
             self.k_cache = self.v_cache = None
             self._fake = torch.empty(16, dtype=torch.uint8)
@@ -82,15 +98,37 @@ class Pool:
         h = ctypes.c_void_p()
         capi.check(self.lib.pa_create_pool(ctypes.byref(self.desc), kp, vp, ctypes.byref(h)),
                    "pa_create_pool")
+        self._finish(h, num_layers, num_blocks, block_size, num_kv_heads, head_dim, max_seqs,
+                     max_seq_len, tdt)
+
+    def _finish(self, h, num_layers, num_blocks, block_size, num_kv_heads, head_dim, max_seqs,
+                max_seq_len, tdt):
         self.handle = h
         self.num_layers, self.num_blocks, self.block_size = num_layers, num_blocks, block_size
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.max_seqs, self.max_seq_len = max_seqs, max_seq_len
         self.torch_dtype = tdt
+        self._device = self.vmm or self.k_cache is not None
+
+    def vmm_stats(self) -> dict:
+        st = capi.pa_vmm_stats()
+        capi.check(self.lib.pa_vmm_info(self.handle, ctypes.byref(st)), "pa_vmm_info")
+        return {name: getattr(st, name) for name, _ in capi.pa_vmm_stats._fields_}
+
+    def vmm_trim(self) -> int:
+        """Unmap the pages of request ids that are not live (synchronise first)."""
+        freed = ctypes.c_int64()
+        capi.check(self.lib.pa_vmm_trim(self.handle, ctypes.byref(freed)), "pa_vmm_trim")
+        return freed.value
 
     # -- lifetime --------------------------------------------------------------
     def close(self) -> None:
         if getattr(self, "handle", None) is not None and self.handle.value:
+            if getattr(self, "vmm", False):
+                # destroying unmaps the caches: nothing queued may still read them
+                import torch
+
+                torch.cuda.synchronize()
             capi.check(self.lib.pa_destroy_pool(self.handle), "pa_destroy_pool")
             self.handle = None
 
@@ -192,7 +230,7 @@ class Pool:
         n = int(pairs.shape[0]) if pairs is not None else 0
         if n == 0:
             return
-        assert self.k_cache is not None, "host-only pool"
+        assert self._device, "host-only pool"
         assert pairs.dtype.is_floating_point is False and pairs.is_cuda and pairs.is_contiguous()
         assert tuple(pairs.shape) == (n, 2)
         capi.check(self.lib.pa_copy_blocks(self.handle, pairs.data_ptr(), n, _stream_handle(stream)),
@@ -203,7 +241,7 @@ class Pool:
         n = int(slots.shape[0])
         if n == 0:
             return
-        assert self.k_cache is not None, "host-only pool"
+        assert self._device, "host-only pool"
         for t in (k, v):
             assert t.is_cuda and t.is_contiguous() and t.dtype == self.torch_dtype
             assert tuple(t.shape) == (n, self.num_kv_heads, self.head_dim)
@@ -230,7 +268,7 @@ class Pool:
         """
         import torch
 
-        assert self.k_cache is not None, "host-only pool"
+        assert self._device, "host-only pool"
         b, hq, d = q.shape
         assert q.is_cuda and q.is_contiguous() and q.dtype == self.torch_dtype and d == self.head_dim
         assert context_lens.is_cuda and context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (b,)

@@ -201,6 +201,21 @@ def test_swap_refuses_bad_images_and_changes_nothing():
     assert lib.pa_swap_out(c.handle, q, None, 0, None) == capi.PA_ERR_INVALID_ARG
 
 
+def test_demand_paged_pool_is_refused_where_it_cannot_work():
+    import ctypes
+
+    lib = capi.load()
+    out = ctypes.c_void_p()
+    paged = capi.pa_pool_desc(1, 16, 16, 1, 64, capi.PA_F32, capi.PA_PAGED, 4, 64)
+    assert lib.pa_create_pool_vmm(ctypes.byref(paged), 1 << 20, ctypes.byref(out)) == \
+        capi.PA_ERR_INVALID_ARG
+    # a request's sub-range of 64 x 64 x 4 B = 16 KiB is below any page size
+    # (without a device: no HIP device at all)
+    small = capi.pa_pool_desc(1, 0, 16, 1, 64, capi.PA_F32, capi.PA_CONTIGUOUS, 4, 64)
+    st = lib.pa_create_pool_vmm(ctypes.byref(small), 1 << 20, ctypes.byref(out))
+    assert st in (capi.PA_ERR_UNSUPPORTED, capi.PA_ERR_HIP) and not out.value
+
+
 def test_contiguous_mode_bit_exact():
     ref, lib = _make(0, 16, 4, 64, layout=AL.CONTIGUOUS)
     ids = [_both(ref, lib, lambda a: a.add())[1] for _ in range(3)]
