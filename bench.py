@@ -244,15 +244,22 @@ class Bench:
         longest = int(max(self.length[r] for r in self.batch)) + max_steps + 1
         self.stride = -(-longest // bs) if self.layout == "paged" else 1
         dev = self.dev
-        self.slots_d = torch.empty(b, dtype=torch.int32, device=dev)
-        self.lens_d = torch.empty(b, dtype=torch.int32, device=dev)
-        self.tables_d = torch.full((b, self.stride), -1, dtype=torch.int32, device=dev)
+        # slots, lengths and tables side by side, so that one copy uploads a
+        # step's arguments (the tables only when they changed)
+        self.n_small = 2 * b
+        self.n_all = 2 * b + b * self.stride
+        self.args_d = torch.full((self.n_all,), -1, dtype=torch.int32, device=dev)
+        self.slots_d = self.args_d[:b]
+        self.lens_d = self.args_d[b:2 * b]
+        self.tables_d = self.args_d[2 * b:].view(b, self.stride)
         self.stage = []
         for _ in range(2):
+            buf = torch.empty(self.n_all, dtype=torch.int32).pin_memory()
             self.stage.append({
-                "slots": torch.empty(b, dtype=torch.int32).pin_memory(),
-                "lens": torch.empty(b, dtype=torch.int32).pin_memory(),
-                "tables": torch.empty((b, self.stride), dtype=torch.int32).pin_memory(),
+                "buf": buf,
+                "slots": buf[:b],
+                "lens": buf[b:2 * b],
+                "tables": buf[2 * b:].view(b, self.stride),
                 "pairs": torch.empty((b, 2), dtype=torch.int32).pin_memory(),
                 "event": torch.cuda.Event(),
             })
@@ -291,13 +298,13 @@ class Bench:
             self.check(lib.pa_get_block_tables(pool.handle, self.rids_c, b, self.stride,
                                                self.p32(st["tables"]), self.p32(st["lens"])),
                        "pa_get_block_tables")
-            self.tables_d.copy_(st["tables"], non_blocking=True)
+            n = self.n_all
             self.tables_dirty = False
         else:
             self.check(lib.pa_get_block_tables(pool.handle, self.rids_c, b, 0, None,
                                                self.p32(st["lens"])), "pa_get_block_tables")
-        self.lens_d.copy_(st["lens"], non_blocking=True)
-        self.slots_d.copy_(st["slots"], non_blocking=True)
+            n = self.n_small
+        self.args_d[:n].copy_(st["buf"][:n], non_blocking=True)
         if self.ncow.value:
             n = self.ncow.value
             self.pairs_d[:n].copy_(st["pairs"][:n], non_blocking=True)
