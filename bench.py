@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--prompt-len", type=int, default=0, help="workload 5: prompt length")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--block-size", type=int, default=0, help="tokens per block (0: workload's, 16)")
+    ap.add_argument("--shared-prefix", type=int, default=0, metavar="TOKENS",
+                    help="decode with pa_decode_shared in partitions of TOKENS tokens (samples "
+                         "sharing a prompt read its blocks once)")
     ap.add_argument("--separate-append", action="store_true",
                     help="pa_append_kv then pa_decode per layer instead of one pa_append_decode")
     ap.add_argument("--layers", type=int, default=0, help="layer pools rotated (0: workload's)")
@@ -229,8 +232,11 @@ class Bench:
             self.pool.append_kv(layer, kr.index_select(0, it).contiguous(),
                                 vr.index_select(0, it).contiguous(), st)
 
-    def prepare(self, max_steps: int, separate_append: bool = False):
-        """Fixed device buffers, double-buffered pinned staging, ctypes arguments."""
+    def prepare(self, max_steps: int, separate_append: bool = False, shared_tokens: int = 0):
+        """Fixed device buffers, double-buffered pinned staging, ctypes arguments.
+
+        shared_tokens > 0: decode with pa_decode_shared in partitions of that
+        many tokens (its append is a separate pa_append_kv)."""
         import ctypes
 
         import torch
@@ -269,6 +275,16 @@ class Bench:
         self.p32 = lambda t: ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_int32))
         self.stream = torch.cuda.current_stream()
         self.sh = ctypes.c_void_p(self.stream.cuda_stream)
+        self.shared_T = shared_tokens
+        if shared_tokens:
+            separate_append = True
+            self.pt = shared_tokens
+            parts = max(2, -(-self.cfg.max_seq_len // shared_tokens))
+            need = b * self.cfg.num_q_heads * parts * (self.cfg.head_dim + 2) * 4
+            self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            self.sh_seq = torch.zeros(b, dtype=torch.int32, device=dev)
+            self.sh_groups = torch.zeros((b, 2), dtype=torch.int32, device=dev)
+            self.update_groups()
         if self.ws is None:
             need = self.pool.workspace_bytes(b, self.cfg.num_q_heads, self.cfg.max_seq_len, self.pt)
             self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
@@ -279,6 +295,14 @@ class Bench:
         self.nstep = 0
         # the tables only change when a block is handed out: upload on demand
         self.tables_dirty = True
+
+    def update_groups(self):
+        """Groups of the batch sharing a block prefix (pa_shared_groups), to the device."""
+        seq, groups, mm, ms = self.pool.shared_groups(self.batch, self.shared_T)
+        self.sh_seq.copy_(self.torch.from_numpy(np.ascontiguousarray(seq)))
+        if len(groups):
+            self.sh_groups[: len(groups)].copy_(self.torch.from_numpy(np.ascontiguousarray(groups)))
+        self.sh_ng, self.sh_mm, self.sh_ms = len(groups), mm, ms
 
     def step(self, ev=None):
         """One decode iteration over all layers; returns the contexts it attended."""
@@ -300,6 +324,8 @@ class Bench:
                        "pa_get_block_tables")
             n = self.n_all
             self.tables_dirty = False
+            if self.shared_T:
+                self.update_groups()
         else:
             self.check(lib.pa_get_block_tables(pool.handle, self.rids_c, b, 0, None,
                                                self.p32(st["lens"])), "pa_get_block_tables")
@@ -326,7 +352,14 @@ class Bench:
             tail = (self.q[layer].data_ptr(), self.dtype_code, cfg.num_q_heads, self.scale, tables,
                     self.stride, req, self.lens_d.data_ptr(), b, max_context, self.pt,
                     self.out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, self.sh)
-            if self.separate_append:
+            if self.shared_T:
+                self.check(lib.pa_decode_shared(
+                    pool.handle, layer, self.q[layer].data_ptr(), self.dtype_code, cfg.num_q_heads,
+                    self.scale, tables, self.stride, self.lens_d.data_ptr(), b, max_context,
+                    self.shared_T, self.sh_seq.data_ptr(), self.sh_groups.data_ptr(), self.sh_ng,
+                    self.sh_mm, self.sh_ms, self.out.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
+                    self.sh), "pa_decode_shared")
+            elif self.separate_append:
                 self.check(lib.pa_decode(pool.handle, layer, *tail), "pa_decode")
             else:
                 self.check(lib.pa_append_decode(pool.handle, layer, self.k_new[layer].data_ptr(),
@@ -522,7 +555,9 @@ def main():
     cfg = W.get(args.config, **over)
     nl = args.layers or cfg.num_layers
     bench = Bench(cfg, args.layout, nl, args.warmup + args.steps + 1, args.partition_tokens)
-    bench.prepare(args.warmup + args.steps, args.separate_append)
+    if args.shared_prefix:
+        args.separate_append = True
+    bench.prepare(args.warmup + args.steps, args.separate_append, args.shared_prefix)
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
@@ -548,7 +583,7 @@ def main():
     achieved = total_alg / (args.steps * nl) / per_launch_s / 1e9
     value = total_kv / dt / 1e9
     b = len(bench.batch)
-    part = bench.pool.partition_tokens(b, int(max(lens)), args.partition_tokens)
+    part = args.shared_prefix or bench.pool.partition_tokens(b, int(max(lens)), args.partition_tokens)
     stats = bench.pool.stats()
     res = {
         "metric": METRIC,
@@ -569,6 +604,8 @@ def main():
             "head_dim": cfg.head_dim, "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
             "mean_context_timed": round(float(np.mean(lens_seen)), 2),
             "layers_rotated": nl, "partition_tokens": part, "layout": args.layout,
+            "decode": "shared prefixes read once (pa_decode_shared)" if args.shared_prefix else
+                      ("pa_append_kv + pa_decode" if args.separate_append else "pa_append_decode"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_us_per_layer": round(per_launch_s * 1e6, 3),
@@ -577,8 +614,10 @@ def main():
         "pool_utilisation": round(stats["utilisation"], 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("pa_decode" if args.separate_append else "pa_append_decode") +
-                      " (decode_partition_kernel, + decode_merge_kernel when contexts are split)",
+            "kernel": ("pa_decode_shared (decode_shared_kernel + decode_partition_kernel + "
+                       "decode_merge_kernel)" if args.shared_prefix else
+                       ("pa_decode" if args.separate_append else "pa_append_decode") +
+                       " (decode_partition_kernel, + decode_merge_kernel when contexts are split)"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

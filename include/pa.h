@@ -226,6 +226,45 @@ pa_status pa_get_block_tables(const pa_pool* pool, const int32_t* req_ids, int32
 
 pa_status pa_get_stats(const pa_pool* pool, pa_stats* out);
 
+/* ---- shared prefixes: one read of a shared block for all its sharers ------
+ * Samples of one prompt (pa_seq_fork) point at the same physical blocks
+ * ([PAS] Summary and Key points; [ROC] "Fragmentation is lost users"), so
+ * their attention over those blocks reads the same K and V.  pa_decode_shared
+ * reads each shared block once per group and KV head and attends every
+ * member's query heads to it; the rest of each context is decoded as by
+ * pa_decode, and the partitions are merged in the same order. */
+
+/* Find the groups among req_ids (in the order given, as the batch will be):
+ * runs of at least two consecutive requests whose block tables start with
+ * the same blocks for at least partition_tokens tokens.  For each request i,
+ * seq_shared_out[i] gets the tokens its group shares, cut to a multiple of
+ * partition_tokens and to every member's length (0 outside groups);
+ * groups_out[2g] and groups_out[2g+1] get the batch index of group g's first
+ * member and its member count (capacity 2n); *n_groups_out the number of
+ * groups; *max_members_out and *max_shared_out the largest group and shared
+ * prefix (0 if none).  Paged only; partition_tokens as for pa_decode. */
+pa_status pa_shared_groups(const pa_pool* pool, const int32_t* req_ids, int32_t n,
+                           int32_t partition_tokens, int32_t* seq_shared_out, int32_t* groups_out,
+                           int32_t* n_groups_out, int32_t* max_members_out, int32_t* max_shared_out);
+
+/* pa_decode for a batch whose groups pa_shared_groups found (the batch in
+ * the order given to it): d_seq_shared (device int32 [num_seqs]) and d_groups
+ * (device int32 [num_groups][2]) are its outputs copied to the device, and
+ * num_groups, max_members, max_shared its host outputs; partition_tokens must
+ * be the one given to it.  The result is pa_decode's with the same
+ * partition_tokens up to the order of fp32 sums within the shared partitions.
+ * The workspace holds max(2, ceil(max_context / partition_tokens)) partitions:
+ * pa_decode_workspace_bytes(pool, num_seqs, num_q_heads,
+ * max(max_context, partition_tokens + 1), partition_tokens) bytes.  Paged
+ * only; query heads per KV head <= 16. */
+pa_status pa_decode_shared(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
+                           int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                           int32_t table_stride, const int32_t* d_context_lens, int32_t num_seqs,
+                           int32_t max_context, int32_t partition_tokens, const int32_t* d_seq_shared,
+                           const int32_t* d_groups, int32_t num_groups, int32_t max_members,
+                           int32_t max_shared, float* d_out, void* d_workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* ---- pre-emption by swapping ([ROC] "Fragmentation is lost users" and the
  * Pre-emption term: when paging runs out, a request's cache is evicted and
  * swapped back in later; [PAS] Summary: the scheduler pre-empts requests) ----

@@ -57,6 +57,8 @@ def build(verbose: bool = False) -> str:
          "-o", os.path.join(BUILD, "kernels.o")],
         [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "swap.hip"),
          "-o", os.path.join(BUILD, "swap.o")],
+        [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "decode_shared.hip"),
+         "-o", os.path.join(BUILD, "decode_shared.o")],
         [hipcc, *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "pa_api.cpp"),
          "-o", os.path.join(BUILD, "pa_api.o")],
         [hipcc, *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "block_allocator.cpp"),
@@ -69,7 +71,8 @@ def build(verbose: bool = False) -> str:
             f.result()
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp,
-          os.path.join(BUILD, "kernels.o"), os.path.join(BUILD, "swap.o"), os.path.join(BUILD, "pa_api.o"),
+          os.path.join(BUILD, "kernels.o"), os.path.join(BUILD, "swap.o"),
+          os.path.join(BUILD, "decode_shared.o"), os.path.join(BUILD, "pa_api.o"),
           os.path.join(BUILD, "block_allocator.o"), os.path.join(BUILD, "vmm.o")], verbose)
     os.replace(tmp, LIB)
     # the benchmark's achievable-bandwidth probe (not part of the library)

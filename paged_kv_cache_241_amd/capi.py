@@ -43,7 +43,7 @@ EXPORTS = (
     "pa_get_block_tables", "pa_get_stats", "pa_copy_blocks", "pa_append_kv",
     "pa_decode_partition_tokens", "pa_decode_workspace_bytes", "pa_decode", "pa_append_decode",
     "pa_swap_bytes", "pa_swap_out", "pa_swap_in", "pa_create_pool_vmm", "pa_vmm_info",
-    "pa_vmm_trim", "pa_last_error",
+    "pa_vmm_trim", "pa_shared_groups", "pa_decode_shared", "pa_last_error",
 )
 
 
@@ -118,6 +118,11 @@ def load() -> ctypes.CDLL:
                                               ctypes.POINTER(_vp)]),
         "pa_vmm_info": (ctypes.c_int, [_vp, ctypes.POINTER(pa_vmm_stats)]),
         "pa_vmm_trim": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_int64)]),
+        "pa_shared_groups": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(_i32),
+                                            ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+        "pa_decode_shared": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _i32, ctypes.c_float, _vp,
+                                            _i32, _vp, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32,
+                                            _vp, _vp, ctypes.c_size_t, _vp]),
         "pa_append_kv": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i32, _vp]),
         "pa_decode_partition_tokens": (ctypes.c_int32, [_vp, _i32, _i32, _i32]),
         "pa_decode_workspace_bytes": (ctypes.c_size_t, [_vp, _i32, _i32, _i32, _i32]),

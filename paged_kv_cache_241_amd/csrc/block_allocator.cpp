@@ -412,4 +412,47 @@ void BlockAllocator::swap_in_undo(int32_t rid) {
   s.swapped = true;
 }
 
+Status BlockAllocator::shared_groups(const int32_t* rids, int32_t n, int32_t unit,
+                                     int32_t* seq_shared, int32_t* groups, int32_t* n_groups,
+                                     int32_t* max_members, int32_t* max_shared,
+                                     std::string* err) const {
+  if (!paged_ || n < 0 || (n > 0 && rids == nullptr) || unit <= 0) {
+    *err = "shared_groups: bad arguments";
+    return kInvalidArg;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    Status st = check_resident(rids[i], err);
+    if (st != kOk) return st;
+  }
+  *n_groups = 0;
+  *max_members = 0;
+  *max_shared = 0;
+  int32_t i = 0;
+  while (i < n) {
+    const Seq& f = seqs_[rids[i]];
+    int64_t common = f.len;
+    int32_t j = i + 1;
+    for (; j < n; ++j) {
+      const Seq& o = seqs_[rids[j]];
+      size_t k = 0;
+      while (k < f.table.size() && k < o.table.size() && f.table[k] == o.table[k]) ++k;
+      const int64_t c = std::min<int64_t>(static_cast<int64_t>(k) * block_size_, std::min(f.len, o.len));
+      if (c < unit) break;
+      common = std::min(common, c);
+    }
+    const int32_t members = j - i;
+    const int32_t shared = members >= 2 ? static_cast<int32_t>(common / unit * unit) : 0;
+    for (int32_t k = i; k < j; ++k) seq_shared[k] = shared;
+    if (shared > 0) {
+      groups[2 * *n_groups] = i;
+      groups[2 * *n_groups + 1] = members;
+      ++*n_groups;
+      *max_members = std::max(*max_members, members);
+      *max_shared = std::max(*max_shared, shared);
+    }
+    i = j;
+  }
+  return kOk;
+}
+
 }  // namespace pa

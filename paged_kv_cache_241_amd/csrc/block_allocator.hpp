@@ -67,6 +67,15 @@ class BlockAllocator {
                 std::string* err) const;
   AllocStats stats() const;
 
+  // Groups of consecutive requests (in the order given) whose tables start
+  // with the same blocks: each run of at least two whose common prefix, cut
+  // to whole units of `unit` tokens and to every member's length, is at
+  // least one unit.  seq_shared[i] gets request i's shared tokens (0 outside
+  // groups), groups[2g], groups[2g+1] the first index and size of group g.
+  Status shared_groups(const int32_t* rids, int32_t n, int32_t unit, int32_t* seq_shared,
+                       int32_t* groups, int32_t* n_groups, int32_t* max_members,
+                       int32_t* max_shared, std::string* err) const;
+
   // Swap-out, in two steps so that the caller can copy the blocks out first:
   // swap_out_blocks reads the resident request's table (its blocks in logical
   // order) and changes nothing; swap_out releases the blocks.

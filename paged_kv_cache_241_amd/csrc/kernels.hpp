@@ -63,12 +63,32 @@ struct DecodeArgs {
   int32_t waves = 4;                 // waves per workgroup: 4 or 8
   int32_t streaming = 1;             // non-temporal K/V loads (no block is shared)
   float scale = 1.0f;
+  // shared-prefix decode: the first seq_shared[s] tokens of sequence s (whole
+  // partitions) are attended by decode_shared_kernel; the partition kernel
+  // skips them.  Null: none.
+  const int32_t* seq_shared = nullptr;
+};
+
+// Groups of sequences whose contexts start with the same blocks
+// (pa_decode_shared): group i is sequences groups[2i] .. groups[2i] +
+// groups[2i+1] - 1 of the batch, all with seq_shared[groups[2i]] shared tokens.
+struct SharedArgs {
+  const int32_t* groups = nullptr;   // [num_groups][2]: first sequence, members
+  int32_t num_groups = 0;
+  int32_t col_blocks = 1;            // workgroups per (group, KV head, partition): 64 query columns each
+  int32_t shared_parts = 0;          // partitions of the longest shared prefix
 };
 
 // Returns hipErrorInvalidValue-free codes from the launch; *supported is set
 // to false (and nothing is launched) when no kernel exists for the shape.
 hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool* supported,
                          hipStream_t stream);
+
+// The shared-prefix pass: partials of every group's shared partitions, for
+// all its members' query heads (a.seq_shared and the split-K workspace are
+// set; launch_decode afterwards does the private partitions and the merge).
+hipError_t launch_decode_shared(const CacheGeom& g, int kind, const DecodeArgs& a,
+                                const SharedArgs& sh, bool* supported, hipStream_t stream);
 
 // Bytes of decode partials for these sizes.
 inline size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,

@@ -2,6 +2,7 @@
 // block allocator and kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <new>
 #include <string>
@@ -116,6 +117,8 @@ bool bad_partition(const pa_pool* p, int32_t partition_tokens) {
   return partition_tokens < 0 || partition_tokens % partition_unit(p) != 0;
 }
 
+
+int32_t num_queries_per_kv(int32_t num_q_heads, int32_t num_kv_heads) { return num_q_heads / num_kv_heads; }
 
 pa::CacheGeom make_geom(const pa_pool_desc* desc, void* k, void* v) {
   pa::CacheGeom g;
@@ -467,8 +470,11 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
                       const int32_t* d_block_tables, int32_t table_stride,
                       const int32_t* d_req_ids, const int32_t* d_context_lens, int32_t num_seqs,
                       int32_t max_context, int32_t partition_tokens, float* d_out,
-                      void* d_workspace, size_t workspace_bytes, void* stream) {
+                      void* d_workspace, size_t workspace_bytes, void* stream,
+                      const int32_t* d_seq_shared = nullptr, const int32_t* d_groups = nullptr,
+                      int32_t num_groups = 0, int32_t max_members = 0, int32_t max_shared = 0) {
   const std::string w(who);
+  const bool shared = d_seq_shared != nullptr;
   if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null pool");
   const pa_pool_desc& d = pool->desc;
   if (layer < 0 || layer >= d.num_layers) return fail(PA_ERR_INVALID_ARG, w + ": layer out of range");
@@ -496,6 +502,15 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
       return fail(PA_ERR_INVALID_ARG, w + ": table_stride is shorter than ceil(max_context / block_size)");
   }
   if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, w + ": scale is NaN");
+  if (shared) {
+    if (d.layout != PA_PAGED) return fail(PA_ERR_INVALID_ARG, w + ": shared prefixes need the paged layout");
+    if (partition_tokens <= 0)
+      return fail(PA_ERR_INVALID_ARG, w + ": give partition_tokens (the shared prefixes are whole partitions)");
+    if (num_groups < 0 || max_shared < 0 || max_shared % partition_tokens != 0 || max_shared > max_context)
+      return fail(PA_ERR_INVALID_ARG, w + ": max_shared must be a multiple of partition_tokens within max_context");
+    if (num_groups > 0 && (d_groups == nullptr || max_members < 1))
+      return fail(PA_ERR_INVALID_ARG, w + ": null groups or max_members < 1");
+  }
   const int64_t grid = static_cast<int64_t>(num_seqs) * d.num_kv_heads;
   pa::DecodeArgs a;
   a.q = d_q;
@@ -510,13 +525,20 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
   const int32_t pt = choose_partition_tokens(pool, num_seqs, max_context, partition_tokens);
   a.partition_chunks = pt / 16;
   a.num_partitions = num_partitions(max_context, pt);
+  if (shared) {
+    // partials and the merge even where one partition would cover a context
+    a.num_partitions = std::max(a.num_partitions, 2);
+    a.seq_shared = d_seq_shared;
+  }
   a.waves = PA_DECODE_WAVES;
   if (d_k_new != nullptr) {
     a.new_k = d_k_new;
     a.new_v = d_v_new;
     a.new_slots = d_slots;
   }
-  a.streaming = pool->alloc.shared_blocks() == 0 ? 1 : 0;
+  // the shared pass reads shared blocks once; the partition kernel then reads
+  // private blocks only
+  a.streaming = shared || pool->alloc.shared_blocks() == 0 ? 1 : 0;
   a.scale = scale;
   if (grid * a.num_partitions > INT32_MAX) return fail(PA_ERR_INVALID_ARG, w + ": launch too large");
   const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, d.head_dim, a.num_partitions);
@@ -530,6 +552,20 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
   }
   bool supported = true;
   const int kind = d.kv_dtype == PA_BF16 ? pa::kBF16 : pa::kF32;
+  if (shared && num_groups > 0 && max_shared > 0) {
+    pa::SharedArgs sh;
+    sh.groups = d_groups;
+    sh.num_groups = num_groups;
+    const int64_t cols = static_cast<int64_t>(max_members) * (num_queries_per_kv(num_q_heads, d.num_kv_heads));
+    sh.col_blocks = static_cast<int32_t>((cols + 63) / 64);
+    sh.shared_parts = max_shared / pt;
+    if (static_cast<int64_t>(num_groups) * d.num_kv_heads * sh.col_blocks * sh.shared_parts > INT32_MAX)
+      return fail(PA_ERR_INVALID_ARG, w + ": launch too large");
+    hipError_t es = pa::launch_decode_shared(pool->geom, kind, a, sh, &supported,
+                                             static_cast<hipStream_t>(stream));
+    if (!supported) return fail(PA_ERR_UNSUPPORTED, w + ": no kernel for this shape");
+    if (es != hipSuccess) return fail(PA_ERR_HIP, std::string(w + ": ") + hipGetErrorString(es));
+  }
   hipError_t e = pa::launch_decode(pool->geom, kind, a, &supported, static_cast<hipStream_t>(stream));
   if (!supported) return fail(PA_ERR_UNSUPPORTED, w + ": no kernel for this shape");
   if (e != hipSuccess) return fail(PA_ERR_HIP, std::string(w + ": ") + hipGetErrorString(e));
@@ -564,6 +600,35 @@ pa_status pa_append_decode(pa_pool* pool, int32_t layer, const void* d_k, const 
   return decode_impl("append_decode", pool, layer, d_k, d_v, d_slots, d_q, q_dtype, num_q_heads,
                      scale, d_block_tables, table_stride, d_req_ids, d_context_lens, num_seqs,
                      max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream);
+}
+
+pa_status pa_shared_groups(const pa_pool* pool, const int32_t* req_ids, int32_t n,
+                           int32_t partition_tokens, int32_t* seq_shared_out, int32_t* groups_out,
+                           int32_t* n_groups_out, int32_t* max_members_out, int32_t* max_shared_out) {
+  if (pool == nullptr || seq_shared_out == nullptr || groups_out == nullptr || n_groups_out == nullptr ||
+      max_members_out == nullptr || max_shared_out == nullptr)
+    return fail(PA_ERR_INVALID_ARG, "shared_groups: null argument");
+  if (!pool->geom.paged) return fail(PA_ERR_INVALID_ARG, "shared_groups: sharing needs the paged layout");
+  if (bad_partition(pool, partition_tokens) || partition_tokens <= 0)
+    return fail(PA_ERR_INVALID_ARG, "shared_groups: partition_tokens must be a positive multiple of 16 and of block_size");
+  std::string err;
+  pa::Status st = pool->alloc.shared_groups(req_ids, n, partition_tokens, seq_shared_out, groups_out,
+                                            n_groups_out, max_members_out, max_shared_out, &err);
+  return from_alloc(st, err);
+}
+
+pa_status pa_decode_shared(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
+                           int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                           int32_t table_stride, const int32_t* d_context_lens, int32_t num_seqs,
+                           int32_t max_context, int32_t partition_tokens, const int32_t* d_seq_shared,
+                           const int32_t* d_groups, int32_t num_groups, int32_t max_members,
+                           int32_t max_shared, float* d_out, void* d_workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (d_seq_shared == nullptr) return fail(PA_ERR_INVALID_ARG, "decode_shared: null seq_shared");
+  return decode_impl("decode_shared", pool, layer, nullptr, nullptr, nullptr, d_q, q_dtype, num_q_heads,
+                     scale, d_block_tables, table_stride, nullptr, d_context_lens, num_seqs,
+                     max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream,
+                     d_seq_shared, d_groups, num_groups, max_members, max_shared);
 }
 
 const char* pa_last_error(void) { return g_err.c_str(); }

@@ -193,6 +193,47 @@ class Pool:
                                                 _ptr32(tables), _ptr32(lens)), "pa_get_block_tables")
         return tables[:n], lens[:n]
 
+    # -- shared prefixes ------------------------------------------------------
+    def shared_groups(self, req_ids, partition_tokens: int):
+        """Groups of consecutive requests with a common block prefix (pa_shared_groups):
+        (seq_shared int32[n], groups int32[g][2], max_members, max_shared)."""
+        rids = np.ascontiguousarray(req_ids, dtype=np.int32)
+        n = len(rids)
+        seq_shared = np.zeros(max(n, 1), dtype=np.int32)
+        groups = np.zeros((max(n, 1), 2), dtype=np.int32)
+        ng, mm, ms = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        capi.check(self.lib.pa_shared_groups(self.handle, _ptr32(rids), n, int(partition_tokens),
+                                             _ptr32(seq_shared), _ptr32(groups), ctypes.byref(ng),
+                                             ctypes.byref(mm), ctypes.byref(ms)), "pa_shared_groups")
+        return seq_shared[:n], groups[: ng.value], mm.value, ms.value
+
+    def decode_shared(self, layer: int, q, scale: float, block_tables, context_lens, max_context: int,
+                      partition_tokens: int, seq_shared, groups, max_members: int, max_shared: int,
+                      out=None, workspace=None, stream=None):
+        """pa_decode_shared: seq_shared int32 [B] and groups int32 [g][2] on the device."""
+        import torch
+
+        assert self._device, "host-only pool"
+        b, hq, d = q.shape
+        assert q.is_cuda and q.is_contiguous() and q.dtype == self.torch_dtype and d == self.head_dim
+        for t in (block_tables, context_lens, seq_shared, groups):
+            assert t.is_cuda and t.dtype == torch.int32 and t.is_contiguous()
+        assert tuple(seq_shared.shape) == (b,) and tuple(context_lens.shape) == (b,)
+        if out is None:
+            out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            parts = max(2, -(-int(max_context) // int(partition_tokens)))
+            need = b * hq * parts * (self.head_dim + 2) * 4
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        capi.check(self.lib.pa_decode_shared(
+            self.handle, layer, q.data_ptr(), _DTYPES[self.kv_dtype], hq, float(scale),
+            block_tables.data_ptr(), int(block_tables.shape[1]), context_lens.data_ptr(), b,
+            int(max_context), int(partition_tokens), seq_shared.data_ptr(),
+            groups.data_ptr() if groups.numel() else None, int(groups.shape[0]), int(max_members),
+            int(max_shared), out.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_handle(stream)), "pa_decode_shared")
+        return out
+
     # -- pre-emption by swapping ---------------------------------------------
     def swap_bytes(self, rid: int) -> int:
         """Bytes of request rid's swap image (include/pa.h lays it out)."""

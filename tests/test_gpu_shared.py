@@ -1,0 +1,98 @@
+"""GPU: shared-prefix decode (pa_decode_shared) against the oracle and pa_decode.
+
+Samples of one prompt share its blocks; pa_decode_shared reads them once per
+group and KV head.  Its output must meet the same tolerances against the fp64
+oracle as pa_decode, and differ from pa_decode with the same partitions only
+by the order of fp32 sums.  Cases: bf16 and fp32, head_dim 64 and 128, blocks
+of 8, 16 and 32, groups wider than one 64-column block, and a batch order that
+mixes groups of several sizes with requests outside any group.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+from gpu_harness import Case, row_rel_err, to_f64
+
+pytestmark = pytest.mark.gpu
+
+F32_ABS = 1e-5
+BF16_STATED = 2e-2
+BF16_INTERNAL = 1e-4
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _run_shared(case: Case, T: int, order):
+    """pa_decode_shared over the batch in `order` (indices into the batch)."""
+    rids = [case.batch_rids[i] for i in order]
+    seq_shared, groups, mm, ms = case.pool.shared_groups(rids, T)
+    idx = torch.tensor(order, dtype=torch.int64, device="cuda")
+    q = case.vals[0][0].index_select(0, idx).contiguous()
+    tables = case.tables.index_select(0, idx).contiguous()
+    lens = case.lens.index_select(0, idx).contiguous()
+    out = case.pool.decode_shared(0, q, case.scale, tables, lens, case.max_context, T,
+                                  torch.from_numpy(seq_shared).cuda(),
+                                  torch.from_numpy(np.ascontiguousarray(groups)).cuda().view(-1, 2),
+                                  mm, ms)
+    torch.cuda.synchronize()
+    back = torch.empty_like(out)
+    back[idx] = out
+    return back, seq_shared, groups
+
+
+def _check_oracle(case: Case, got: torch.Tensor):
+    g = to_f64(got)
+    ref = case.reference(range(case.cfg.batch))
+    for s in range(case.cfg.batch):
+        if case.cfg.kv_dtype == "f32":
+            assert float(np.max(np.abs(g[s] - ref[s]))) <= F32_ABS, s
+        else:
+            err = row_rel_err(g[s], ref[s])
+            assert err <= BF16_STATED and err <= BF16_INTERNAL, (s, err)
+
+
+@pytest.mark.parametrize("over,T", [
+    ({"batch": 24, "prompt_len": 200, "private_len": 40, "num_blocks": 200}, 32),
+    ({"batch": 24, "prompt_len": 200, "private_len": 40, "num_blocks": 200, "head_dim": 64,
+      "kv_dtype": "f32"}, 64),
+    ({"batch": 24, "prompt_len": 200, "private_len": 40, "num_blocks": 400, "block_size": 8}, 16),
+    ({"batch": 24, "prompt_len": 200, "private_len": 40, "num_blocks": 120, "block_size": 32}, 64),
+    # 16 samples x 8 query heads per KV head = 128 columns: two column blocks
+    ({"batch": 32, "samples": 16, "prompt_len": 100, "private_len": 10, "num_blocks": 200}, 32),
+])
+def test_shared_decode_matches_oracle_and_plain_decode(over, T):
+    cfg = W.get(5, **over)
+    case = Case(cfg)
+    got, seq_shared, groups = _run_shared(case, T, list(range(cfg.batch)))
+    assert len(groups) == cfg.batch // cfg.samples and int(seq_shared.min()) > 0
+    _check_oracle(case, got)
+    plain = case.decode(partition_tokens=T)
+    for s in range(cfg.batch):
+        err = row_rel_err(to_f64(got[s]), to_f64(plain[s]))
+        assert err <= 1e-5, (s, err)
+
+
+def test_mixed_groups_and_singletons():
+    cfg = W.get(5, batch=24, prompt_len=200, private_len=40, num_blocks=200)
+    case = Case(cfg)
+    # prompt-major batch: samples of prompt p are 8p .. 8p+7
+    order = [0, 1, 2, 8, 3, 4, 16, 5, 6, 7] + list(range(9, 16)) + list(range(17, 24))
+    got, seq_shared, groups = _run_shared(case, 32, order)
+    sizes = [int(g[1]) for g in groups]
+    assert sizes == [3, 2, 3, 7, 7]
+    assert int((seq_shared == 0).sum()) == 2
+    _check_oracle(case, got)
+    plain = case.decode(partition_tokens=32)
+    for s in range(cfg.batch):
+        assert row_rel_err(to_f64(got[s]), to_f64(plain[s])) <= 1e-5, s
