@@ -408,8 +408,6 @@ def measured_traffic(workload: str):
     one workload and one kernel source; the figure is used only while both
     still match (the kernel source's SHA-256 is compared).
     """
-    import hashlib
-
     try:
         text = open(COUNTERS_FILE).read()
     except OSError:
@@ -422,11 +420,24 @@ def measured_traffic(workload: str):
                 fields = kv
     if not fields:
         return None
-    src = os.path.join(ROOT, "paged_kv_cache_241_amd", "csrc", "kernels.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if digest != fields.get("kernels_hip_sha256_16"):
+    if kernel_source_digest() != fields.get("kernel_src_sha256_16"):
         return None
     return int(fields["traffic_bytes_per_launch"])
+
+
+# the sources the decode partition kernel is compiled from
+KERNEL_SOURCES = ("kernels.hip", "decode_common.hpp", "kernels.hpp")
+
+
+def kernel_source_digest() -> str:
+    """First 16 hex digits of SHA-256 over the partition kernel's sources, in order."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_241_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def kv_bytes(cfg, lens) -> int:

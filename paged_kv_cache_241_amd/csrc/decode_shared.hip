@@ -9,14 +9,19 @@
 // partition of the shared prefix).  A query column is one (member, query
 // head) pair; wave w owns columns 16w .. 16w + 15 of the block, the same
 // 16-column MFMA tile the partition kernel uses for one sequence's heads.
-// Per 16-token chunk the workgroup copies K and V once into LDS (double
-// buffered, one barrier per chunk); every wave reads its operands from LDS in
-// the lane layout of the partition kernel and runs the same score tile,
-// online softmax and P V tiles over all chunks of the partition.  Each wave
-// writes its columns' partials (running max, weight sum, unnormalised output)
-// into the split-K workspace at the members' own partition slots; the
-// partition kernel does the private partitions and the merge kernel combines
-// them all in partition order.
+// Per stage of two 16-token chunks the workgroup copies K and V once into LDS
+// (double buffered, one barrier per stage); every wave reads its operands
+// from LDS and runs the score tiles, one online-softmax step and the P V
+// products over all stages of the partition.  Each wave writes its columns'
+// partials (running max, weight sum, unnormalised output) into the split-K
+// workspace at the members' own partition slots; the partition kernel does
+// the private partitions and the merge kernel combines them all in partition
+// order.
+//
+// What bounds it (measured on MI355X with per-workgroup clocks): the
+// workgroups' compute per stage (score tiles, softmax, P V on the VALU and
+// MFMA of a SIMD shared by 2-3 waves) more than the wait for the next stage's
+// loads, plus the launch ramp of ~640 workgroups.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -33,6 +38,18 @@ constexpr int kSharedWaves = 4;
 constexpr int kColsPerWave = 16;
 constexpr int kColsPerBlock = kSharedWaves * kColsPerWave;
 
+// max over lanes l, l ^ 16 and l ^ 32 with the cross-lane swaps of the VALU
+// (v_permlane16_swap: rows 1 and 3 of the first operand trade places with
+// rows 0 and 2 of the second; v_permlane32_swap: the upper half of the first
+// with the lower half of the second).  Swapping x with itself leaves x[l] in
+// one result and x[l ^ 16] (x[l ^ 32]) in the other, in every lane.
+__device__ __forceinline__ float max_rows(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+}
+
 template <int KIND, int D, int BS>
 __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(CacheGeom geo,
                                                                              DecodeArgs a,
@@ -41,8 +58,24 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(Cac
   constexpr int NX = GG::NX, NN = GG::NN, TILE = GG::TILE, ELT = GG::ELT;
   constexpr int kThreads = kSharedWaves * kWave;
   constexpr int kUnits = D * ELT;  // 16-byte units of one chunk's K, and of its V
-  // two stage buffers of 2 chunks' K and V
-  __shared__ __align__(16) char lds[2 * 2 * 2 * kUnits * 16];
+  // Stages of STEP consecutive chunks move through LDS (double buffered).
+  // K keeps the tile layout, [D/VE pieces][16 rows][16 B] per chunk: the
+  // score operands of a wave are 1 KiB contiguous reads.  V is regrouped:
+  // record (token group j4, dim e) holds tokens 4*j4 .. 4*j4+3 of dim e of
+  // each of the stage's chunks, chunk after chunk, so that a lane's P V
+  // operand is one 16-byte read and the 16 lanes of a token group read 256
+  // contiguous bytes (no bank conflicts); the four token groups are padded
+  // apart by 128 bytes.  For bf16 the two chunks of a stage form one 32-token
+  // P V step of v_mfma_f32_16x16x32_bf16, token (chunk j, 4*j4+i) being k
+  // index 8*j4 + 4*j + i of both operands.
+  constexpr int STEP = 2;
+  constexpr int kStage = STEP * kUnits;  // 16-byte units of a stage's K (and of its V)
+  constexpr int kVRec = 4 * ELT * STEP;
+  constexpr int kVSeg = D * kVRec + 128;
+  constexpr int kKBytes = kStage * 16;
+  constexpr int kStageBuf = kKBytes + 4 * kVSeg;
+  static_assert(KIND != kBF16 || kVRec == 16, "a bf16 record is one 32-token operand");
+  __shared__ __align__(16) char lds[2 * kStageBuf];
 
   const int hkv = geo.num_kv_heads;
   int w = blockIdx.x;
@@ -90,74 +123,121 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(Cac
   const const_i32_ptr table = reinterpret_cast<const_i32_ptr>(
       reinterpret_cast<uintptr_t>(a.tables + static_cast<int64_t>(first) * a.table_stride));
 
-  // Stages of STEP consecutive chunks move through LDS.  Chunk j of a stage
-  // is K as [D/VE pieces][16 rows][16 B] and V as [D][16 tokens] -- the tile
-  // layouts of a 16-token block: unit uu < kUnits of a chunk's K is piece
-  // uu/16, row uu%16; of its V, dim uu/ELT, tokens (uu%ELT)*16/ELT on.  The
-  // next stage's loads are in flight while a stage is computed, and one
-  // barrier and one softmax step serve STEP chunks: a stage's critical path
-  // (LDS write, barrier, LDS read, the score tile, the max reduction, the P V
-  // tiles) is what bounds this kernel, not its memory traffic.
-  constexpr int STEP = 2;
-  constexpr int kStage = STEP * kUnits;  // 16-byte units of a stage's K (and of its V)
+  // Thread u of the workgroup moves units u, u + kThreads, ... of a stage:
+  // unit uu < kUnits of chunk j is K piece uu/16, row uu%16, and V dim uu/ELT,
+  // tokens (uu%ELT)*16/ELT on.  kUnits is a multiple of the wave, so a
+  // unit's chunk j is wave-uniform, and with blocks of at least a chunk its
+  // table entry is a scalar load.  The next stage's loads are in flight while
+  // a stage is computed; one barrier and one softmax step serve STEP chunks.
   constexpr int kPerS = (kStage + kThreads - 1) / kThreads;
-  constexpr int kStageBuf = 2 * kStage * 16;
-  static_assert(2 * kStageBuf <= static_cast<int>(sizeof(lds)), "LDS stage buffers");
+  static_assert(kUnits % kWave == 0, "a wave's units lie in one chunk");
+  // chunk of the stage that unit tid + k*kThreads belongs to
+  auto chunk_of = [&](int k) -> int {
+    if constexpr (kUnits % kThreads == 0) return (k * kThreads) / kUnits;
+    else return __builtin_amdgcn_readfirstlane((wave * kWave + k * kThreads) / kUnits);
+  };
+  // the lane's offsets of its units inside a (block, head) tile, for blocks
+  // of at least a chunk (the chunk's first row adds a wave-uniform part)
+  uint32_t ko[kPerS], vo[kPerS];
+#pragma unroll
+  for (int k = 0; k < kPerS; ++k) {
+    const int uu = tid + k * kThreads - chunk_of(k) * kUnits;
+    ko[k] = static_cast<uint32_t>(((uu / 16) * BS + uu % 16) * 16);
+    vo[k] = static_cast<uint32_t>(((uu / ELT) * BS + (uu % ELT) * (16 / ELT)) * ELT);
+  }
   uint4 sk[kPerS], sv[kPerS];
   // stage st of the partition: chunks cb + st*STEP + j, clamped into the
   // partition (the clamped copies are masked out below)
-  auto load_stage = [&](int st) {
+  auto load_stage = [&](int st, uint4 (&sk)[kPerS], uint4 (&sv)[kPerS]) {
+    if constexpr (BS >= kChunk) {
+      const char* kb[STEP];
+      const char* vb[STEP];
 #pragma unroll
-    for (int k = 0; k < kPerS; ++k) {
-      const int u = tid + k * kThreads;
-      if (kPerS * kThreads == kStage || u < kStage) {
-        const int uu = u % kUnits;
-        const int c = min(cb + st * STEP + u / kUnits, ce - 1);
-        const int t = c * kChunk + uu % 16;
-        const int tv = c * kChunk + (uu % ELT) * (16 / ELT);
-        int64_t bk, bv;
-        if constexpr (BS >= kChunk) {
-          bk = bv = static_cast<int64_t>(table[(c * kChunk) / BS]);
-        } else {
-          bk = static_cast<int64_t>(table[t / BS]);
-          bv = static_cast<int64_t>(table[tv / BS]);
+      for (int j = 0; j < STEP; ++j) {
+        const int c = min(cb + st * STEP + j, ce - 1);
+        const int64_t blk = table[__builtin_amdgcn_readfirstlane((c * kChunk) / BS)];
+        const int64_t tile = (blk * hkv + kvh) * TILE;
+        kb[j] = kl + tile + ((c * kChunk) % BS) * 16;
+        vb[j] = vl + tile + ((c * kChunk) % BS) * ELT;
+      }
+#pragma unroll
+      for (int k = 0; k < kPerS; ++k) {
+        if (kPerS * kThreads == kStage || tid + k * kThreads < kStage) {
+          const int j = chunk_of(k);
+          const char* kbj = kb[0];
+          const char* vbj = vb[0];
+#pragma unroll
+          for (int jj = 1; jj < STEP; ++jj) {
+            kbj = j == jj ? kb[jj] : kbj;
+            vbj = j == jj ? vb[jj] : vbj;
+          }
+          // a wave-uniform base plus a 32-bit lane offset (kept a 32-bit
+          // value by the empty asm): the loads take the scalar-base form
+          uint32_t ok = ko[k], ov = vo[k];
+          asm volatile("" : "+v"(ok), "+v"(ov));
+          sk[k] = ld16(kbj + ok);
+          sv[k] = ld16(vbj + ov);
         }
-        sk[k] = ld16(kl + (bk * hkv + kvh) * TILE + ((uu / 16) * BS + t % BS) * 16);
-        sv[k] = ld16(vl + (bv * hkv + kvh) * TILE + ((uu / ELT) * BS + tv % BS) * ELT);
+      }
+    } else {
+      // blocks shorter than a chunk: each unit finds its own block
+#pragma unroll
+      for (int k = 0; k < kPerS; ++k) {
+        const int u = tid + k * kThreads;
+        if (kPerS * kThreads == kStage || u < kStage) {
+          const int j = chunk_of(k);
+          const int uu = u - j * kUnits;
+          const int c = min(cb + st * STEP + j, ce - 1);
+          const int t = c * kChunk + uu % 16;
+          const int tv = c * kChunk + (uu % ELT) * (16 / ELT);
+          const int32_t* trow = a.tables + static_cast<int64_t>(first) * a.table_stride;
+          const int64_t bk = trow[t / BS], bv = trow[tv / BS];
+          sk[k] = ld16(kl + (bk * hkv + kvh) * TILE + ((uu / 16) * BS + t % BS) * 16);
+          sv[k] = ld16(vl + (bv * hkv + kvh) * TILE + ((uu / ELT) * BS + tv % BS) * ELT);
+        }
       }
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf, const uint4 (&sk)[kPerS], const uint4 (&sv)[kPerS]) {
     char* kd = lds + buf * kStageBuf;
-    char* vd = kd + kStage * 16;
+    char* vd = kd + kKBytes;
 #pragma unroll
     for (int k = 0; k < kPerS; ++k) {
       const int u = tid + k * kThreads;
       if (kPerS * kThreads == kStage || u < kStage) {
         *reinterpret_cast<uint4*>(kd + u * 16) = sk[k];
-        *reinterpret_cast<uint4*>(vd + u * 16) = sv[k];
+        const int j = chunk_of(k);
+        const int uu = u - j * kUnits;
+        const int e = uu / ELT, q = uu % ELT;
+        if constexpr (KIND == kBF16) {
+          // tokens 8q .. 8q+7: token groups 2q and 2q+1
+          *reinterpret_cast<uint2*>(vd + (2 * q) * kVSeg + e * kVRec + j * 8) = make_uint2(sv[k].x, sv[k].y);
+          *reinterpret_cast<uint2*>(vd + (2 * q + 1) * kVSeg + e * kVRec + j * 8) = make_uint2(sv[k].z, sv[k].w);
+        } else {
+          // tokens 4q .. 4q+3: token group q
+          *reinterpret_cast<uint4*>(vd + q * kVSeg + e * kVRec + j * 16) = sv[k];
+        }
       }
     }
   };
 
+  // acc[nb][i] = O[dim nb*16 + 4*j4 + i][column n]: the P V product is taken
+  // as V^T P^T, so a column's rescale factor is its own lane's
   float m = -INFINITY;
   float lsum = 0.0f;
   floatx4_t acc[NN];
 #pragma unroll
   for (int nb = 0; nb < NN; ++nb) acc[nb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // Two stages in flight: while stage st is computed from LDS buffer st % 2,
+  // stage st + 1 is loaded into registers; it goes to the other buffer after
+  // the compute.  (A third stage in flight, in a second register set, was
+  // measured slower: it costs occupancy and the wait is not the bound.)
   const int stages = (ce - cb + STEP - 1) / STEP;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int st = 0; st < stages; ++st) {
-    const int buf = st & 1;
-    // loads past the last stage re-read the partition's last chunk (an L2
-    // hit) rather than branch: a branch around loads makes the wait for them
-    // also wait for every newer load
-    load_stage(min(st + 1, stages - 1));
+  // one online-softmax step and the P V products of the stage in LDS buffer buf
+  auto compute = [&](int buf, int st) {
     const char* kd = lds + buf * kStageBuf;
-    const char* vd = kd + kStage * 16;
+    const char* vd = kd + kKBytes;
     // S[j][token 4*j4+i][column n]: the score tiles of the stage's chunks
     floatx4_t S[STEP];
 #pragma unroll
@@ -191,82 +271,90 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(Cac
         mx = fmaxf(mx, sc[j][i]);
       }
     }
-    mx = fmaxf(mx, xor16(mx));
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_rows(mx);
     const float mn = fmaxf(m, mx);
     const float alpha = fexp2(m - mn);
     m = mn;
     if (__any(alpha != 1.0f)) {
-      float ai[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * j4 + i);
 #pragma unroll
       for (int nb = 0; nb < NN; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[nb][i] *= ai[i];
+        for (int i = 0; i < 4; ++i) acc[nb][i] *= alpha;
     }
+    float p[STEP][4];
+#pragma unroll
+    for (int j = 0; j < STEP; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[j][i] = fexp2(sc[j][i] - mn);
     float part_sum = 0.0f;
+    if constexpr (KIND == kBF16) {
+      // weight = high + low, both bf16; the sum is what the MFMA multiplies
+      uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int j = 0; j < STEP; ++j) {
-      float p[4];
+      for (int j = 0; j < STEP; ++j) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = fexp2(sc[j][i] - mn);
-      const char* vj = vd + j * kUnits * 16;
-      if constexpr (KIND == kBF16) {
-        const uint32_t hi01 = pack_bf16(p[0], p[1]), hi23 = pack_bf16(p[2], p[3]);
-        const float h0f = bf16_lo(hi01), h1f = bf16_hi(hi01), h2f = bf16_lo(hi23), h3f = bf16_hi(hi23);
-        const uint32_t lo01 = pack_bf16(p[0] - h0f, p[1] - h1f), lo23 = pack_bf16(p[2] - h2f, p[3] - h3f);
-        part_sum += ((h0f + bf16_lo(lo01)) + (h1f + bf16_hi(lo01))) +
-                    ((h2f + bf16_lo(lo23)) + (h3f + bf16_hi(lo23)));
-        const short4_t phi = __builtin_bit_cast(short4_t, make_uint2(hi01, hi23));
-        const short4_t plo = __builtin_bit_cast(short4_t, make_uint2(lo01, lo23));
-#pragma unroll
-        for (int nb = 0; nb < NN; ++nb) {
-          const uint2 vop = *reinterpret_cast<const uint2*>(vj + ((nb * 16 + n) * 16 + 4 * j4) * ELT);
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, __builtin_bit_cast(short4_t, vop),
-                                                             acc[nb], 0, 0, 0);
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, __builtin_bit_cast(short4_t, vop),
-                                                             acc[nb], 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+          const float a0 = p[j][2 * h], a1 = p[j][2 * h + 1];
+          const uint32_t wh = pack_bf16(a0, a1);
+          const float h0 = bf16_lo(wh), h1 = bf16_hi(wh);
+          const uint32_t wl = pack_bf16(a0 - h0, a1 - h1);
+          part_sum += (h0 + bf16_lo(wl)) + (h1 + bf16_hi(wl));
+          hi[2 * j + h] = wh;
+          lo[2 * j + h] = wl;
         }
-      } else {
-        part_sum += (p[0] + p[1]) + (p[2] + p[3]);
+      }
+      const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+      const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+      for (int nb = 0; nb < NN; ++nb) {
+        const uint4 vop = *reinterpret_cast<const uint4*>(vd + j4 * kVSeg + (nb * 16 + n) * kVRec);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vop), phi, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vop), plo, acc[nb], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < STEP; ++j) {
+        part_sum += (p[j][0] + p[j][1]) + (p[j][2] + p[j][3]);
 #pragma unroll
         for (int nb = 0; nb < NN; ++nb) {
-          const uint4 vop = *reinterpret_cast<const uint4*>(vj + ((nb * 16 + n) * 16 + 4 * j4) * ELT);
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[0], __uint_as_float(vop.x), acc[nb], 0, 0, 0);
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[1], __uint_as_float(vop.y), acc[nb], 0, 0, 0);
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[2], __uint_as_float(vop.z), acc[nb], 0, 0, 0);
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[3], __uint_as_float(vop.w), acc[nb], 0, 0, 0);
+          const uint4 vop = *reinterpret_cast<const uint4*>(vd + j4 * kVSeg + (nb * 16 + n) * kVRec + j * 16);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vop.x), p[j][0], acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vop.y), p[j][1], acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vop.z), p[j][2], acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vop.w), p[j][3], acc[nb], 0, 0, 0);
         }
       }
     }
     lsum = lsum * alpha + part_sum;
-    store_stage(buf ^ 1);
+  };
+  load_stage(0, sk, sv);
+  store_stage(0, sk, sv);
+  __syncthreads();
+  for (int st = 0; st < stages; ++st) {
+    // loads past the last stage re-read the partition's last chunk (an L2
+    // hit) rather than branch: a branch around loads makes the wait for them
+    // also wait for every newer load
+    load_stage(min(st + 1, stages - 1), sk, sv);
+    compute(st & 1, st);
+    store_stage((st & 1) ^ 1, sk, sv);
     __syncthreads();
   }
 
   // partials of this wave's columns at the members' partition slot `part`
   lsum += xor16(lsum);
   lsum += xor32(lsum);
-  const int P = a.num_partitions;
-  float* acc_ws = a.ws + static_cast<int64_t>(a.num_seqs) * a.num_q_heads * P * 2;
-  auto prow = [&](int col) -> int64_t {
-    const int64_t row = static_cast<int64_t>(first + col / G) * a.num_q_heads + kvh * G + col % G;
-    return row * P + part;
-  };
-  if (j4 == 0 && col0 + n < ncols) {
-    const int64_t r = prow(col0 + n);
-    a.ws[r * 2] = m;
-    a.ws[r * 2 + 1] = lsum;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int col = col0 + 4 * j4 + i;
-    if (col < ncols) {
-      const int64_t r = prow(col);
-#pragma unroll
-      for (int nb = 0; nb < NN; ++nb) acc_ws[r * D + nb * 16 + n] = acc[nb][i];
+  if (col0 + n < ncols) {
+    const int P = a.num_partitions;
+    const int col = col0 + n;
+    const int64_t r = (static_cast<int64_t>(first + col / G) * a.num_q_heads + kvh * G + col % G) * P + part;
+    if (j4 == 0) {
+      a.ws[r * 2] = m;
+      a.ws[r * 2 + 1] = lsum;
     }
+    float* o = a.ws + static_cast<int64_t>(a.num_seqs) * a.num_q_heads * P * 2 + r * D + 4 * j4;
+#pragma unroll
+    for (int nb = 0; nb < NN; ++nb)
+      *reinterpret_cast<float4*>(o + nb * 16) = make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
   }
 }
 

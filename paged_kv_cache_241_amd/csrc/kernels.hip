@@ -50,7 +50,7 @@
 namespace pa {
 namespace {
 
-constexpr int kMergeThreads = 64;
+constexpr int kMergeWaves = 4;   // merge rows per workgroup, one a wave
 constexpr int kMaxGroup = 16;     // query heads per KV head the tile can hold
 constexpr int kMaxMergeLds = 64 * 1024;
 
@@ -451,33 +451,63 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
   }
 }
 
-// Merge context partitions in partition order: one workgroup per (seq, q head).
+// Merge context partitions in partition order: one wave per (seq, q head),
+// kMergeWaves rows per workgroup.  Lane l holds the running max and weight sum
+// of partition p0 + l (64 partitions a round) and D / 64 output dims; a row's
+// loads are all issued before its arithmetic.  The sums run over p in order,
+// as fma(w_p, acc_p, .) and fma(w_p, l_p, .).
 template <int D>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
-  const int sh = blockIdx.x;
-  const int s = sh / a.num_q_heads;
+__global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int E = D / kWave;
+  static_assert(E * kWave == D, "D is a multiple of the wave");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+  const int64_t sh = static_cast<int64_t>(blockIdx.x) * kMergeWaves +
+                     __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (sh >= rows) return;
+  const int s = static_cast<int>(sh / a.num_q_heads);
   const int P = a.num_partitions;
   const int L = a.lens[s];
   const int tp = a.partition_chunks * kChunk;
   const int ps = (L + tp - 1) / tp;
-  const float* ml = a.ws + static_cast<int64_t>(sh) * P * 2;
-  const float* accp = a.ws + static_cast<int64_t>(a.num_seqs) * a.num_q_heads * P * 2 +
-                      static_cast<int64_t>(sh) * P * D;
-  float* o = a.out + static_cast<int64_t>(sh) * D;
-  if (ps == 0) {
-    for (int e = threadIdx.x; e < D; e += kMergeThreads) o[e] = 0.0f;
-    return;
-  }
-  float mx = ml[0];
-  for (int p = 1; p < ps; ++p) mx = fmaxf(mx, ml[2 * p]);
-  for (int e = threadIdx.x; e < D; e += kMergeThreads) {
-    float A = 0.0f, Lt = 0.0f;
-    for (int p = 0; p < ps; ++p) {
-      const float wt = fexp2(ml[2 * p] - mx);
-      A = fmaf(wt, accp[p * D + e], A);
-      Lt = fmaf(wt, ml[2 * p + 1], Lt);
+  const float* ml = a.ws + sh * P * 2;
+  const float* accp = a.ws + rows * P * 2 + sh * P * D + lane * E;
+  float* o = a.out + sh * D + lane * E;
+  float A[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) A[e] = 0.0f;
+  if (ps > 0) {
+    float mx = -INFINITY;
+    for (int p0 = 0; p0 < ps; p0 += kWave)
+      if (p0 + lane < ps) mx = fmaxf(mx, ml[2 * (p0 + lane)]);
+#pragma unroll
+    for (int x = kWave / 2; x >= 1; x /= 2) mx = fmaxf(mx, __shfl_xor(mx, x));
+    float Lt = 0.0f;
+    for (int p0 = 0; p0 < ps; p0 += kWave) {
+      float wl = 0.0f, ll = 0.0f;
+      if (p0 + lane < ps) {
+        wl = fexp2(ml[2 * (p0 + lane)] - mx);
+        ll = ml[2 * (p0 + lane) + 1];
+      }
+      const int n = min(kWave, ps - p0);
+      const float* ap = accp + static_cast<int64_t>(p0) * D;
+#pragma unroll 8
+      for (int k = 0; k < n; ++k) {
+        const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
+        const float lk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ll), k));
+#pragma unroll
+        for (int e = 0; e < E; ++e) A[e] = fmaf(wt, ap[k * D + e], A[e]);
+        Lt = fmaf(wt, lk, Lt);
+      }
     }
-    o[e] = A / Lt;
+#pragma unroll
+    for (int e = 0; e < E; ++e) A[e] = A[e] / Lt;
+  }
+  if constexpr (E == 2) {
+    *reinterpret_cast<float2*>(o) = make_float2(A[0], A[1]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = A[e];
   }
 }
 
@@ -553,10 +583,14 @@ hipError_t launch_decode_w(const CacheGeom& g, const DecodeArgs& a, hipStream_t 
   else
     hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, false>), dim3(static_cast<uint32_t>(nwork)),
                        dim3(W * kWave), merge_lds_bytes(W, G, D), st, g, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_partitions == 1) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(static_cast<uint32_t>(a.num_seqs) * a.num_q_heads),
-                     dim3(kMergeThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_merge_d(const DecodeArgs& a, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(static_cast<uint32_t>((rows + kMergeWaves - 1) / kMergeWaves)),
+                     dim3(kMergeWaves * kWave), 0, st, a);
   return hipGetLastError();
 }
 
@@ -602,16 +636,18 @@ hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool
                          hipStream_t stream) {
   *supported = true;
   if (a.num_seqs <= 0) return hipSuccess;
-  if (a.num_q_heads / g.num_kv_heads > kMaxGroup) {
+  if (a.num_q_heads / g.num_kv_heads > kMaxGroup || (g.head_dim != 128 && g.head_dim != 64)) {
     *supported = false;
     return hipSuccess;
   }
-  if (kind == kBF16 && g.head_dim == 128) return launch_decode_bs<kBF16, 128>(g, a, supported, stream);
-  if (kind == kBF16 && g.head_dim == 64) return launch_decode_bs<kBF16, 64>(g, a, supported, stream);
-  if (kind == kF32 && g.head_dim == 128) return launch_decode_bs<kF32, 128>(g, a, supported, stream);
-  if (kind == kF32 && g.head_dim == 64) return launch_decode_bs<kF32, 64>(g, a, supported, stream);
-  *supported = false;
-  return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (kind == kBF16 && g.head_dim == 128) e = launch_decode_bs<kBF16, 128>(g, a, supported, stream);
+  else if (kind == kBF16 && g.head_dim == 64) e = launch_decode_bs<kBF16, 64>(g, a, supported, stream);
+  else if (kind == kF32 && g.head_dim == 128) e = launch_decode_bs<kF32, 128>(g, a, supported, stream);
+  else if (kind == kF32 && g.head_dim == 64) e = launch_decode_bs<kF32, 64>(g, a, supported, stream);
+  else *supported = false;
+  if (!*supported || e != hipSuccess || a.num_partitions == 1) return e;
+  return g.head_dim == 128 ? launch_merge_d<128>(a, stream) : launch_merge_d<64>(a, stream);
 }
 
 }  // namespace pa

@@ -79,14 +79,16 @@ struct SharedArgs {
   int32_t shared_parts = 0;          // partitions of the longest shared prefix
 };
 
-// Returns hipErrorInvalidValue-free codes from the launch; *supported is set
-// to false (and nothing is launched) when no kernel exists for the shape.
+// The partition kernel and, with several partitions, the merge.  *supported
+// is set to false (and nothing is launched) when no kernel exists for the
+// shape.
 hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool* supported,
                          hipStream_t stream);
 
 // The shared-prefix pass: partials of every group's shared partitions, for
 // all its members' query heads (a.seq_shared and the split-K workspace are
-// set; launch_decode afterwards does the private partitions and the merge).
+// set; launch_decode does the private partitions and the merge, which must
+// follow this pass).
 hipError_t launch_decode_shared(const CacheGeom& g, int kind, const DecodeArgs& a,
                                 const SharedArgs& sh, bool* supported, hipStream_t stream);
 
