@@ -81,26 +81,33 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
   const int P = a.num_partitions;
   const int hkv = geo.num_kv_heads;
   const int G = a.num_q_heads / hkv;
+  // Work items are (r, sequence, KV head) with r the partition's place
+  // counted from the end of its context (r = 0: the last partition, the
+  // only one that may be partly filled), r-major and r descending: full
+  // partitions are dispatched first and each context's last, shorter one
+  // last, so the launch ends on short workgroups.  Items past a context's
+  // first partition have nothing to do.
   const int work = work_item(blockIdx.x, gridDim.x, !NT);
-  const int part = work % P;
-  const int sk = work / P;
-  const int kvh = sk % hkv;
-  const int s = sk / hkv;
+  const int pairs = a.num_seqs * hkv;
+  const int r = P - 1 - work / pairs;
+  const int kvh = (work % pairs) % hkv;
+  const int s = (work % pairs) / hkv;
   const int tid = threadIdx.x;
   const int h0 = kvh * G;
 
   const int L = a.lens[s];
   const int nch = (L + kChunk - 1) / kChunk;
-  const int cb = part * a.partition_chunks;
-  const int ce = min(nch, cb + a.partition_chunks);
-  if (a.seq_shared != nullptr && cb * kChunk < a.seq_shared[s]) return;  // the shared pass's
-  if (cb >= ce) {
+  const int part = (nch + a.partition_chunks - 1) / a.partition_chunks - 1 - r;
+  if (part < 0) {
     if (P == 1) {  // empty context: zero output
       float* o = a.out + (static_cast<int64_t>(s) * a.num_q_heads + h0) * D;
       for (int e = tid; e < G * D; e += kThreads) o[e] = 0.0f;
     }
     return;
   }
+  const int cb = part * a.partition_chunks;
+  const int ce = min(nch, cb + a.partition_chunks);
+  if (a.seq_shared != nullptr && cb * kChunk < a.seq_shared[s]) return;  // the shared pass's
 
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -117,12 +124,17 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
   // copy in LDS and stores the row into the cache after its loop.  (Narrow
   // row stores at the end cost less than writing the whole chunk back from
   // the operand registers, whose writes would interleave with the reads.)
+  // The row and the slot are loaded whatever the slot says: only their use
+  // waits for the slot (a slot < 0 appends nothing and the cache is read as
+  // it is), so no load of the workgroup's start waits on another.
   constexpr int kRowVec = D * ELT / 16;  // 16-byte pieces of one row
   __shared__ uint4 sm_new[2 * kRowVec];  // K pieces, then V pieces
-  const bool own_new = a.new_k != nullptr && wave == 0 && ce == nch && a.new_slots[s] >= 0;
+  const bool last_new = a.new_k != nullptr && wave == 0 && ce == nch;
+  int slot_new = -1;
   uint4 nk[NX];      // lane (n, j4): K pieces x*4+j4 of the new row
   uint32_t nv[NN];   // lane (n, j4): V element nb*16+n of the new row
-  if (own_new) {
+  if (last_new) {
+    slot_new = a.new_slots[s];
     const int64_t src = (static_cast<int64_t>(s) * hkv + kvh) * D * ELT;
     const char* nk_row = static_cast<const char*>(a.new_k) + src;
     const char* nv_row = static_cast<const char*>(a.new_v) + src;
@@ -134,6 +146,8 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
       else nv[nb] = *reinterpret_cast<const uint32_t*>(nv_row + (nb * 16 + n) * 4);
     }
   }
+  // evaluated where it is used, so that only those uses wait for the slot
+  auto own_new = [&]() -> bool { return last_new && slot_new >= 0; };
 
   // q operand: head n of the group, zero beyond G (the row address is
   // clamped to a head of this group so that it always exists)
@@ -370,7 +384,7 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
     const int64_t u = u_next;
     if constexpr (BS >= kChunk) u_next = block_of_chunk(max(c - kWaves, cb));
     load(c, u, kbuf, vbuf);
-    if (own_new) patch_new(c, kbuf, vbuf);
+    if (own_new()) patch_new(c, kbuf, vbuf);
     process(std::true_type{}, c, kbuf, vbuf);
     c -= kWaves;
   }
@@ -427,9 +441,9 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
   }
   // the appended row into the cache: K as 16-byte pieces, V element by
   // element ([D][BS] tiles)
-  if (own_new && lane < kRowVec) {
+  if (own_new() && lane < kRowVec) {
     constexpr int VE = GG::VE;
-    const int slot = a.new_slots[s];
+    const int slot = slot_new;
     const int q = lane;
     const int64_t u = slot / BS;
     const int o = slot % BS;
