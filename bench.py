@@ -279,8 +279,8 @@ class Bench:
         if shared_tokens:
             separate_append = True
             self.pt = shared_tokens
-            parts = max(2, -(-self.cfg.max_seq_len // shared_tokens))
-            need = b * self.cfg.num_q_heads * parts * (self.cfg.head_dim + 2) * 4
+            need = self.pool.workspace_bytes(b, self.cfg.num_q_heads,
+                                             max(self.cfg.max_seq_len, shared_tokens + 1), shared_tokens)
             self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
             self.sh_seq = torch.zeros(b, dtype=torch.int32, device=dev)
             self.sh_groups = torch.zeros((b, 2), dtype=torch.int32, device=dev)

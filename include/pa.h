@@ -351,7 +351,10 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int32_t num_seqs, int32_t 
  *   max_context:    bound on the lengths; sizes the launch.
  *   d_out:          device fp32 [num_seqs][num_q_heads][head_dim].
  *   d_workspace:    device scratch of >= pa_decode_workspace_bytes(...) bytes
- *                   (may be NULL when that is 0).
+ *                   (may be NULL when that is 0): the partitions' partial
+ *                   results and, before them in time, the launch's work plan
+ *                   (which partitions hold tokens, longest first); written
+ *                   and read within the call.
  *   partition_tokens: context tokens per workgroup, 0 = the library's choice,
  *                   else a multiple of 16 and of block_size; contexts longer
  *                   than one partition are split and merged (split-K).

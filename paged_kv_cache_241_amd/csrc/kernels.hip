@@ -81,30 +81,41 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
   const int P = a.num_partitions;
   const int hkv = geo.num_kv_heads;
   const int G = a.num_q_heads / hkv;
-  // Work items are (r, sequence, KV head) with r the partition's place
-  // counted from the end of its context (r = 0: the last partition, the
-  // only one that may be partly filled), r-major and r descending: full
-  // partitions are dispatched first and each context's last, shorter one
-  // last, so the launch ends on short workgroups.  Items past a context's
-  // first partition have nothing to do.
-  const int work = work_item(blockIdx.x, gridDim.x, !NT);
-  const int pairs = a.num_seqs * hkv;
-  const int r = P - 1 - work / pairs;
-  const int kvh = (work % pairs) % hkv;
-  const int s = (work % pairs) / hkv;
+  // With a plan (split contexts), workgroup i takes the KV head i % hkv of
+  // plan item i / hkv; the items with work fill the front of the grid,
+  // longest first, and the grid's tail exits at once.  Without one (one
+  // partition per context), work items are (r, sequence, KV head) with r a
+  // partition's place counted from the end of its context, r-major and
+  // descending; with one partition that is each context's only one.
   const int tid = threadIdx.x;
-  const int h0 = kvh * G;
-
-  const int L = a.lens[s];
-  const int nch = (L + kChunk - 1) / kChunk;
-  const int part = (nch + a.partition_chunks - 1) / a.partition_chunks - 1 - r;
-  if (part < 0) {
-    if (P == 1) {  // empty context: zero output
-      float* o = a.out + (static_cast<int64_t>(s) * a.num_q_heads + h0) * D;
-      for (int e = tid; e < G * D; e += kThreads) o[e] = 0.0f;
+  int s, kvh, part, L;
+  if (a.plan != nullptr) {
+    const int2 it = a.plan[blockIdx.x / hkv];
+    if (it.x < 0) return;
+    s = it.x / P;
+    part = it.x % P;
+    kvh = blockIdx.x % hkv;
+    L = it.y;
+  } else {
+    const int work = work_item(blockIdx.x, gridDim.x, !NT);
+    const int pairs = a.num_seqs * hkv;
+    const int r = P - 1 - work / pairs;
+    kvh = (work % pairs) % hkv;
+    s = (work % pairs) / hkv;
+    L = a.lens[s];
+    // partitions holding tokens (at most P: contexts are at most max_context)
+    const int np = min((L + a.partition_chunks * kChunk - 1) / (a.partition_chunks * kChunk), P);
+    part = np - 1 - r;
+    if (part < 0) {
+      if (P == 1) {  // empty context: zero output
+        float* o = a.out + (static_cast<int64_t>(s) * a.num_q_heads + kvh * G) * D;
+        for (int e = tid; e < G * D; e += kThreads) o[e] = 0.0f;
+      }
+      return;
     }
-    return;
   }
+  const int h0 = kvh * G;
+  const int nch = (L + kChunk - 1) / kChunk;
   const int cb = part * a.partition_chunks;
   const int ce = min(nch, cb + a.partition_chunks);
   if (a.seq_shared != nullptr && cb * kChunk < a.seq_shared[s]) return;  // the shared pass's
@@ -465,6 +476,96 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
   }
 }
 
+// Work plan of a launch split into partitions: plan[i] = {s * P + part, L_s}
+// for the i-th (sequence, partition) with tokens to attend, {-1, 0} past the
+// last.  Full partitions come first (in sequence order for up to 1024
+// sequences), then every context's last partition, longest first
+// (kPlanBuckets length classes; the order within a class varies between
+// runs, which changes no result: each partition is computed on its own and
+// merged in partition order).  Shared
+// prefixes (seq_shared) are left out.  The partition kernel's grid then ends
+// on its shortest workgroups, and the items without work (contexts shorter
+// than the longest) come after all others instead of among them.  One
+// workgroup.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 64;  // one per lane of a wave
+constexpr int kPlanKeep = 4;      // sequences per thread kept in registers
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a, int2* __restrict__ plan) {
+  static_assert(kPlanBuckets == kWave, "one length class per lane");
+  __shared__ int hist[kPlanBuckets];
+  __shared__ int cursor[kPlanBuckets];
+  __shared__ int wsum[kPlanThreads / kWave];
+  __shared__ int total;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int B = a.num_seqs, P = a.num_partitions, pc = a.partition_chunks;
+  // sequence s: L, partitions [first, np) hold its unshared tokens, the last
+  // one has `last` chunks
+  struct Span { int L, first, np, last; };
+  auto span = [&](int s) -> Span {
+    Span r;
+    r.L = a.lens[s];
+    const int nch = (r.L + kChunk - 1) / kChunk;
+    r.np = min((nch + pc - 1) / pc, P);
+    r.first = a.seq_shared != nullptr ? min(a.seq_shared[s] / (pc * kChunk), r.np) : 0;
+    r.last = r.np > 0 ? min(nch - (r.np - 1) * pc, pc) : 0;
+    return r;
+  };
+  // length class, 0 for the longest last partitions
+  auto bucket = [&](int last) { return kPlanBuckets - 1 - ((last - 1) * kPlanBuckets) / pc; };
+  if (tid < kPlanBuckets) hist[tid] = 0;
+  Span keep[kPlanKeep];
+#pragma unroll
+  for (int k = 0; k < kPlanKeep; ++k)
+    keep[k] = tid + k * kPlanThreads < B ? span(tid + k * kPlanThreads) : Span{0, 0, 0, 0};
+  __syncthreads();
+  int mine = 0;  // full partitions of this thread's sequences
+  auto count = [&](const Span& r) {
+    if (r.np > r.first) {
+      mine += r.np - 1 - r.first;
+      atomicAdd(&hist[bucket(r.last)], 1);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kPlanKeep; ++k) count(keep[k]);
+  for (int s = tid + kPlanKeep * kPlanThreads; s < B; s += kPlanThreads) count(span(s));
+  const int x = wave_incl_scan(mine, lane);
+  if (lane == kWave - 1) wsum[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    // offsets of the waves' full partitions, then of the length classes
+    // after all full partitions, longest class first
+    const int v = wave_incl_scan(lane < kPlanThreads / kWave ? wsum[lane] : 0, lane);
+    if (lane < kPlanThreads / kWave) wsum[lane] = v;
+    const int full = __shfl(v, kPlanThreads / kWave - 1);
+    const int h = hist[lane];
+    const int hs = wave_incl_scan(h, lane);
+    cursor[lane] = full + hs - h;
+    if (lane == kWave - 1) total = full + hs;
+  }
+  __syncthreads();
+  int pos = (wave > 0 ? wsum[wave - 1] : 0) + x - mine;
+  auto place = [&](int s, const Span& r) {
+    for (int p = r.first; p < r.np - 1; ++p) plan[pos++] = make_int2(s * P + p, r.L);
+    if (r.np > r.first) plan[atomicAdd(&cursor[bucket(r.last)], 1)] = make_int2(s * P + r.np - 1, r.L);
+  };
+#pragma unroll
+  for (int k = 0; k < kPlanKeep; ++k)
+    if (tid + k * kPlanThreads < B) place(tid + k * kPlanThreads, keep[k]);
+  for (int s = tid + kPlanKeep * kPlanThreads; s < B; s += kPlanThreads) place(s, span(s));
+  for (int i = total + tid; i < B * P; i += kPlanThreads) plan[i] = make_int2(-1, 0);
+}
+
 // Merge context partitions in partition order: one wave per (seq, q head),
 // kMergeWaves rows per workgroup.  Lane l holds the running max and weight sum
 // of partition p0 + l (64 partitions a round) and D / 64 output dims; a row's
@@ -483,7 +584,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(Decod
   const int P = a.num_partitions;
   const int L = a.lens[s];
   const int tp = a.partition_chunks * kChunk;
-  const int ps = (L + tp - 1) / tp;
+  const int ps = min((L + tp - 1) / tp, P);
   const float* ml = a.ws + sh * P * 2;
   const float* accp = a.ws + rows * P * 2 + sh * P * D + lane * E;
   float* o = a.out + sh * D + lane * E;
@@ -654,11 +755,24 @@ hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool
     *supported = false;
     return hipSuccess;
   }
+  DecodeArgs ap = a;
+  // Split launches run from a plan (decode_plan_kernel), except after a
+  // shared-prefix pass: there every context has one private partition left,
+  // and the plan's launch costs more (measured) than the skipped partitions.
+  if (a.num_partitions > 1 && a.seq_shared == nullptr) {
+    // the plan follows the partials in the workspace
+    int2* plan = reinterpret_cast<int2*>(a.ws + static_cast<int64_t>(a.num_seqs) * a.num_q_heads *
+                                                    a.num_partitions * (g.head_dim + 2));
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, plan);
+    hipError_t ep = hipGetLastError();
+    if (ep != hipSuccess) return ep;
+    ap.plan = plan;
+  }
   hipError_t e = hipSuccess;
-  if (kind == kBF16 && g.head_dim == 128) e = launch_decode_bs<kBF16, 128>(g, a, supported, stream);
-  else if (kind == kBF16 && g.head_dim == 64) e = launch_decode_bs<kBF16, 64>(g, a, supported, stream);
-  else if (kind == kF32 && g.head_dim == 128) e = launch_decode_bs<kF32, 128>(g, a, supported, stream);
-  else if (kind == kF32 && g.head_dim == 64) e = launch_decode_bs<kF32, 64>(g, a, supported, stream);
+  if (kind == kBF16 && g.head_dim == 128) e = launch_decode_bs<kBF16, 128>(g, ap, supported, stream);
+  else if (kind == kBF16 && g.head_dim == 64) e = launch_decode_bs<kBF16, 64>(g, ap, supported, stream);
+  else if (kind == kF32 && g.head_dim == 128) e = launch_decode_bs<kF32, 128>(g, ap, supported, stream);
+  else if (kind == kF32 && g.head_dim == 64) e = launch_decode_bs<kF32, 64>(g, ap, supported, stream);
   else *supported = false;
   if (!*supported || e != hipSuccess || a.num_partitions == 1) return e;
   return g.head_dim == 128 ? launch_merge_d<128>(a, stream) : launch_merge_d<64>(a, stream);

@@ -67,6 +67,10 @@ struct DecodeArgs {
   // partitions) are attended by decode_shared_kernel; the partition kernel
   // skips them.  Null: none.
   const int32_t* seq_shared = nullptr;
+  // work plan of a split launch (decode_plan_kernel's output in the
+  // workspace): item i = {s * num_partitions + partition, L_s}, {-1, 0} past
+  // the last.  Null: the grid enumerates every (partition, sequence, head).
+  const int2* plan = nullptr;
 };
 
 // Groups of sequences whose contexts start with the same blocks
@@ -92,12 +96,14 @@ hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool
 hipError_t launch_decode_shared(const CacheGeom& g, int kind, const DecodeArgs& a,
                                 const SharedArgs& sh, bool* supported, hipStream_t stream);
 
-// Bytes of decode partials for these sizes.
+// Bytes of decode partials for these sizes, then the work plan (one int2
+// per (sequence, partition)).
 inline size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                      int32_t num_partitions) {
   if (num_partitions <= 1) return 0;
   return static_cast<size_t>(num_seqs) * num_q_heads * num_partitions *
-         (static_cast<size_t>(head_dim) + 2) * sizeof(float);
+             (static_cast<size_t>(head_dim) + 2) * sizeof(float) +
+         static_cast<size_t>(num_seqs) * num_partitions * 2 * sizeof(int32_t);
 }
 
 }  // namespace pa

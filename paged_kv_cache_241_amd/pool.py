@@ -222,8 +222,9 @@ class Pool:
         if out is None:
             out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
         if workspace is None:
-            parts = max(2, -(-int(max_context) // int(partition_tokens)))
-            need = b * hq * parts * (self.head_dim + 2) * 4
+            # at least two partitions: the shared pass always writes partials
+            need = self.workspace_bytes(b, hq, max(int(max_context), int(partition_tokens) + 1),
+                                        partition_tokens)
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         capi.check(self.lib.pa_decode_shared(
             self.handle, layer, q.data_ptr(), _DTYPES[self.kv_dtype], hq, float(scale),

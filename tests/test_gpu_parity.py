@@ -267,6 +267,54 @@ def test_partitions_change_only_rounding():
         assert row_rel_err(to_f64(c32.decode(partition_tokens=pt)), one) <= 1e-6
 
 
+def test_split_plan_lists_every_partition_once_longest_last_ones_first():
+    # White-box look at the work plan that split launches keep in the
+    # workspace after the partials: item {s * P + part, L_s} per partition
+    # with tokens, full partitions first (in sequence order for batches of up
+    # to 1024), then each
+    # context's last partition from the longest down (64 length classes),
+    # then {-1, 0}.
+    cfg = W.get(3, batch=40)
+    case = Case(cfg)
+    lens = case.lens.clone()
+    lens[3] = 0
+    lens[7] = 1
+    pt = 128
+    b, hq, d = cfg.batch, cfg.num_q_heads, cfg.head_dim
+    P = -(-case.max_context // pt)
+    need = case.pool.workspace_bytes(b, hq, case.max_context, pt)
+    partial_bytes = b * hq * P * (d + 2) * 4
+    assert need == partial_bytes + b * P * 8
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    out = case.pool.decode(0, case.vals[0][0], case.scale, case.tables, lens, case.max_context,
+                           partition_tokens=pt, workspace=ws)
+    torch.cuda.synchronize()
+    plan = ws[partial_bytes:].view(torch.int32).view(-1, 2).cpu().numpy()
+    L = lens.cpu().numpy()
+    nparts = [-(-int(x) // pt) for x in L]
+    expected = {s * P + p for s in range(b) for p in range(nparts[s])}
+    n = len(expected)
+    assert (plan[n:] == [-1, 0]).all()
+    items = plan[:n]
+    assert set(items[:, 0].tolist()) == expected and len(set(items[:, 0].tolist())) == n
+    assert all(int(L[it // P]) == ln for it, ln in items.tolist())
+    full = sum(max(k - 1, 0) for k in nparts)
+    heads = [(it // P, it % P) for it in items[:full, 0].tolist()]
+    assert heads == sorted(heads) and all(p < nparts[s] - 1 for s, p in heads)
+    pc = pt // 16
+
+    def cls(s):
+        last = -(-int(L[s]) // 16) - (nparts[s] - 1) * pc
+        return ((last - 1) * 64) // pc
+
+    lasts = [cls(it // P) for it in items[full:, 0].tolist()]
+    assert all(it % P == nparts[it // P] - 1 for it in items[full:, 0].tolist())
+    assert lasts == sorted(lasts, reverse=True)
+    ref = case.decode(partition_tokens=pt)
+    keep = [s for s in range(b) if L[s] == int(case.lens[s])]
+    assert torch.equal(out[keep], ref[keep])
+
+
 def test_empty_context_gives_zeros_and_others_unchanged():
     cfg = W.get(2, batch=4, num_blocks=300)
     case = Case(cfg)
