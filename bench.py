@@ -426,7 +426,7 @@ def measured_traffic(workload: str):
 
 
 # the sources the decode partition kernel is compiled from
-KERNEL_SOURCES = ("kernels.hip", "decode_common.hpp", "kernels.hpp")
+KERNEL_SOURCES = ("kernels.hip", "decode_partition.hpp", "decode_common.hpp", "kernels.hpp")
 
 
 def kernel_source_digest() -> str:

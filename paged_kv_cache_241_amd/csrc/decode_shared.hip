@@ -24,11 +24,13 @@
 // loads, plus the launch ramp of ~640 workgroups.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
 
 #include "decode_common.hpp"
+#include "decode_partition.hpp"
 #include "kernels.hpp"
 
 namespace pa {
@@ -50,10 +52,21 @@ __device__ __forceinline__ float max_rows(float x) {
   return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
 }
 
+// Chunks per stage of the shared pass: two for bf16 (one 32-token P V step),
+// one for fp32 (which keeps the two stage buffers within 64 KiB).
+template <int KIND>
+constexpr int shared_step() { return KIND == kBF16 ? 2 : 1; }
+// LDS bytes of the shared pass: two stage buffers (see below)
+template <int KIND, int D>
+constexpr int shared_lds_bytes() {
+  constexpr int ELT = KIND == kBF16 ? 2 : 4, STEP = shared_step<KIND>();
+  return 2 * (STEP * D * ELT * 16 + 4 * (D * 4 * ELT * STEP + 128));
+}
+
+// The shared pass of workgroup w, with `lds` shared_lds_bytes() of LDS.
 template <int KIND, int D, int BS>
-__global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(CacheGeom geo,
-                                                                             DecodeArgs a,
-                                                                             SharedArgs g) {
+__device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeArgs& a, const SharedArgs& g,
+                                            int w, char* lds) {
   using GG = Geo<KIND, D, BS>;
   constexpr int NX = GG::NX, NN = GG::NN, TILE = GG::TILE, ELT = GG::ELT;
   constexpr int kThreads = kSharedWaves * kWave;
@@ -68,17 +81,16 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(Cac
   // apart by 128 bytes.  For bf16 the two chunks of a stage form one 32-token
   // P V step of v_mfma_f32_16x16x32_bf16, token (chunk j, 4*j4+i) being k
   // index 8*j4 + 4*j + i of both operands.
-  constexpr int STEP = 2;
+  constexpr int STEP = shared_step<KIND>();
   constexpr int kStage = STEP * kUnits;  // 16-byte units of a stage's K (and of its V)
   constexpr int kVRec = 4 * ELT * STEP;
   constexpr int kVSeg = D * kVRec + 128;
   constexpr int kKBytes = kStage * 16;
   constexpr int kStageBuf = kKBytes + 4 * kVSeg;
   static_assert(KIND != kBF16 || kVRec == 16, "a bf16 record is one 32-token operand");
-  __shared__ __align__(16) char lds[2 * kStageBuf];
+  static_assert(2 * kStageBuf == shared_lds_bytes<KIND, D>(), "LDS stage buffers");
 
   const int hkv = geo.num_kv_heads;
-  int w = blockIdx.x;
   const int part = w % g.shared_parts;
   w /= g.shared_parts;
   const int cblk = w % g.col_blocks;
@@ -358,17 +370,38 @@ __global__ __launch_bounds__(kSharedWaves * kWave) void decode_shared_kernel(Cac
   }
 }
 
+// One launch: workgroups [0, n_shared) do the shared pass, the rest the
+// private partitions (the partition kernel's body, whose workgroups for
+// shared partitions exit at once).  Both kinds are resident together, so
+// the shared pass's compute overlaps the private partitions' HBM stream.
+template <int KIND, int D, int BS>
+__global__ __launch_bounds__(kSharedWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(decode_min_waves_per_eu<KIND, BS>())))
+void decode_shared_kernel(CacheGeom geo, DecodeArgs a, SharedArgs g) {
+  extern __shared__ __align__(16) char lds_dyn[];
+  const int bid = blockIdx.x;
+  if (bid < g.n_shared) {
+    shared_pass<KIND, D, BS>(geo, a, g, bid, lds_dyn);
+  } else {
+    decode_partition_body<KIND, D, BS, kSharedWaves, true>(geo, a, bid - g.n_shared,
+                                                             gridDim.x - g.n_shared,
+                                                             reinterpret_cast<float*>(lds_dyn));
+  }
+}
+
 template <int KIND, int D>
 hipError_t launch_shared_d(const CacheGeom& g, const DecodeArgs& a, const SharedArgs& sh,
                            bool* supported, hipStream_t st) {
-  const int64_t nwork =
-      static_cast<int64_t>(sh.num_groups) * g.num_kv_heads * sh.col_blocks * sh.shared_parts;
+  const int64_t nwork = static_cast<int64_t>(sh.n_shared) +
+                        static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
   if (nwork == 0) return hipSuccess;
+  const int G = a.num_q_heads / g.num_kv_heads;
+  const size_t lds = static_cast<size_t>(std::max(shared_lds_bytes<KIND, D>(), merge_lds_bytes(kSharedWaves, G, D)));
   const dim3 grid(static_cast<uint32_t>(nwork)), block(kSharedWaves * kWave);
   switch (g.block_size) {
-    case 8: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 8>), grid, block, 0, st, g, a, sh); break;
-    case 16: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 16>), grid, block, 0, st, g, a, sh); break;
-    case 32: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 32>), grid, block, 0, st, g, a, sh); break;
+    case 8: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 8>), grid, block, lds, st, g, a, sh); break;
+    case 16: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 16>), grid, block, lds, st, g, a, sh); break;
+    case 32: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 32>), grid, block, lds, st, g, a, sh); break;
     default: *supported = false; return hipSuccess;
   }
   return hipGetLastError();

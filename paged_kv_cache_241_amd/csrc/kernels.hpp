@@ -81,6 +81,7 @@ struct SharedArgs {
   int32_t num_groups = 0;
   int32_t col_blocks = 1;            // workgroups per (group, KV head, partition): 64 query columns each
   int32_t shared_parts = 0;          // partitions of the longest shared prefix
+  int32_t n_shared = 0;              // shared-pass workgroups: groups x KV heads x col_blocks x shared_parts
 };
 
 // The partition kernel and, with several partitions, the merge.  *supported
@@ -89,10 +90,13 @@ struct SharedArgs {
 hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool* supported,
                          hipStream_t stream);
 
-// The shared-prefix pass: partials of every group's shared partitions, for
-// all its members' query heads (a.seq_shared and the split-K workspace are
-// set; launch_decode does the private partitions and the merge, which must
-// follow this pass).
+// The merge of a split launch's partials (nothing when unsplit).
+hipError_t launch_merge(const CacheGeom& g, const DecodeArgs& a, hipStream_t stream);
+
+// Shared-prefix decode in one launch: the partials of every group's shared
+// partitions, for all its members' query heads, and beside them the private
+// partitions (a.seq_shared and the split-K workspace are set); the merge
+// (launch_merge) must follow.
 hipError_t launch_decode_shared(const CacheGeom& g, int kind, const DecodeArgs& a,
                                 const SharedArgs& sh, bool* supported, hipStream_t stream);
 

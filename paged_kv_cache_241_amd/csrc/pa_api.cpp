@@ -559,12 +559,16 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
     const int64_t cols = static_cast<int64_t>(max_members) * (num_queries_per_kv(num_q_heads, d.num_kv_heads));
     sh.col_blocks = static_cast<int32_t>((cols + 63) / 64);
     sh.shared_parts = max_shared / pt;
-    if (static_cast<int64_t>(num_groups) * d.num_kv_heads * sh.col_blocks * sh.shared_parts > INT32_MAX)
-      return fail(PA_ERR_INVALID_ARG, w + ": launch too large");
+    const int64_t n_shared = static_cast<int64_t>(num_groups) * d.num_kv_heads * sh.col_blocks * sh.shared_parts;
+    if (n_shared + grid * a.num_partitions > INT32_MAX) return fail(PA_ERR_INVALID_ARG, w + ": launch too large");
+    sh.n_shared = static_cast<int32_t>(n_shared);
+    // one launch for the shared pass and the private partitions, then the merge
     hipError_t es = pa::launch_decode_shared(pool->geom, kind, a, sh, &supported,
                                              static_cast<hipStream_t>(stream));
     if (!supported) return fail(PA_ERR_UNSUPPORTED, w + ": no kernel for this shape");
+    if (es == hipSuccess) es = pa::launch_merge(pool->geom, a, static_cast<hipStream_t>(stream));
     if (es != hipSuccess) return fail(PA_ERR_HIP, std::string(w + ": ") + hipGetErrorString(es));
+    return PA_OK;
   }
   hipError_t e = pa::launch_decode(pool->geom, kind, a, &supported, static_cast<hipStream_t>(stream));
   if (!supported) return fail(PA_ERR_UNSUPPORTED, w + ": no kernel for this shape");
