@@ -3,9 +3,10 @@
 Samples of one prompt share its blocks; pa_decode_shared reads them once per
 group and KV head.  Its output must meet the same tolerances against the fp64
 oracle as pa_decode, and differ from pa_decode with the same partitions only
-by the order of fp32 sums.  Cases: bf16 and fp32, head_dim 64 and 128, blocks
-of 8, 16 and 32, groups wider than one 64-column block, and a batch order that
-mixes groups of several sizes with requests outside any group.
+by the order of fp32 sums.  Cases: bf16 and fp32 each with head_dim 64 and
+128, blocks of 8, 16 and 32, groups wider than one 64-column block, a batch
+order that mixes groups of several sizes with requests outside any group, and
+the full-size workload in the benchmark's launch on sampled rows.
 """
 
 from __future__ import annotations
@@ -70,6 +71,9 @@ def _check_oracle(case: Case, got: torch.Tensor):
     ({"batch": 24, "prompt_len": 200, "private_len": 40, "num_blocks": 120, "block_size": 32}, 64),
     # 16 samples x 8 query heads per KV head = 128 columns: two column blocks
     ({"batch": 32, "samples": 16, "prompt_len": 100, "private_len": 10, "num_blocks": 200}, 32),
+    # fp32 with head_dim 128 (one-chunk stages), bf16 with head_dim 64
+    ({"batch": 16, "prompt_len": 160, "private_len": 40, "num_blocks": 200, "kv_dtype": "f32"}, 64),
+    ({"batch": 24, "prompt_len": 200, "private_len": 40, "num_blocks": 200, "head_dim": 64}, 96),
 ])
 def test_shared_decode_matches_oracle_and_plain_decode(over, T):
     cfg = W.get(5, **over)
@@ -96,3 +100,22 @@ def test_mixed_groups_and_singletons():
     plain = case.decode(partition_tokens=32)
     for s in range(cfg.batch):
         assert row_rel_err(to_f64(got[s]), to_f64(plain[s])) <= 1e-5, s
+
+
+def test_full_size_in_the_benchmark_launch_sampled_rows():
+    # The shared-prefix workload at full size (320 samples of 40 prompts of
+    # 2048 tokens, 256 private tokens each) with 1024-token partitions, as
+    # bench.py --shared-prefix 1024 launches it; rows checked against the
+    # oracle on a sample (every prompt's first sample, both ends of a group).
+    cfg = W.get(5)
+    case = Case(cfg)
+    got, seq_shared, groups = _run_shared(case, 1024, list(range(cfg.batch)))
+    assert len(groups) == cfg.batch // cfg.samples and int(seq_shared.min()) == 2048
+    assert torch.isfinite(got).all()
+    rng = np.random.default_rng(5)
+    sample = sorted(set([0, 7, 8, cfg.batch - 1] + [int(x) for x in rng.choice(cfg.batch, 4, replace=False)]))
+    g = to_f64(got)
+    ref = case.reference(sample)
+    for s in sample:
+        err = row_rel_err(g[s], ref[s])
+        assert err <= BF16_STATED and err <= BF16_INTERNAL, (s, err)
