@@ -52,6 +52,7 @@ namespace pa {
 namespace {
 
 constexpr int kMergeWaves = 4;   // merge rows per workgroup, one a wave
+constexpr int kMergeUnroll = 8;  // rows of up to this many partitions load all at once
 constexpr int kMaxGroup = 16;     // query heads per KV head the tile can hold
 constexpr int kMaxMergeLds = 64 * 1024;
 
@@ -154,10 +155,11 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a,
 }
 
 // Merge context partitions in partition order: one wave per (seq, q head),
-// kMergeWaves rows per workgroup.  Lane l holds the running max and weight sum
-// of partition p0 + l (64 partitions a round) and D / 64 output dims; a row's
-// loads are all issued before its arithmetic.  The sums run over p in order,
-// as fma(w_p, acc_p, .) and fma(w_p, l_p, .).
+// kMergeWaves rows per workgroup, D / 64 output dims a lane.  Rows of up to
+// kMergeUnroll partitions issue all their loads (maxima and sums as scalar
+// loads, partial outputs as vector loads) before any arithmetic; longer rows
+// hold the maxima and sums of 64 partitions a round in the lanes.  The sums
+// run over p in order, as fma(w_p, acc_p, .) and fma(w_p, l_p, .).
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(DecodeArgs a) {
   constexpr int E = D / kWave;
@@ -178,7 +180,40 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(Decod
   float A[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) A[e] = 0.0f;
-  if (ps > 0) {
+  if (ps > 0 && ps <= kMergeUnroll) {
+    // all of the row's loads at once (indices clamped into [0, ps), the
+    // copies past ps weigh nothing), then the same sums as below
+    float mp[kMergeUnroll], lp[kMergeUnroll], ap[kMergeUnroll][E];
+#pragma unroll
+    for (int k = 0; k < kMergeUnroll; ++k) {
+      const int p = min(k, ps - 1);
+      mp[k] = ml[2 * p];
+      lp[k] = ml[2 * p + 1];
+#pragma unroll
+      for (int e = 0; e < E; ++e) ap[k][e] = accp[p * D + e];
+    }
+    // (the clamped copies repeat partition ps - 1: the max is unchanged)
+    float mx = mp[0];
+#pragma unroll
+    for (int k = 1; k < kMergeUnroll; ++k) mx = fmaxf(mx, mp[k]);
+    // selects rather than branches, so that every load is used and issued
+    // up front
+    float Lt = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMergeUnroll; ++k) {
+      const float wt = fexp2(mp[k] - mx);
+      const bool live = k < ps;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float t = fmaf(wt, ap[k][e], A[e]);
+        A[e] = live ? t : A[e];
+      }
+      const float lt = fmaf(wt, lp[k], Lt);
+      Lt = live ? lt : Lt;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) A[e] = A[e] / Lt;
+  } else if (ps > 0) {
     float mx = -INFINITY;
     for (int p0 = 0; p0 < ps; p0 += kWave)
       if (p0 + lane < ps) mx = fmaxf(mx, ml[2 * (p0 + lane)]);
