@@ -1,6 +1,11 @@
-// The decode partition kernel's body (kernels.hip launches it alone; the
-// shared-prefix launch in decode_shared.hip runs it for the private
-// partitions beside the shared pass).
+// The decode partition kernel's body: attention of one query token per
+// request over K/V held in fixed blocks reached through a block table
+// ("Running Out of Cache", paging paragraph and Terms), or over a per-request
+// sub-tensor at reqId x S ("Leveraging Low-Level CUDA APIs for vAttention's
+// Dynamic Memory", 5.2.3), for one context partition of one (sequence, KV
+// head).  kernels.hip launches it alone; the shared-prefix launch in
+// decode_shared.hip runs it for the private partitions beside the shared
+// pass.
 #pragma once
 
 #include <hip/hip_runtime.h>

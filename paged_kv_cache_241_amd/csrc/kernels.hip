@@ -37,7 +37,13 @@
 //   * waves merge through LDS in a fixed order; partitions are merged by a
 //     second small kernel in partition order.  Every reduction order depends
 //     only on logical token positions, so results do not depend on which
-//     physical blocks hold the tokens, nor on paged vs contiguous storage.
+//     physical blocks hold the tokens, nor on paged vs contiguous storage;
+//   * a launch split into partitions runs from a work plan (one small
+//     kernel): only partitions holding tokens, full ones first and each
+//     context's last one longest first, so that the grid holds no empty
+//     workgroups among the others and ends on short ones.
+// The partition kernel's body is in decode_partition.hpp (the shared-prefix
+// launch runs it too).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
