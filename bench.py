@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--prompt-len", type=int, default=0, help="workload 5: prompt length")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--block-size", type=int, default=0, help="tokens per block (0: workload's, 16)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="workloads 2 and 4: number of sequences (0: the workload's)")
+    ap.add_argument("--context", type=int, default=0,
+                    help="workloads 2 and 4: context length (0: the workload's)")
     ap.add_argument("--shared-prefix", type=int, default=0, metavar="TOKENS",
                     help="decode with pa_decode_shared in partitions of TOKENS tokens (samples "
                          "sharing a prompt read its blocks once)")
@@ -559,10 +563,22 @@ def main():
         if base.num_blocks:
             over["num_blocks"] = base.num_blocks * base.block_size // args.block_size
         base = W.get(args.config, **over)
+    if args.batch or args.context:
+        if not base.context:
+            print(json.dumps({"error": "--batch and --context apply to the uniform-context workloads 2 and 4"}))
+            sys.exit(2)
+        over["batch"] = args.batch or base.batch
+        over["context"] = args.context or base.context
+        steps = args.warmup + args.steps + 2
+        need = -(-over["batch"] * min(over["context"] + steps, base.max_seq_len) // base.block_size) + 16
+        over["num_blocks"] = max(base.num_blocks, need)
+        base = W.get(args.config, **over)
     nominal = base.context
     if nominal:
-        # centre the timed steps on the nominal context
-        over["context"] = nominal - args.warmup - (args.steps - 1) // 2
+        # centre the timed steps on the nominal context, and keep the last
+        # step within the per-request cap
+        over["context"] = min(nominal - args.warmup - (args.steps - 1) // 2,
+                              base.max_seq_len - args.warmup - args.steps - 1)
     cfg = W.get(args.config, **over)
     nl = args.layers or cfg.num_layers
     bench = Bench(cfg, args.layout, nl, args.warmup + args.steps + 1, args.partition_tokens)
@@ -610,7 +626,9 @@ def main():
         "dtype": cfg.kv_dtype,
         "data": "synthetic",
         "config": {
-            "workload": cfg.name + ("" if args.layout == "paged" else ", contiguous reqId x S layout"),
+            "workload": cfg.name + ("" if args.layout == "paged" else ", contiguous reqId x S layout") +
+                        (f" (run with batch {b}, context about {cfg.context + args.warmup + (args.steps - 1) // 2})"
+                         if args.batch or args.context else ""),
             "batch": b, "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
             "head_dim": cfg.head_dim, "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
             "mean_context_timed": round(float(np.mean(lens_seen)), 2),
@@ -625,10 +643,11 @@ def main():
         "pool_utilisation": round(stats["utilisation"], 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("pa_decode_shared (decode_shared_kernel + decode_partition_kernel + "
+            "kernel": ("pa_decode_shared (decode_shared_kernel: shared pass and private partitions; "
                        "decode_merge_kernel)" if args.shared_prefix else
                        ("pa_decode" if args.separate_append else "pa_append_decode") +
-                       " (decode_partition_kernel, + decode_merge_kernel when contexts are split)"),
+                       " (decode_partition_kernel; decode_plan_kernel and decode_merge_kernel "
+                       "when contexts are split)"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

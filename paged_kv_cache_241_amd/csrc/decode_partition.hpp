@@ -50,12 +50,14 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   const int P = a.num_partitions;
   const int hkv = geo.num_kv_heads;
   const int G = a.num_q_heads / hkv;
-  // With a plan (split contexts), workgroup i takes the KV head i % hkv of
-  // plan item i / hkv; the items with work fill the front of the grid,
+  // With a plan (large split launches), workgroup i takes the KV head i % hkv
+  // of plan item i / hkv; the items with work fill the front of the grid,
   // longest first, and the grid's tail exits at once.  Without one, work
   // items are (r, sequence, KV head), r-major, with r a partition's place
   // counted from the end of its context: with one partition per context
-  // that is each context's only one; after a shared-prefix pass the private
+  // that is each context's only one; in a small split launch r runs
+  // downwards, so that each context's last, partly filled partition comes
+  // last; after a shared-prefix pass it runs upwards, so that the private
   // partitions (the last ones) come first and the shared ones, which exit at
   // once, after them.
   const int tid = threadIdx.x;
@@ -70,7 +72,7 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   } else {
     const int work = work_item(bid, nblocks, !NT);
     const int pairs = a.num_seqs * hkv;
-    const int r = work / pairs;
+    const int r = a.seq_shared != nullptr ? work / pairs : P - 1 - work / pairs;
     kvh = (work % pairs) % hkv;
     s = (work % pairs) / hkv;
     L = a.lens[s];

@@ -82,6 +82,7 @@ void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
 // than the longest) come after all others instead of among them.  One
 // workgroup.
 constexpr int kPlanThreads = 1024;
+constexpr int64_t kPlanMinGrid = 2048;  // two rounds of resident workgroups (256 CUs x 4)
 constexpr int kPlanBuckets = 64;  // one per lane of a wave
 constexpr int kPlanKeep = 4;      // sequences per thread kept in registers
 
@@ -164,8 +165,9 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a,
 // kMergeWaves rows per workgroup, D / 64 output dims a lane.  Rows of up to
 // kMergeUnroll partitions issue all their loads (maxima and sums as scalar
 // loads, partial outputs as vector loads) before any arithmetic; longer rows
-// hold the maxima and sums of 64 partitions a round in the lanes.  The sums
-// run over p in order, as fma(w_p, acc_p, .) and fma(w_p, l_p, .).
+// find their maximum 64 partitions a round in the lanes, then load and sum
+// kMergeUnroll partitions at a time.  The sums run over p in order, as
+// fma(w_p, acc_p, .) and fma(w_p, l_p, .).
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(DecodeArgs a) {
   constexpr int E = D / kWave;
@@ -220,27 +222,35 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(Decod
 #pragma unroll
     for (int e = 0; e < E; ++e) A[e] = A[e] / Lt;
   } else if (ps > 0) {
+    // the maximum over all partitions (64 a round in the lanes), then the
+    // sums in groups of kMergeUnroll partitions whose loads issue together
     float mx = -INFINITY;
     for (int p0 = 0; p0 < ps; p0 += kWave)
       if (p0 + lane < ps) mx = fmaxf(mx, ml[2 * (p0 + lane)]);
 #pragma unroll
     for (int x = kWave / 2; x >= 1; x /= 2) mx = fmaxf(mx, __shfl_xor(mx, x));
     float Lt = 0.0f;
-    for (int p0 = 0; p0 < ps; p0 += kWave) {
-      float wl = 0.0f, ll = 0.0f;
-      if (p0 + lane < ps) {
-        wl = fexp2(ml[2 * (p0 + lane)] - mx);
-        ll = ml[2 * (p0 + lane) + 1];
-      }
-      const int n = min(kWave, ps - p0);
-      const float* ap = accp + static_cast<int64_t>(p0) * D;
-#pragma unroll 8
-      for (int k = 0; k < n; ++k) {
-        const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k));
-        const float lk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ll), k));
+    for (int p0 = 0; p0 < ps; p0 += kMergeUnroll) {
+      float mp[kMergeUnroll], lp[kMergeUnroll], ap[kMergeUnroll][E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) A[e] = fmaf(wt, ap[k * D + e], A[e]);
-        Lt = fmaf(wt, lk, Lt);
+      for (int k = 0; k < kMergeUnroll; ++k) {
+        const int p = min(p0 + k, ps - 1);
+        mp[k] = ml[2 * p];
+        lp[k] = ml[2 * p + 1];
+#pragma unroll
+        for (int e = 0; e < E; ++e) ap[k][e] = accp[static_cast<int64_t>(p) * D + e];
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeUnroll; ++k) {
+        const float wt = fexp2(mp[k] - mx);
+        const bool live = p0 + k < ps;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float t = fmaf(wt, ap[k][e], A[e]);
+          A[e] = live ? t : A[e];
+        }
+        const float lt = fmaf(wt, lp[k], Lt);
+        Lt = live ? lt : Lt;
       }
     }
 #pragma unroll
@@ -389,10 +399,13 @@ hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool
     return hipSuccess;
   }
   DecodeArgs ap = a;
-  // Split launches run from a plan (decode_plan_kernel), except after a
-  // shared-prefix pass: there every context has one private partition left,
-  // and the plan's launch costs more (measured) than the skipped partitions.
-  if (a.num_partitions > 1 && a.seq_shared == nullptr) {
+  // Large split launches run from a plan (decode_plan_kernel).  Below
+  // kPlanMinGrid workgroups the plan's launch (~3 us) costs more than it
+  // saves (measured: batch 1-16 with contexts of 4-8 K tokens); after a
+  // shared-prefix pass every context has one private partition left, and
+  // the plan does not pay either.
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
+  if (a.num_partitions > 1 && a.seq_shared == nullptr && grid >= kPlanMinGrid) {
     // the plan follows the partials in the workspace
     int2* plan = reinterpret_cast<int2*>(a.ws + static_cast<int64_t>(a.num_seqs) * a.num_q_heads *
                                                     a.num_partitions * (g.head_dim + 2));
