@@ -267,18 +267,15 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(Decod
 // ---------------------------------------------------------------------------
 // append and copy-on-write copies
 // ---------------------------------------------------------------------------
-// One thread per (token, KV head, 16-byte chunk of the row): the K chunk is
-// stored whole, the V chunk's elements go to their dims' rows of the V tile.
-__global__ __launch_bounds__(256) void append_kv_kernel(CacheGeom g, int32_t layer,
-                                                        const uint4* __restrict__ k,
-                                                        const uint4* __restrict__ v,
-                                                        const int32_t* __restrict__ slots,
-                                                        int32_t n) {
+// One (token, KV head, 16-byte piece of the row) of an append: the K piece
+// is stored whole, the V piece's elements go to their dims' rows of the V
+// tile.  idx = (token * num_kv_heads + head) * pieces + piece.
+__device__ __forceinline__ void append_item(const CacheGeom& g, int32_t layer, const uint4* __restrict__ k,
+                                            const uint4* __restrict__ v, const int32_t* __restrict__ slots,
+                                            int64_t idx) {
   const int ve = 16 / g.elt;
   const int chunks = g.head_dim / ve;
   const int per_tok = g.num_kv_heads * chunks;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<int64_t>(n) * per_tok) return;
   const int i = static_cast<int>(idx / per_tok);
   const int rem = static_cast<int>(idx % per_tok);
   const int h = rem / chunks, q = rem % chunks;
@@ -307,6 +304,42 @@ __global__ __launch_bounds__(256) void append_kv_kernel(CacheGeom g, int32_t lay
     for (int e = 0; e < 4; ++e)
       *reinterpret_cast<uint32_t*>(vt + ((d0 + e) * g.block_size + o) * 4) = ws[e];
   }
+}
+
+// One thread per (token, KV head, 16-byte piece of the row): the decode
+// step's append (one scattered token per sequence).
+__global__ __launch_bounds__(256) void append_kv_kernel(CacheGeom g, int32_t layer,
+                                                        const uint4* __restrict__ k,
+                                                        const uint4* __restrict__ v,
+                                                        const int32_t* __restrict__ slots,
+                                                        int32_t n) {
+  const int64_t per_tok = static_cast<int64_t>(g.num_kv_heads) * (g.head_dim * g.elt / 16);
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(n) * per_tok) return;
+  append_item(g, layer, k, v, slots, idx);
+}
+
+// Appends of many tokens (prompt ingestion): the same items as
+// append_kv_kernel, in windows of 16 tokens ordered token-fastest, so that
+// 16 lanes of a wave hold consecutive tokens of one (head, piece).  A
+// prefill's consecutive tokens sit in consecutive rows of a block's tiles:
+// those lanes' K pieces then form one 256-byte run and their V elements
+// whole 32-byte rows, which the memory system merges into full-sector writes
+// instead of 2-byte ones; each lane group reads 64 contiguous bytes a token.
+constexpr int kBulkMinTokens = 256;   // appends of fewer tokens use append_kv_kernel
+
+__global__ __launch_bounds__(256) void append_kv_bulk_kernel(CacheGeom g, int32_t layer,
+                                                             const uint4* __restrict__ k,
+                                                             const uint4* __restrict__ v,
+                                                             const int32_t* __restrict__ slots,
+                                                             int32_t n) {
+  const int64_t pieces = static_cast<int64_t>(g.num_kv_heads) * (g.head_dim * g.elt / 16);
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  // windows of 16 tokens: token-fastest inside a window, then (head, piece)
+  const int64_t win = x / (16 * pieces), r = x % (16 * pieces);
+  const int64_t token = win * 16 + r % 16, hp = r / 16;  // hp: head * pieces-per-head + piece
+  if (token >= n) return;
+  append_item(g, layer, k, v, slots, token * pieces + hp);
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CacheGeom g,
@@ -372,6 +405,14 @@ hipError_t launch_append(const CacheGeom& g, int32_t layer, const void* k, const
   if (n <= 0) return hipSuccess;
   const int64_t threads = static_cast<int64_t>(n) * g.num_kv_heads * (g.head_dim * g.elt / 16);
   const uint32_t blocks = static_cast<uint32_t>((threads + 255) / 256);
+  if (n >= kBulkMinTokens) {
+    // whole 16-token windows (the last one partly empty)
+    const int64_t wthreads = static_cast<int64_t>((n + 15) / 16) * 16 * g.num_kv_heads * (g.head_dim * g.elt / 16);
+    const uint32_t wblocks = static_cast<uint32_t>((wthreads + 255) / 256);
+    hipLaunchKernelGGL(append_kv_bulk_kernel, dim3(wblocks), dim3(256), 0, stream, g, layer,
+                       static_cast<const uint4*>(k), static_cast<const uint4*>(v), slots, n);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(append_kv_kernel, dim3(blocks), dim3(256), 0, stream, g, layer,
                      static_cast<const uint4*>(k), static_cast<const uint4*>(v), slots, n);
   return hipGetLastError();

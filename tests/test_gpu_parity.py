@@ -112,6 +112,41 @@ def test_append_and_copy_bit_exact_whole_cache(cid, over):
     assert np.array_equal(A.v_rows(_bits(case.pool.v_cache)), exp["v"])
 
 
+def test_bulk_append_scattered_and_straddling_slots_bit_exact():
+    # Appends of 256 tokens or more take the bulk kernel (16-token windows,
+    # token-fastest).  Here their slots are scattered (one token for each of
+    # 300 sequences, twice), then one more token for each and a 700-token
+    # prompt in the same call: the prompt starts at index 300 of the call, so
+    # its 16-token windows straddle its blocks.
+    from paged_kv_cache_241_amd.pool import Pool
+
+    hkv, d, bs = 2, 128, 16
+    nb = 300 + -(-700 // bs) + 4
+    pool = Pool(1, nb, bs, hkv, d, "bf16", "paged", max_seqs=400, max_seq_len=1024)
+    pool.set_free_order(W.free_order(nb, 2417))
+    saved = {}
+    for name, t, off in (("k", pool.k_cache, 21), ("v", pool.v_cache, 22)):
+        saved[name] = W.normal(tuple(t.shape), 2417 + off, "bf16", "cuda")
+        t.copy_(saved[name])
+    exp = {"k": A.k_rows(_bits(saved["k"]))[0], "v": np.ascontiguousarray(A.v_rows(_bits(saved["v"])))[0]}
+    rids = [pool.add() for _ in range(301)]
+    gen = torch.Generator(device="cpu").manual_seed(2417)
+    for rids_now, counts in ((rids[:300], [1] * 300), (rids[:300], [1] * 300),
+                             (rids, [1] * 300 + [700])):
+        slots, _ = pool.reserve(rids_now, counts)
+        n = len(slots)
+        assert n >= 256
+        kr = torch.randn((n, hkv, d), generator=gen).to(torch.bfloat16)
+        vr = torch.randn((n, hkv, d), generator=gen).to(torch.bfloat16)
+        pool.append_kv(0, kr.cuda(), vr.cuda(), torch.from_numpy(slots.astype(np.int32)).cuda())
+        exp["k"] = A.append_scatter(exp["k"], slots, _bits(kr))
+        exp["v"] = A.append_scatter(exp["v"], slots, _bits(vr))
+    torch.cuda.synchronize()
+    assert np.array_equal(A.k_rows(_bits(pool.k_cache))[0], exp["k"])
+    assert np.array_equal(A.v_rows(_bits(pool.v_cache))[0], exp["v"])
+    pool.close()
+
+
 # --------------------------------------------------------------------------
 # decode parity
 # --------------------------------------------------------------------------
