@@ -1,4 +1,5 @@
-"""Compile-time guard on the decode kernels' registers (CPU only, needs hipcc).
+"""Compile-time guard on the decode kernels' registers (CPU only, needs hipcc): the partition
+kernel and the shared-prefix launch that runs its body.
 
 A runtime-indexed register array or an over-large live set silently sends
 values to scratch memory, which cut the decode rate by a third in one
@@ -24,12 +25,12 @@ def _hipcc():
     return None
 
 
-@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
-def test_decode_kernels_use_no_scratch_and_keep_occupancy():
+def _resources(source: str) -> dict:
+    """Per-kernel resource remarks of one source file: {name: {remark: value}}."""
     from paged_kv_cache_241_amd import build
 
     cmd = [_hipcc(), *build.HIP_FLAGS, "-I", os.path.join(ROOT, "include"),
-           "-c", os.path.join(build.CSRC, "kernels.hip"), "-o", os.devnull,
+           "-c", os.path.join(build.CSRC, source), "-o", os.devnull,
            "-Rpass-analysis=kernel-resource-usage"]
     res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stderr[-2000:]
@@ -44,6 +45,28 @@ def test_decode_kernels_use_no_scratch_and_keep_occupancy():
         m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+)", line)
         if m and name:
             kernels[name][m.group(1).strip()] = int(m.group(2))
+    return kernels
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_shared_prefix_kernels_use_no_scratch_and_keep_occupancy():
+    # the shared-prefix launch runs the partition kernel's body for its
+    # private partitions: the same guard applies to it
+    kernels = _resources("decode_shared.hip")
+    shared = {k: v for k, v in kernels.items() if "decode_shared_kernel" in k}
+    assert len(shared) == 2 * 2 * 3   # dtype x head_dim x block
+    for k, v in shared.items():
+        assert v.get("ScratchSize", 0) == 0, (k, v)
+        assert v.get("VGPRs Spill", 0) == 0, (k, v)
+    big = {k: v for k, v in shared.items() if re.search(r"ILi1ELi(64|128)ELi(16|32)E", k)}
+    assert len(big) == 2 * 2
+    for k, v in big.items():
+        assert v["Occupancy"] >= 4, (k, v)
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not available")
+def test_decode_kernels_use_no_scratch_and_keep_occupancy():
+    kernels = _resources("kernels.hip")
     decode = {k: v for k, v in kernels.items() if "decode_partition_kernel" in k}
     assert len(decode) == 2 * 2 * 3 * 2 * 2   # dtype x head_dim x block x waves x streaming
     for k, v in decode.items():
