@@ -60,7 +60,6 @@ namespace {
 constexpr int kMergeWaves = 4;   // merge rows per workgroup, one a wave
 constexpr int kMergeUnroll = 8;  // rows of up to this many partitions load all at once
 constexpr int kMaxGroup = 16;     // query heads per KV head the tile can hold
-constexpr int kMaxMergeLds = 64 * 1024;
 
 template <int KIND, int D, int BS, int W, bool NT>
 __global__ __launch_bounds__(W * kWave)
@@ -359,8 +358,9 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CacheGeom g,
   }
 }
 
-template <int KIND, int D, int BS, int W>
-hipError_t launch_decode_w(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
+template <int KIND, int D, int BS>
+hipError_t launch_decode_t(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
+  constexpr int W = kDecodeWaves;
   const int64_t nwork = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
   const int G = a.num_q_heads / g.num_kv_heads;
   if (a.streaming)
@@ -378,14 +378,6 @@ hipError_t launch_merge_d(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(static_cast<uint32_t>((rows + kMergeWaves - 1) / kMergeWaves)),
                      dim3(kMergeWaves * kWave), 0, st, a);
   return hipGetLastError();
-}
-
-template <int KIND, int D, int BS>
-hipError_t launch_decode_t(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
-  const int G = a.num_q_heads / g.num_kv_heads;
-  if (a.waves == 8 && merge_lds_bytes(8, G, D) <= kMaxMergeLds)
-    return launch_decode_w<KIND, D, BS, 8>(g, a, st);
-  return launch_decode_w<KIND, D, BS, 4>(g, a, st);
 }
 
 template <int KIND, int D>

@@ -10,6 +10,9 @@ namespace pa {
 
 enum Kind : int { kF32 = 0, kBF16 = 1 };
 
+// Waves per workgroup of the decode partition kernel.
+constexpr int kDecodeWaves = 4;
+
 // Cache geometry.  Per layer, K and V are arrays of tiles, one tile per
 // (block, KV head):
 //   K tile [head_dim/VE][block_size][VE]  (16-byte chunks, VE = 16/elt)
@@ -60,7 +63,6 @@ struct DecodeArgs {
   const void* new_k = nullptr;
   const void* new_v = nullptr;
   const int32_t* new_slots = nullptr;
-  int32_t waves = 4;                 // waves per workgroup: 4 or 8
   int32_t streaming = 1;             // non-temporal K/V loads (no block is shared)
   float scale = 1.0f;
   // shared-prefix decode: the first seq_shared[s] tokens of sequence s (whole

@@ -85,9 +85,6 @@ int64_t layer_bytes(const pa_pool_desc* d) {
 // are cut into kSplitTokens partitions (22% faster on the ragged
 // Exp(1024)+Exp(256) mix than one partition).  Partitions hold at least
 // kMinTokens so that every wave streams several chunks.
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 4
-#endif
 constexpr int64_t kTargetWaves = 2048;
 constexpr int32_t kSplitAbove = 4096;
 constexpr int32_t kSplitTokens = 1024;
@@ -100,7 +97,7 @@ int32_t choose_partition_tokens(const pa_pool* p, int32_t num_seqs, int32_t max_
   const int32_t unit = partition_unit(p);
   if (partition_tokens > 0) return partition_tokens;
   if (max_context <= 0) return unit;
-  const int64_t waves = static_cast<int64_t>(num_seqs) * p->desc.num_kv_heads * PA_DECODE_WAVES;
+  const int64_t waves = static_cast<int64_t>(num_seqs) * p->desc.num_kv_heads * pa::kDecodeWaves;
   const int64_t parts = (kTargetWaves + waves - 1) / waves;
   int64_t tokens = (max_context + parts - 1) / parts;
   if (max_context > kSplitAbove && tokens > kSplitTokens) tokens = kSplitTokens;
@@ -530,7 +527,6 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
     a.num_partitions = std::max(a.num_partitions, 2);
     a.seq_shared = d_seq_shared;
   }
-  a.waves = PA_DECODE_WAVES;
   if (d_k_new != nullptr) {
     a.new_k = d_k_new;
     a.new_v = d_v_new;

@@ -68,13 +68,13 @@ def test_shared_prefix_kernels_use_no_scratch_and_keep_occupancy():
 def test_decode_kernels_use_no_scratch_and_keep_occupancy():
     kernels = _resources("kernels.hip")
     decode = {k: v for k, v in kernels.items() if "decode_partition_kernel" in k}
-    assert len(decode) == 2 * 2 * 3 * 2 * 2   # dtype x head_dim x block x waves x streaming
+    assert len(decode) == 2 * 2 * 3 * 2   # dtype x head_dim x block x streaming
     for k, v in decode.items():
         assert v.get("ScratchSize", 0) == 0, (k, v)
         assert v.get("VGPRs Spill", 0) == 0, (k, v)
     # template arguments: <KIND, D, BS, W, NT>, KIND 1 = bf16
     bf16_big_blocks = {k: v for k, v in decode.items()
                        if re.search(r"ILi1ELi(64|128)ELi(16|32)ELi", k)}
-    assert len(bf16_big_blocks) == 2 * 2 * 2 * 2
+    assert len(bf16_big_blocks) == 2 * 2 * 2
     for k, v in bf16_big_blocks.items():
         assert v["Occupancy"] >= 4, (k, v)
