@@ -582,6 +582,15 @@ def main():
         over["context"] = min(nominal - args.warmup - (args.steps - 1) // 2,
                               base.max_seq_len - args.warmup - args.steps - 1)
     cfg = W.get(args.config, **over)
+    if not cfg.context:
+        # drawn or listed contexts grow by one token a step: lift the
+        # per-request cap where the longest would outgrow it (the tiny
+        # workload's 100-token context passes its 128-token cap in 29 steps)
+        longest = int(W.plan(cfg).lengths.max())
+        grown = -(-(longest + args.warmup + args.steps + 1) // cfg.block_size) * cfg.block_size
+        if grown > cfg.max_seq_len:
+            over["max_seq_len"] = grown
+            cfg = W.get(args.config, **over)
     nl = args.layers or cfg.num_layers
     bench = Bench(cfg, args.layout, nl, args.warmup + args.steps + 1, args.partition_tokens)
     if args.shared_prefix:
@@ -659,7 +668,10 @@ def main():
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
         },
     }
-    if args.config == 2 and args.layout == "paged" and args.partition_tokens == 0:
+    # the counters were taken on workload 2 as it stands: no other batch,
+    # context, block size, layer count or partition size
+    as_counted = not (args.batch or args.context or args.block_size or args.layers or args.partition_tokens)
+    if args.config == 2 and args.layout == "paged" and as_counted:
         res["roofline"]["traffic"] = measured_traffic(
             "cfg2-paged" + ("" if args.separate_append else "-fused"))
     if not args.no_cpu_baseline:
