@@ -122,3 +122,26 @@ def test_many_short_sequences_split_into_many_partitions(B):
         lens = np.maximum(lens, 1)   # each sequence appends its last token in the launch
     sample = sorted(set([0, 1, 2, B - 1] + [int(x) for x in rng.choice(B, 40, replace=False)]))
     _run(rng, 2, 4, 64, 16, "bf16", "paged", lens, 16, fused, max_seq_len=128, check_rows=sample)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_large_ragged_batch(seed):
+    # 16-300 sequences with Exp(300 | 1000 | 2500) contexts, one of them at
+    # the 8192-token cap in a third of the cases: split launches with and
+    # without the work plan; sampled rows (both ends, the longest, 8 more)
+    rng = np.random.default_rng(9000 + seed)
+    hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 4, 7, 8]))
+    bs = int(rng.choice([8, 16, 16, 32]))
+    dtype = "bf16" if rng.integers(4) else "f32"
+    mean = float(rng.choice([300, 1000, 2500]))
+    B = int(rng.integers(16, 300))
+    B = min(B, max(16, int(150000 / mean)))
+    lens = np.minimum(8192, np.maximum(1, np.rint(rng.exponential(mean, B)))).astype(np.int64)
+    lens[rng.integers(B)] = 8192 if rng.integers(3) == 0 else lens[0]
+    fused = bool(rng.integers(2))
+    layout = "paged" if rng.integers(4) else "contiguous"
+    unit = max(16, bs)
+    pt = int(rng.choice([0, 0, 256, 512, 1024])) // unit * unit
+    rows = sorted(set([0, B - 1, int(np.argmax(lens))] + [int(x) for x in rng.choice(B, 8, replace=False)]))
+    _run(rng, hkv, G, 128, bs, dtype, layout, lens, pt, fused, max_seq_len=8192, check_rows=rows)

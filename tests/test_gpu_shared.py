@@ -5,8 +5,10 @@ group and KV head.  Its output must meet the same tolerances against the fp64
 oracle as pa_decode, and differ from pa_decode with the same partitions only
 by the order of fp32 sums.  Cases: bf16 and fp32 each with head_dim 64 and
 128, blocks of 8, 16 and 32, groups wider than one 64-column block, a batch
-order that mixes groups of several sizes with requests outside any group, and
-the full-size workload in the benchmark's launch on sampled rows.
+order that mixes groups of several sizes with requests outside any group, the
+full-size workload in the benchmark's launch on sampled rows, and seeded
+random batches (prompts, samples per prompt, prompt and private lengths,
+heads, head_dim, dtype, block size, partition size, batch order all drawn).
 """
 
 from __future__ import annotations
@@ -119,3 +121,33 @@ def test_full_size_in_the_benchmark_launch_sampled_rows():
     for s in sample:
         err = row_rel_err(g[s], ref[s])
         assert err <= BF16_STATED and err <= BF16_INTERNAL, (s, err)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_shared_batches(seed):
+    rng = np.random.default_rng(7000 + seed)
+    samples = int(rng.integers(2, 17))
+    prompts = int(rng.integers(1, 5))
+    bs = int(rng.choice([8, 16, 32]))
+    d = int(rng.choice([64, 128]))
+    dtype = "bf16" if rng.integers(3) else "f32"
+    unit = max(16, bs)
+    T = unit * int(rng.integers(1, 5))
+    prompt = int(rng.integers(T, 4 * T + 60))
+    private = int(rng.integers(1, 80))
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 4, 8]))
+    batch = samples * prompts
+    cfg = W.get(5, batch=batch, samples=samples, prompt_len=prompt, private_len=private,
+                num_blocks=batch * (-(-(prompt + private) // bs) + 2), block_size=bs, head_dim=d,
+                kv_dtype=dtype, num_kv_heads=hkv, num_q_heads=hq,
+                max_seq_len=-(-(prompt + private + 1) // unit) * unit + 64, seed=7000 + seed)
+    case = Case(cfg)
+    order = list(range(batch))
+    if rng.integers(2):
+        rng.shuffle(order)
+    got, _, _ = _run_shared(case, T, order)
+    _check_oracle(case, got)
+    plain = case.decode(partition_tokens=T)
+    for s in range(batch):
+        assert row_rel_err(to_f64(got[s]), to_f64(plain[s])) <= 1e-5, s
