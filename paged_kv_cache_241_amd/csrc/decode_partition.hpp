@@ -27,6 +27,14 @@ namespace {
 // per SIMD (the occupancy the HBM stream needs); the others would spill.
 template <int KIND, int BS>
 constexpr int decode_min_waves_per_eu() { return KIND == kBF16 && BS >= kChunk ? 4 : 1; }
+// The two-chunk pipeline (PIPE) keeps a second chunk's K/V operands in
+// registers; it runs only on grids of at most one wave per SIMD, so it may
+// take up to 256 VGPRs.  It exists for bf16 caches whose blocks hold whole
+// chunks.
+template <int KIND, int BS, bool PIPE>
+constexpr int decode_waves_per_eu() { return PIPE ? 2 : decode_min_waves_per_eu<KIND, BS>(); }
+template <int KIND, int BS>
+constexpr bool decode_pipe_ok() { return KIND == kBF16 && BS >= kChunk; }
 // LDS bytes of the wave merge: per wave, G maxima, G sums and G x D partial
 // outputs.
 __host__ __device__ constexpr int merge_lds_bytes(int waves, int G, int D) {
@@ -36,8 +44,9 @@ __host__ __device__ constexpr int merge_lds_bytes(int waves, int G, int D) {
 // The body of decode_partition_kernel for workgroup `bid` of `nblocks`, with
 // `lds` the launch's dynamic LDS (at least merge_lds_bytes(W, G, D) bytes):
 // also run by the workgroups of the shared-prefix launch that do the
-// private partitions.
-template <int KIND, int D, int BS, int W, bool NT>
+// private partitions.  PIPE: each wave keeps the loads of its next chunk in
+// flight while it computes the current one.
+template <int KIND, int D, int BS, int W, bool NT, bool PIPE = false>
 __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, const DecodeArgs& a, int bid,
                                                       int nblocks, float* lds) {
   using GG = Geo<KIND, D, BS>;
@@ -357,27 +366,61 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
       }
     }
   };
-  // The block of the next chunk is fetched one chunk ahead of its loads (an
-  // index clamped into the partition rather than a branch).
   uint4 kbuf[NX];
   VOp vbuf[NN];
   int c = ce - 1 - wave;
-  int64_t u_next = 0;
-  if constexpr (BS >= kChunk) u_next = block_of_chunk(max(c, cb));
-  if (c >= cb) {
-    const int64_t u = u_next;
-    if constexpr (BS >= kChunk) u_next = block_of_chunk(max(c - kWaves, cb));
-    load(c, u, kbuf, vbuf);
-    if (own_new()) patch_new(c, kbuf, vbuf);
-    process(std::true_type{}, c, kbuf, vbuf);
-    c -= kWaves;
-  }
-  while (c >= cb) {
-    const int64_t u = u_next;
-    if constexpr (BS >= kChunk) u_next = block_of_chunk(max(c - kWaves, cb));
-    load(c, u, kbuf, vbuf);
-    process(std::false_type{}, c, kbuf, vbuf);
-    c -= kWaves;
+  if constexpr (PIPE) {
+    static_assert(decode_pipe_ok<KIND, BS>(), "the pipeline needs whole chunks per block");
+    // Two operand sets, A (kbuf, vbuf) and B (kb2, vb2), used in turn: the
+    // loads of chunk c - W are issued before chunk c is computed.  Every
+    // branch below is taken after the loads it depends on were issued on all
+    // paths into it, so the wait before a chunk's arithmetic covers that
+    // chunk's loads and not the next ones.
+    uint4 kb2[NX];
+    VOp vb2[NN];
+    if (c >= cb) {
+      load(c, block_of_chunk(c), kbuf, vbuf);
+      if (c - kWaves >= cb) {
+        load(c - kWaves, block_of_chunk(c - kWaves), kb2, vb2);
+        if (own_new()) patch_new(c, kbuf, vbuf);
+        process(std::true_type{}, c, kbuf, vbuf);
+        c -= kWaves;
+        // here chunk c >= cb is in flight in B
+        while (true) {
+          if (c - kWaves < cb) { process(std::false_type{}, c, kb2, vb2); break; }
+          load(c - kWaves, block_of_chunk(c - kWaves), kbuf, vbuf);
+          process(std::false_type{}, c, kb2, vb2);
+          c -= kWaves;
+          if (c - kWaves < cb) { process(std::false_type{}, c, kbuf, vbuf); break; }
+          load(c - kWaves, block_of_chunk(c - kWaves), kb2, vb2);
+          process(std::false_type{}, c, kbuf, vbuf);
+          c -= kWaves;
+        }
+      } else {
+        if (own_new()) patch_new(c, kbuf, vbuf);
+        process(std::true_type{}, c, kbuf, vbuf);
+      }
+    }
+  } else {
+    // The block of the next chunk is fetched one chunk ahead of its loads (an
+    // index clamped into the partition rather than a branch).
+    int64_t u_next = 0;
+    if constexpr (BS >= kChunk) u_next = block_of_chunk(max(c, cb));
+    if (c >= cb) {
+      const int64_t u = u_next;
+      if constexpr (BS >= kChunk) u_next = block_of_chunk(max(c - kWaves, cb));
+      load(c, u, kbuf, vbuf);
+      if (own_new()) patch_new(c, kbuf, vbuf);
+      process(std::true_type{}, c, kbuf, vbuf);
+      c -= kWaves;
+    }
+    while (c >= cb) {
+      const int64_t u = u_next;
+      if constexpr (BS >= kChunk) u_next = block_of_chunk(max(c - kWaves, cb));
+      load(c, u, kbuf, vbuf);
+      process(std::false_type{}, c, kbuf, vbuf);
+      c -= kWaves;
+    }
   }
 
   // weight sum of head n over the wave's tokens, then merge the waves:

@@ -38,6 +38,9 @@
 //     second small kernel in partition order.  Every reduction order depends
 //     only on logical token positions, so results do not depend on which
 //     physical blocks hold the tokens, nor on paged vs contiguous storage;
+//   * grids of at most one wave per SIMD (a batch of one or two long
+//     contexts) keep two chunks' loads in flight per wave (two operand sets
+//     in registers); fuller grids hide the HBM latency with resident waves;
 //   * a launch split into partitions runs from a work plan (one small
 //     kernel): only partitions holding tokens, full ones first and each
 //     context's last one longest first, so that the grid holds no empty
@@ -61,12 +64,12 @@ constexpr int kMergeWaves = 4;   // merge rows per workgroup, one a wave
 constexpr int kMergeUnroll = 8;  // rows of up to this many partitions load all at once
 constexpr int kMaxGroup = 16;     // query heads per KV head the tile can hold
 
-template <int KIND, int D, int BS, int W, bool NT>
+template <int KIND, int D, int BS, int W, bool NT, bool PIPE>
 __global__ __launch_bounds__(W * kWave)
-__attribute__((amdgpu_waves_per_eu(decode_min_waves_per_eu<KIND, BS>())))
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<KIND, BS, PIPE>())))
 void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
   extern __shared__ float lds[];
-  decode_partition_body<KIND, D, BS, W, NT>(geo, a, blockIdx.x, gridDim.x, lds);
+  decode_partition_body<KIND, D, BS, W, NT, PIPE>(geo, a, blockIdx.x, gridDim.x, lds);
 }
 
 // Work plan of a launch split into partitions: plan[i] = {s * P + part, L_s}
@@ -358,18 +361,36 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CacheGeom g,
   }
 }
 
-template <int KIND, int D, int BS>
-hipError_t launch_decode_t(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
+template <int KIND, int D, int BS, bool PIPE>
+hipError_t launch_decode_p(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
   constexpr int W = kDecodeWaves;
   const int64_t nwork = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
   const int G = a.num_q_heads / g.num_kv_heads;
   if (a.streaming)
-    hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, true>), dim3(static_cast<uint32_t>(nwork)),
+    hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, true, PIPE>), dim3(static_cast<uint32_t>(nwork)),
                        dim3(W * kWave), merge_lds_bytes(W, G, D), st, g, a);
   else
-    hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, false>), dim3(static_cast<uint32_t>(nwork)),
+    hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, false, PIPE>), dim3(static_cast<uint32_t>(nwork)),
                        dim3(W * kWave), merge_lds_bytes(W, G, D), st, g, a);
   return hipGetLastError();
+}
+
+// Grids of at most kPipeMaxWaves waves (one per SIMD: a batch of one or two
+// long contexts) run the two-chunk pipeline: with one chunk in flight per
+// wave they wait out an HBM round trip per chunk.  Measured on MI355X,
+// Llama-3-8B shape: batch 1 x 8192 tokens 15.1 -> 13.5 us, batch 1 x 2048
+// 12.2 -> 10.3 us.  Fuller grids keep one chunk in flight (at two waves per
+// SIMD the pipeline gained 1-2% at batch 4-8 and lost 1.6% on the Yi-34B
+// share).
+constexpr int64_t kPipeMaxWaves = 1024;
+
+template <int KIND, int D, int BS>
+hipError_t launch_decode_t(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
+  if constexpr (decode_pipe_ok<KIND, BS>()) {
+    const int64_t nwork = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
+    if (a.plan == nullptr && nwork * kDecodeWaves <= kPipeMaxWaves) return launch_decode_p<KIND, D, BS, true>(g, a, st);
+  }
+  return launch_decode_p<KIND, D, BS, false>(g, a, st);
 }
 
 template <int D>

@@ -5,7 +5,8 @@ A runtime-indexed register array or an over-large live set silently sends
 values to scratch memory, which cut the decode rate by a third in one
 measured case.  Every decode kernel must use no scratch, and every bf16
 instantiation whose blocks hold at least one 16-token chunk (block 16 or 32,
-head_dim 64 or 128) must keep 4 waves per SIMD.
+head_dim 64 or 128) must keep 4 waves per SIMD; the two-chunk pipeline variant (launched only on
+grids of at most one wave per SIMD) must keep 2.
 """
 
 import os
@@ -68,13 +69,23 @@ def test_shared_prefix_kernels_use_no_scratch_and_keep_occupancy():
 def test_decode_kernels_use_no_scratch_and_keep_occupancy():
     kernels = _resources("kernels.hip")
     decode = {k: v for k, v in kernels.items() if "decode_partition_kernel" in k}
-    assert len(decode) == 2 * 2 * 3 * 2   # dtype x head_dim x block x streaming
+    # template arguments: <KIND, D, BS, W, NT, PIPE>, KIND 1 = bf16; the
+    # two-chunk pipeline exists for bf16 with blocks of 16 or 32
+    single = {k: v for k, v in decode.items() if re.search(r"ELb[01]ELb0EE", k)}
+    pipe = {k: v for k, v in decode.items() if re.search(r"ELb[01]ELb1EE", k)}
+    assert len(single) == 2 * 2 * 3 * 2   # dtype x head_dim x block x streaming
+    assert len(pipe) == 2 * 2 * 2         # head_dim x block x streaming
+    assert len(decode) == len(single) + len(pipe)
     for k, v in decode.items():
         assert v.get("ScratchSize", 0) == 0, (k, v)
         assert v.get("VGPRs Spill", 0) == 0, (k, v)
-    # template arguments: <KIND, D, BS, W, NT>, KIND 1 = bf16
-    bf16_big_blocks = {k: v for k, v in decode.items()
+    bf16_big_blocks = {k: v for k, v in single.items()
                        if re.search(r"ILi1ELi(64|128)ELi(16|32)ELi", k)}
     assert len(bf16_big_blocks) == 2 * 2 * 2
     for k, v in bf16_big_blocks.items():
         assert v["Occupancy"] >= 4, (k, v)
+    # the pipeline runs on grids of at most one wave per SIMD: two waves per
+    # SIMD of headroom
+    for k, v in pipe.items():
+        assert re.search(r"ILi1ELi(64|128)ELi(16|32)ELi", k), k
+        assert v["Occupancy"] >= 2, (k, v)
