@@ -40,6 +40,12 @@ constexpr bool decode_pipe_ok() { return KIND == kBF16 && BS >= kChunk; }
 __host__ __device__ constexpr int merge_lds_bytes(int waves, int G, int D) {
   return waves * G * (D + 2) * 4;
 }
+// LDS bytes after the merge area that a fused append stages its tail chunk in
+// (blocks of at least a chunk): the chunk's V tile rows (D x 16 tokens), the
+// two K rows that share the new row's 32-byte sectors, and the slot.
+__host__ __device__ constexpr int append_stage_bytes(int D, int elt) {
+  return D * 16 * elt + 2 * D * elt + 16;
+}
 
 // The body of decode_partition_kernel for workgroup `bid` of `nblocks`, with
 // `lds` the launch's dynamic LDS (at least merge_lds_bytes(W, G, D) bytes):
@@ -113,10 +119,9 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   //
   // Fused append: token L-1 arrives in new_k / new_v.  Wave 0 loads the row
   // into registers next to q, so its latency overlaps everything up to the
-  // first chunk, where selects put it into the operand registers; it keeps a
-  // copy in LDS and stores the row into the cache after its loop.  (Narrow
-  // row stores at the end cost less than writing the whole chunk back from
-  // the operand registers, whose writes would interleave with the reads.)
+  // first chunk, where selects put it into the operand registers; the
+  // stores into the cache come after the loop, from LDS.  (Stores issued
+  // during the loop, where they interleave with the reads, cost more.)
   // The row and the slot are loaded whatever the slot says: only their use
   // waits for the slot (a slot < 0 appends nothing and the cache is read as
   // it is), so no load of the workgroup's start waits on another.
@@ -141,6 +146,18 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   }
   // evaluated where it is used, so that only those uses wait for the slot
   auto own_new = [&]() -> bool { return last_new && slot_new >= 0; };
+  // With blocks of at least a chunk the new row is stored as whole 32-byte
+  // sectors: the tail chunk's V rows and the K row sharing each of the new
+  // row's K sectors, staged in LDS past the merge area as they were loaded
+  // (plus the new row), are written back after the loop, so every other
+  // byte goes back unchanged.  Partial-sector stores of the row alone cost
+  // 1.9 us of the 47 us launch on the Llama-3-8B batch-64 layer.
+  constexpr bool kWholeSectors = BS >= kChunk;
+  const bool wg_appends = a.new_k != nullptr && ce == nch;   // the same in every wave
+  char* stage = reinterpret_cast<char*>(lds) + merge_lds_bytes(kWaves, G, D);
+  char* stage_v = stage;                                    // [D][16] elements
+  char* stage_k = stage + D * kChunk * ELT;                 // [2][D] elements
+  int* stage_slot = reinterpret_cast<int*>(stage_k + 2 * D * ELT);
 
   // q operand: head n of the group, zero beyond G (the row address is
   // clamped to a head of this group so that it always exists)
@@ -243,9 +260,18 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
       kk[x].z = krow ? nk[x].z : kk[x].z;
       kk[x].w = krow ? nk[x].w : kk[x].w;
     }
-    if (krow) {
+    if constexpr (!kWholeSectors) {
+      if (krow) {
 #pragma unroll
-      for (int x = 0; x < NX; ++x) sm_new[x * 4 + j4] = nk[x];
+        for (int x = 0; x < NX; ++x) sm_new[x * 4 + j4] = nk[x];
+      }
+    } else {
+      // K rows o and o ^ 1 of the chunk (o = the new row), patched
+      if ((n >> 1) == (((L - 1) % kChunk) >> 1)) {
+#pragma unroll
+        for (int x = 0; x < NX; ++x)
+          *reinterpret_cast<uint4*>(stage_k + ((n & 1) * D * ELT) + (x * 4 + j4) * 16) = kk[x];
+      }
     }
     const int e = L - 1 - (c * kChunk + 4 * j4);
 #pragma unroll
@@ -262,7 +288,12 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
         vv[nb].w = e == 3 ? h : vv[nb].w;
       }
     }
-    if (e >= 0 && e < 4) {
+    if constexpr (kWholeSectors) {
+      // the chunk's V as loaded, with the new row: tokens 4*j4 .. 4*j4+3 of
+      // dim nb*16+n
+#pragma unroll
+      for (int nb = 0; nb < NN; ++nb) *reinterpret_cast<VOp*>(stage_v + ((nb * 16 + n) * kChunk + 4 * j4) * ELT) = vv[nb];
+    } else if (e >= 0 && e < 4) {
       char* nv_lds = reinterpret_cast<char*>(sm_new + kRowVec);
 #pragma unroll
       for (int nb = 0; nb < NN; ++nb) {
@@ -382,6 +413,7 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
       load(c, block_of_chunk(c), kbuf, vbuf);
       if (c - kWaves >= cb) {
         load(c - kWaves, block_of_chunk(c - kWaves), kb2, vb2);
+        if (kWholeSectors && last_new && lane == 0) *stage_slot = slot_new;
         if (own_new()) patch_new(c, kbuf, vbuf);
         process(std::true_type{}, c, kbuf, vbuf);
         c -= kWaves;
@@ -397,6 +429,7 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
           c -= kWaves;
         }
       } else {
+        if (kWholeSectors && last_new && lane == 0) *stage_slot = slot_new;
         if (own_new()) patch_new(c, kbuf, vbuf);
         process(std::true_type{}, c, kbuf, vbuf);
       }
@@ -410,6 +443,7 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
       const int64_t u = u_next;
       if constexpr (BS >= kChunk) u_next = block_of_chunk(max(c - kWaves, cb));
       load(c, u, kbuf, vbuf);
+      if (kWholeSectors && last_new && lane == 0) *stage_slot = slot_new;
       if (own_new()) patch_new(c, kbuf, vbuf);
       process(std::true_type{}, c, kbuf, vbuf);
       c -= kWaves;
@@ -465,9 +499,34 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
       }
     }
   }
+  if constexpr (kWholeSectors) {
+    // whole sectors from the staged chunk, by every thread: the chunk's D V
+    // rows (16 tokens each) and K rows o & ~1, o | 1 of every 16-byte piece
+    if (wg_appends) {
+      const int slot = *stage_slot;
+      if (slot >= 0) {
+        const int64_t u = slot / BS;
+        const int o = slot % BS;                 // row in the block
+        const int row0 = o - o % kChunk;          // the chunk's first row
+        const int64_t tile = static_cast<int64_t>(a.layer) * geo.layer_bytes + (u * hkv + kvh) * TILE;
+        constexpr int kVUnits = D * kChunk * ELT / 16;   // 16-byte units of the chunk's V
+        constexpr int kPerRow = kChunk * ELT / 16;        // units per dim row
+        for (int t = tid; t < kVUnits; t += kThreads) {
+          const int e = t / kPerRow, q = t % kPerRow;
+          *reinterpret_cast<uint4*>(geo.v_base + tile + (e * BS + row0) * ELT + q * 16) =
+              *reinterpret_cast<const uint4*>(stage_v + t * 16);
+        }
+        for (int t = tid; t < 2 * kRowVec; t += kThreads) {
+          const int r = t / kRowVec, q = t % kRowVec;   // row (o & ~1) + r, piece q
+          *reinterpret_cast<uint4*>(geo.k_base + tile + (q * BS + (o & ~1) + r) * 16) =
+              *reinterpret_cast<const uint4*>(stage_k + r * D * ELT + q * 16);
+        }
+      }
+    }
+  }
   // the appended row into the cache: K as 16-byte pieces, V element by
   // element ([D][BS] tiles)
-  if (own_new() && lane < kRowVec) {
+  if (!kWholeSectors && own_new() && lane < kRowVec) {
     constexpr int VE = GG::VE;
     const int slot = slot_new;
     const int q = lane;
