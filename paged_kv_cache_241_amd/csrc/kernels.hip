@@ -40,7 +40,9 @@
 //     physical blocks hold the tokens, nor on paged vs contiguous storage;
 //   * grids of at most one wave per SIMD (a batch of one or two long
 //     contexts) keep two chunks' loads in flight per wave (two operand sets
-//     in registers); fuller grids hide the HBM latency with resident waves;
+//     in registers); grids of at most two waves per SIMD let the waves that
+//     hold one chunk more than the others load their first two chunks
+//     together; fuller grids hide the HBM latency with resident waves;
 //   * a launch split into partitions runs from a work plan (one small
 //     kernel): only partitions holding tokens, full ones first and each
 //     context's last one longest first, so that the grid holds no empty
@@ -64,12 +66,12 @@ constexpr int kMergeWaves = 4;   // merge rows per workgroup, one a wave
 constexpr int kMergeUnroll = 8;  // rows of up to this many partitions load all at once
 constexpr int kMaxGroup = 16;     // query heads per KV head the tile can hold
 
-template <int KIND, int D, int BS, int W, bool NT, bool PIPE>
+template <int KIND, int D, int BS, int W, bool NT, bool PIPE, bool BAL = false>
 __global__ __launch_bounds__(W * kWave)
-__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<KIND, BS, PIPE>())))
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<KIND, BS, PIPE, BAL>())))
 void decode_partition_kernel(CacheGeom geo, DecodeArgs a) {
   extern __shared__ float lds[];
-  decode_partition_body<KIND, D, BS, W, NT, PIPE>(geo, a, blockIdx.x, gridDim.x, lds);
+  decode_partition_body<KIND, D, BS, W, NT, PIPE, BAL>(geo, a, blockIdx.x, gridDim.x, lds);
 }
 
 // Work plan of a launch split into partitions: plan[i] = {s * P + part, L_s}
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CacheGeom g,
   }
 }
 
-template <int KIND, int D, int BS, bool PIPE>
+template <int KIND, int D, int BS, bool PIPE, bool BAL = false>
 hipError_t launch_decode_p(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
   constexpr int W = kDecodeWaves;
   const int64_t nwork = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
@@ -369,10 +371,10 @@ hipError_t launch_decode_p(const CacheGeom& g, const DecodeArgs& a, hipStream_t 
   const size_t lds = static_cast<size_t>(merge_lds_bytes(W, G, D)) +
                      (a.new_k != nullptr && BS >= kChunk ? append_stage_bytes(D, g.elt) : 0);
   if (a.streaming)
-    hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, true, PIPE>), dim3(static_cast<uint32_t>(nwork)),
+    hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, true, PIPE, BAL>), dim3(static_cast<uint32_t>(nwork)),
                        dim3(W * kWave), lds, st, g, a);
   else
-    hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, false, PIPE>), dim3(static_cast<uint32_t>(nwork)),
+    hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, false, PIPE, BAL>), dim3(static_cast<uint32_t>(nwork)),
                        dim3(W * kWave), lds, st, g, a);
   return hipGetLastError();
 }
@@ -385,12 +387,19 @@ hipError_t launch_decode_p(const CacheGeom& g, const DecodeArgs& a, hipStream_t 
 // SIMD the pipeline gained 1-2% at batch 4-8 and lost 1.6% on the Yi-34B
 // share).
 constexpr int64_t kPipeMaxWaves = 1024;
+// Grids of at most two waves per SIMD (e.g. 64 sequences x 8 KV heads, one
+// partition each) run the balanced start: its first step holds a second
+// operand set (141 VGPRs, three waves per SIMD, more than such a grid
+// places), which four waves per SIMD could not afford.
+constexpr int64_t kBalancedMaxWaves = 2048;
 
 template <int KIND, int D, int BS>
 hipError_t launch_decode_t(const CacheGeom& g, const DecodeArgs& a, hipStream_t st) {
   if constexpr (decode_pipe_ok<KIND, BS>()) {
     const int64_t nwork = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
     if (a.plan == nullptr && nwork * kDecodeWaves <= kPipeMaxWaves) return launch_decode_p<KIND, D, BS, true>(g, a, st);
+    if (a.plan == nullptr && nwork * kDecodeWaves <= kBalancedMaxWaves)
+      return launch_decode_p<KIND, D, BS, false, true>(g, a, st);
   }
   return launch_decode_p<KIND, D, BS, false>(g, a, st);
 }

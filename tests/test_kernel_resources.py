@@ -6,7 +6,8 @@ values to scratch memory, which cut the decode rate by a third in one
 measured case.  Every decode kernel must use no scratch, and every bf16
 instantiation whose blocks hold at least one 16-token chunk (block 16 or 32,
 head_dim 64 or 128) must keep 4 waves per SIMD; the two-chunk pipeline variant (launched only on
-grids of at most one wave per SIMD) must keep 2.
+grids of at most one wave per SIMD) and the balanced-start variant (at most
+two) must keep 2.
 """
 
 import os
@@ -71,11 +72,14 @@ def test_decode_kernels_use_no_scratch_and_keep_occupancy():
     decode = {k: v for k, v in kernels.items() if "decode_partition_kernel" in k}
     # template arguments: <KIND, D, BS, W, NT, PIPE>, KIND 1 = bf16; the
     # two-chunk pipeline exists for bf16 with blocks of 16 or 32
-    single = {k: v for k, v in decode.items() if re.search(r"ELb[01]ELb0EE", k)}
-    pipe = {k: v for k, v in decode.items() if re.search(r"ELb[01]ELb1EE", k)}
+    # <KIND, D, BS, W, NT, PIPE, BAL>
+    single = {k: v for k, v in decode.items() if re.search(r"ELb[01]ELb0ELb0EE", k)}
+    pipe = {k: v for k, v in decode.items() if re.search(r"ELb[01]ELb1ELb0EE", k)}
+    balanced = {k: v for k, v in decode.items() if re.search(r"ELb[01]ELb0ELb1EE", k)}
     assert len(single) == 2 * 2 * 3 * 2   # dtype x head_dim x block x streaming
     assert len(pipe) == 2 * 2 * 2         # head_dim x block x streaming
-    assert len(decode) == len(single) + len(pipe)
+    assert len(balanced) == 2 * 2 * 2
+    assert len(decode) == len(single) + len(pipe) + len(balanced)
     for k, v in decode.items():
         assert v.get("ScratchSize", 0) == 0, (k, v)
         assert v.get("VGPRs Spill", 0) == 0, (k, v)
@@ -87,5 +91,9 @@ def test_decode_kernels_use_no_scratch_and_keep_occupancy():
     # the pipeline runs on grids of at most one wave per SIMD: two waves per
     # SIMD of headroom
     for k, v in pipe.items():
+        assert re.search(r"ILi1ELi(64|128)ELi(16|32)ELi", k), k
+        assert v["Occupancy"] >= 2, (k, v)
+    # the balanced start runs on grids of at most two waves per SIMD
+    for k, v in balanced.items():
         assert re.search(r"ILi1ELi(64|128)ELi(16|32)ELi", k), k
         assert v["Occupancy"] >= 2, (k, v)
