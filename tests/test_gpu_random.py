@@ -145,3 +145,15 @@ def test_large_ragged_batch(seed):
     pt = int(rng.choice([0, 0, 256, 512, 1024])) // unit * unit
     rows = sorted(set([0, B - 1, int(np.argmax(lens))] + [int(x) for x in rng.choice(B, 8, replace=False)]))
     _run(rng, hkv, G, 128, bs, dtype, layout, lens, pt, fused, max_seq_len=8192, check_rows=rows)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_balanced_start_band_all_rows(fused):
+    # 48 sequences x 8 KV heads, one partition each: 384 workgroups, 1536
+    # waves, the band that runs the balanced start.  Contexts of 900-1100
+    # tokens give every chunk count modulo 4, so one, two or three waves
+    # load their first two chunks together; every row is checked.
+    rng = np.random.default_rng(4848 + fused)
+    lens = rng.integers(900, 1101, 48).astype(np.int64)
+    lens[:4] = [1024, 1025, 1041, 1057]   # 64, 65, 66 and 67 chunks
+    _run(rng, 8, 4, 128, 16, "bf16", "paged", lens, 0, fused, max_seq_len=2048)
