@@ -382,7 +382,10 @@ pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dt
  *               < 0: sequence s appends nothing (its cache is read as is).
  * The other arguments, the result and the errors are those of pa_decode.  The
  * cache afterwards equals pa_append_kv's; the output equals pa_decode's after
- * that append, bit for bit. */
+ * that append, bit for bit.  With blocks of 16 or more tokens the launch
+ * stores whole 32-byte sectors: it rewrites the 16 token rows around each new
+ * token (every other row with the bytes it read from it earlier in the same
+ * launch), so nothing else may write those rows while the launch runs. */
 pa_status pa_append_decode(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
                            const int32_t* d_slots, const void* d_q, pa_dtype q_dtype,
                            int32_t num_q_heads, float scale, const int32_t* d_block_tables,
