@@ -415,9 +415,12 @@ def test_fused_append_decode_equals_separate_calls(cid, over, layout, pt):
         assert fus.pool.stats()["cow_copies"] == (cfg.batch // cfg.samples) * (cfg.samples - 1)
 
 
-def test_fused_append_skips_negative_slots():
-    cfg = W.get(2, batch=5, num_blocks=5 * 64 + 5)
-    case = Case(cfg, step_append=False)
+@pytest.mark.parametrize("batch", [5, 48])
+def test_fused_append_skips_negative_slots(batch):
+    # batch 5: the small-grid pipeline; 48 x 8 KV heads: the balanced start
+    cfg = W.get(2, batch=batch, num_blocks=batch * 64 + batch)
+    case = Case(cfg, step_append=False, fill=0.0)
+    ref = Case(cfg, step_append=False, fill=0.0)
     k, v = case.step_kv()
     slots = case.step_slots.clone()
     # sequences 1 and 3 get their token through a separate append first
@@ -427,3 +430,8 @@ def test_fused_append_skips_negative_slots():
     slots[3] = -1
     out = case.decode(append=(k, v, slots))
     _check(case, out, range(cfg.batch))
+    # the caches hold every new row exactly once and nothing else changed:
+    # the same bytes as separate appends of all rows
+    ref.pool.append_kv(0, k, v, ref.step_slots)
+    assert torch.equal(case.pool.k_cache, ref.pool.k_cache)
+    assert torch.equal(case.pool.v_cache, ref.pool.v_cache)
