@@ -395,6 +395,13 @@ def test_append_and_decode_over_several_layers():
     (4, {"batch": 5, "num_blocks": 400}, "contiguous", 0),
     (5, {"batch": 16, "prompt_len": 300, "private_len": 1, "num_blocks": 300}, "paged", 128),
     (1, {"kv_dtype": "f32"}, "paged", 0),
+    # 8-token blocks (the row stored alone) and 32-token blocks (half a block
+    # rewritten in whole sectors)
+    (2, {"batch": 6, "num_blocks": 2 * (6 * 64 + 9), "block_size": 8}, "paged", 0),
+    (2, {"batch": 6, "num_blocks": 6 * 32 + 9, "block_size": 32}, "paged", 0),
+    # the balanced start (48 x 8 workgroups) and a planned split launch
+    (2, {"batch": 48, "num_blocks": 48 * 64 + 48}, "paged", 0),
+    (3, {"batch": 64}, "paged", 256),
 ])
 def test_fused_append_decode_equals_separate_calls(cid, over, layout, pt):
     cfg = W.get(cid, **over)
