@@ -81,7 +81,8 @@ typedef enum pa_status {
   PA_ERR_UNKNOWN_SEQ = -4,   /* request id is not live */
   PA_ERR_WORKSPACE = -5,     /* decode workspace missing or too small */
   PA_ERR_HIP = -6,           /* a HIP call failed (launch error) */
-  PA_ERR_UNSUPPORTED = -7    /* valid request this build has no kernel for */
+  PA_ERR_UNSUPPORTED = -7,   /* valid request this build has no kernel for */
+  PA_ERR_NO_MEMORY = -8      /* the library's host-side state could not be allocated */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;

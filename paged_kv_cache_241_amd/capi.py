@@ -23,6 +23,7 @@ PA_ERR_UNKNOWN_SEQ = -4
 PA_ERR_WORKSPACE = -5
 PA_ERR_HIP = -6
 PA_ERR_UNSUPPORTED = -7
+PA_ERR_NO_MEMORY = -8
 
 PA_F32 = 0
 PA_BF16 = 1
@@ -33,7 +34,7 @@ STATUS_NAMES = {
     PA_OK: "PA_OK", PA_ERR_INVALID_ARG: "PA_ERR_INVALID_ARG", PA_ERR_NO_BLOCKS: "PA_ERR_NO_BLOCKS",
     PA_ERR_NO_REQ_ID: "PA_ERR_NO_REQ_ID", PA_ERR_UNKNOWN_SEQ: "PA_ERR_UNKNOWN_SEQ",
     PA_ERR_WORKSPACE: "PA_ERR_WORKSPACE", PA_ERR_HIP: "PA_ERR_HIP",
-    PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED",
+    PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED", PA_ERR_NO_MEMORY: "PA_ERR_NO_MEMORY",
 }
 
 # every function include/pa.h declares

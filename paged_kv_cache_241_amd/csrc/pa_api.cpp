@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <exception>
 #include <cstdint>
 #include <new>
 #include <string>
@@ -34,6 +35,22 @@ thread_local std::string g_err;
 pa_status fail(pa_status st, const std::string& msg) {
   g_err = msg;
   return st;
+}
+
+// Every pa_status entry point runs its body through guarded(): nothing
+// throws across the C ABI.  A failed host allocation (the allocator's tables,
+// error text) becomes PA_ERR_NO_MEMORY, anything else PA_ERR_INVALID_ARG.
+template <class F>
+pa_status guarded(const char* who, F&& body) {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return fail(PA_ERR_NO_MEMORY, std::string(who) + ": out of host memory");
+  } catch (const std::exception& e) {
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": " + e.what());
+  } catch (...) {
+    return fail(PA_ERR_INVALID_ARG, std::string(who) + ": unexpected error");
+  }
 }
 
 pa_status from_alloc(pa::Status st, const std::string& msg) {
@@ -198,250 +215,284 @@ size_t pa_bytes_per_token(const pa_pool_desc* desc) {
 
 pa_status pa_create_pool(const pa_pool_desc* desc, void* d_k_cache, void* d_v_cache,
                          pa_pool** out) {
-  if (out == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool: null output");
-  *out = nullptr;
-  const std::string why = check_desc(desc);
-  if (!why.empty()) return fail(PA_ERR_INVALID_ARG, "create_pool: " + why);
-  if (d_k_cache == nullptr || d_v_cache == nullptr)
-    return fail(PA_ERR_INVALID_ARG, "create_pool: null cache pointer");
-  if ((reinterpret_cast<uintptr_t>(d_k_cache) | reinterpret_cast<uintptr_t>(d_v_cache)) & 15)
-    return fail(PA_ERR_INVALID_ARG, "create_pool: caches must be 16-byte aligned");
-  pa_pool* p = new (std::nothrow) pa_pool(*desc, make_geom(desc, d_k_cache, d_v_cache));
-  if (p == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool: out of host memory");
-  *out = p;
-  return PA_OK;
+  return guarded("create_pool", [&]() -> pa_status {
+    if (out == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool: null output");
+    *out = nullptr;
+    const std::string why = check_desc(desc);
+    if (!why.empty()) return fail(PA_ERR_INVALID_ARG, "create_pool: " + why);
+    if (d_k_cache == nullptr || d_v_cache == nullptr)
+      return fail(PA_ERR_INVALID_ARG, "create_pool: null cache pointer");
+    if ((reinterpret_cast<uintptr_t>(d_k_cache) | reinterpret_cast<uintptr_t>(d_v_cache)) & 15)
+      return fail(PA_ERR_INVALID_ARG, "create_pool: caches must be 16-byte aligned");
+    pa_pool* p = new (std::nothrow) pa_pool(*desc, make_geom(desc, d_k_cache, d_v_cache));
+    if (p == nullptr) return fail(PA_ERR_NO_MEMORY, "create_pool: out of host memory");
+    *out = p;
+    return PA_OK;
+  });
 }
 
 pa_status pa_create_pool_vmm(const pa_pool_desc* desc, size_t physical_bytes, pa_pool** out) {
-  if (out == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool_vmm: null output");
-  *out = nullptr;
-  const std::string why = check_desc(desc);
-  if (!why.empty()) return fail(PA_ERR_INVALID_ARG, "create_pool_vmm: " + why);
-  if (desc->layout != PA_CONTIGUOUS)
-    return fail(PA_ERR_INVALID_ARG, "create_pool_vmm: demand paging backs the contiguous layout");
-  int device = 0;
-  hipError_t e = hipGetDevice(&device);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(PA_ERR_HIP, std::string("create_pool_vmm: ") + hipGetErrorString(e));
-  }
-  const int64_t region = layer_bytes(desc) / desc->max_seqs;
-  pa::VirtualCache* vc = nullptr;
-  const std::string err =
-      pa::VirtualCache::create(desc->num_layers, desc->max_seqs, region, physical_bytes, device, &vc);
-  if (!err.empty()) return fail(PA_ERR_UNSUPPORTED, "create_pool_vmm: " + err);
-  pa_pool* p = new (std::nothrow) pa_pool(*desc, make_geom(desc, vc->k_base(), vc->v_base()));
-  if (p == nullptr) {
-    delete vc;
-    return fail(PA_ERR_INVALID_ARG, "create_pool_vmm: out of host memory");
-  }
-  p->vmm = vc;
-  *out = p;
-  return PA_OK;
+  return guarded("create_pool_vmm", [&]() -> pa_status {
+    if (out == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool_vmm: null output");
+    *out = nullptr;
+    const std::string why = check_desc(desc);
+    if (!why.empty()) return fail(PA_ERR_INVALID_ARG, "create_pool_vmm: " + why);
+    if (desc->layout != PA_CONTIGUOUS)
+      return fail(PA_ERR_INVALID_ARG, "create_pool_vmm: demand paging backs the contiguous layout");
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_HIP, std::string("create_pool_vmm: ") + hipGetErrorString(e));
+    }
+    const int64_t region = layer_bytes(desc) / desc->max_seqs;
+    pa::VirtualCache* vc = nullptr;
+    const std::string err =
+        pa::VirtualCache::create(desc->num_layers, desc->max_seqs, region, physical_bytes, device, &vc);
+    if (!err.empty()) return fail(PA_ERR_UNSUPPORTED, "create_pool_vmm: " + err);
+    pa_pool* p = new (std::nothrow) pa_pool(*desc, make_geom(desc, vc->k_base(), vc->v_base()));
+    if (p == nullptr) {
+      delete vc;
+      return fail(PA_ERR_NO_MEMORY, "create_pool_vmm: out of host memory");
+    }
+    p->vmm = vc;
+    *out = p;
+    return PA_OK;
+  });
 }
 
 pa_status pa_vmm_info(const pa_pool* pool, pa_vmm_stats* out) {
-  if (pool == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_info: null argument");
-  if (pool->vmm == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_info: not a demand-paged pool");
-  out->page_bytes = pool->vmm->page_bytes();
-  out->mapped_bytes = pool->vmm->bytes_mapped();
-  out->budget_bytes = pool->vmm->bytes_budget();
-  out->region_bytes = pool->vmm->region_bytes();
-  return PA_OK;
+  return guarded("vmm_info", [&]() -> pa_status {
+    if (pool == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_info: null argument");
+    if (pool->vmm == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_info: not a demand-paged pool");
+    out->page_bytes = pool->vmm->page_bytes();
+    out->mapped_bytes = pool->vmm->bytes_mapped();
+    out->budget_bytes = pool->vmm->bytes_budget();
+    out->region_bytes = pool->vmm->region_bytes();
+    return PA_OK;
+  });
 }
 
 pa_status pa_vmm_trim(pa_pool* pool, int64_t* freed_bytes_out) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_trim: null pool");
-  if (pool->vmm == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_trim: not a demand-paged pool");
-  const int64_t before = pool->vmm->bytes_mapped();
-  for (int32_t r = 0; r < pool->desc.max_seqs; ++r) {
-    int32_t len = 0;
-    if (!pool->alloc.length(r, &len)) pool->vmm->trim(r);
-  }
-  if (freed_bytes_out) *freed_bytes_out = before - pool->vmm->bytes_mapped();
-  return PA_OK;
+  return guarded("vmm_trim", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_trim: null pool");
+    if (pool->vmm == nullptr) return fail(PA_ERR_INVALID_ARG, "vmm_trim: not a demand-paged pool");
+    const int64_t before = pool->vmm->bytes_mapped();
+    for (int32_t r = 0; r < pool->desc.max_seqs; ++r) {
+      int32_t len = 0;
+      if (!pool->alloc.length(r, &len)) pool->vmm->trim(r);
+    }
+    if (freed_bytes_out) *freed_bytes_out = before - pool->vmm->bytes_mapped();
+    return PA_OK;
+  });
 }
 
 pa_status pa_destroy_pool(pa_pool* pool) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "destroy_pool: null pool");
-  delete pool;
-  return PA_OK;
+  return guarded("destroy_pool", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "destroy_pool: null pool");
+    delete pool;
+    return PA_OK;
+  });
 }
 
 pa_status pa_set_free_order(pa_pool* pool, const int32_t* block_ids, int32_t n) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "set_free_order: null pool");
-  std::string err;
-  pa::Status st = pool->alloc.set_free_order(block_ids, n, &err);
-  return from_alloc(st, err);
+  return guarded("set_free_order", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "set_free_order: null pool");
+    std::string err;
+    pa::Status st = pool->alloc.set_free_order(block_ids, n, &err);
+    return from_alloc(st, err);
+  });
 }
 
 pa_status pa_seq_add(pa_pool* pool, int32_t* req_id_out) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "seq_add: null pool");
-  std::string err;
-  pa::Status st = pool->alloc.add(req_id_out, &err);
-  return from_alloc(st, err);
+  return guarded("seq_add", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "seq_add: null pool");
+    std::string err;
+    pa::Status st = pool->alloc.add(req_id_out, &err);
+    return from_alloc(st, err);
+  });
 }
 
 pa_status pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* child_out) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "seq_fork: null pool");
-  std::string err;
-  pa::Status st = pool->alloc.fork(parent, child_out, &err);
-  return from_alloc(st, err);
+  return guarded("seq_fork", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "seq_fork: null pool");
+    std::string err;
+    pa::Status st = pool->alloc.fork(parent, child_out, &err);
+    return from_alloc(st, err);
+  });
 }
 
 pa_status pa_seq_free(pa_pool* pool, int32_t req_id) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "seq_free: null pool");
-  std::string err;
-  pa::Status st = pool->alloc.free_seq(req_id, &err);
-  return from_alloc(st, err);
+  return guarded("seq_free", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "seq_free: null pool");
+    std::string err;
+    pa::Status st = pool->alloc.free_seq(req_id, &err);
+    return from_alloc(st, err);
+  });
 }
 
 pa_status pa_reserve(pa_pool* pool, const int32_t* req_ids, int32_t n, const int32_t* counts,
                      int32_t* slots_out, int64_t slots_cap, int32_t* cow_pairs_out,
                      int32_t cow_cap, int32_t* n_cow_out) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "reserve: null pool");
-  std::string err;
-  if (pool->vmm != nullptr) {
-    // demand paging: back every listed request's grown prefix first, all or
-    // nothing against the physical budget
-    int64_t total = 0;
-    pa::Status st = pool->alloc.check_growth(req_ids, n, counts, &total, &err);
-    if (st != pa::kOk) return from_alloc(st, err);
-    if (total > slots_cap || (total > 0 && slots_out == nullptr))
-      return fail(PA_ERR_INVALID_ARG, "reserve: slots_out holds " + std::to_string(slots_cap) +
-                                          " slots, " + std::to_string(total) + " needed");
-    const int64_t unit = static_cast<int64_t>(pool->desc.num_kv_heads) * pool->desc.head_dim *
-                         pool->desc.block_size * elt_bytes(pool->desc.kv_dtype);
-    std::vector<int64_t> bytes(n);
-    int64_t more = 0;
-    for (int32_t i = 0; i < n; ++i) {
-      int32_t len = 0;
-      pool->alloc.length(req_ids[i], &len);
-      const int64_t grown = static_cast<int64_t>(len) + (counts ? counts[i] : 1);
-      bytes[i] = (grown + pool->desc.block_size - 1) / pool->desc.block_size * unit;
-      more += pool->vmm->bytes_short(req_ids[i], bytes[i]);
+  return guarded("reserve", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "reserve: null pool");
+    std::string err;
+    if (pool->vmm != nullptr) {
+      // demand paging: back every listed request's grown prefix first, all or
+      // nothing against the physical budget
+      int64_t total = 0;
+      pa::Status st = pool->alloc.check_growth(req_ids, n, counts, &total, &err);
+      if (st != pa::kOk) return from_alloc(st, err);
+      if (total > slots_cap || (total > 0 && slots_out == nullptr))
+        return fail(PA_ERR_INVALID_ARG, "reserve: slots_out holds " + std::to_string(slots_cap) +
+                                            " slots, " + std::to_string(total) + " needed");
+      const int64_t unit = static_cast<int64_t>(pool->desc.num_kv_heads) * pool->desc.head_dim *
+                           pool->desc.block_size * elt_bytes(pool->desc.kv_dtype);
+      std::vector<int64_t> bytes(n);
+      int64_t more = 0;
+      for (int32_t i = 0; i < n; ++i) {
+        int32_t len = 0;
+        pool->alloc.length(req_ids[i], &len);
+        const int64_t grown = static_cast<int64_t>(len) + (counts ? counts[i] : 1);
+        bytes[i] = (grown + pool->desc.block_size - 1) / pool->desc.block_size * unit;
+        more += pool->vmm->bytes_short(req_ids[i], bytes[i]);
+      }
+      if (more > pool->vmm->bytes_free())
+        return fail(PA_ERR_NO_BLOCKS, "reserve: needs " + std::to_string(more) +
+                                          " more bytes of physical memory, " +
+                                          std::to_string(pool->vmm->bytes_free()) + " left");
+      for (int32_t i = 0; i < n; ++i) {
+        const std::string e = pool->vmm->grow(req_ids[i], bytes[i]);
+        if (!e.empty()) return fail(PA_ERR_HIP, "reserve: " + e);
+      }
     }
-    if (more > pool->vmm->bytes_free())
-      return fail(PA_ERR_NO_BLOCKS, "reserve: needs " + std::to_string(more) +
-                                        " more bytes of physical memory, " +
-                                        std::to_string(pool->vmm->bytes_free()) + " left");
-    for (int32_t i = 0; i < n; ++i) {
-      const std::string e = pool->vmm->grow(req_ids[i], bytes[i]);
-      if (!e.empty()) return fail(PA_ERR_HIP, "reserve: " + e);
-    }
-  }
-  pa::Status st = pool->alloc.reserve(req_ids, n, counts, slots_out, slots_cap, cow_pairs_out,
-                                      cow_cap, n_cow_out, &err);
-  return from_alloc(st, err);
+    pa::Status st = pool->alloc.reserve(req_ids, n, counts, slots_out, slots_cap, cow_pairs_out,
+                                        cow_cap, n_cow_out, &err);
+    return from_alloc(st, err);
+  });
 }
 
 pa_status pa_get_block_tables(const pa_pool* pool, const int32_t* req_ids, int32_t n,
                               int32_t stride, int32_t* tables_out, int32_t* lens_out) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "get_block_tables: null pool");
-  std::string err;
-  pa::Status st = pool->alloc.tables(req_ids, n, stride, tables_out, lens_out, &err);
-  return from_alloc(st, err);
+  return guarded("get_block_tables", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "get_block_tables: null pool");
+    std::string err;
+    pa::Status st = pool->alloc.tables(req_ids, n, stride, tables_out, lens_out, &err);
+    return from_alloc(st, err);
+  });
 }
 
 pa_status pa_get_stats(const pa_pool* pool, pa_stats* out) {
-  if (pool == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARG, "get_stats: null argument");
-  const pa::AllocStats s = pool->alloc.stats();
-  out->free_blocks = s.free_blocks;
-  out->used_blocks = s.used_blocks;
-  out->tokens = s.tokens;
-  out->logical_tokens = s.logical_tokens;
-  out->reserved_tokens = s.reserved_tokens;
-  out->live_seqs = s.live_seqs;
-  out->cow_copies = s.cow_copies;
-  out->shared_blocks = s.shared_blocks;
-  out->utilisation = s.utilisation;
-  out->swapped_seqs = s.swapped_seqs;
-  out->swapped_tokens = s.swapped_tokens;
-  return PA_OK;
+  return guarded("get_stats", [&]() -> pa_status {
+    if (pool == nullptr || out == nullptr) return fail(PA_ERR_INVALID_ARG, "get_stats: null argument");
+    const pa::AllocStats s = pool->alloc.stats();
+    out->free_blocks = s.free_blocks;
+    out->used_blocks = s.used_blocks;
+    out->tokens = s.tokens;
+    out->logical_tokens = s.logical_tokens;
+    out->reserved_tokens = s.reserved_tokens;
+    out->live_seqs = s.live_seqs;
+    out->cow_copies = s.cow_copies;
+    out->shared_blocks = s.shared_blocks;
+    out->utilisation = s.utilisation;
+    out->swapped_seqs = s.swapped_seqs;
+    out->swapped_tokens = s.swapped_tokens;
+    return PA_OK;
+  });
 }
 
 pa_status pa_swap_bytes(const pa_pool* pool, int32_t req_id, size_t* bytes_out) {
-  if (pool == nullptr || bytes_out == nullptr) return fail(PA_ERR_INVALID_ARG, "swap_bytes: null argument");
-  int32_t len = 0;
-  pa_status st = swap_length(pool, req_id, "swap_bytes", &len);
-  if (st != PA_OK) return st;
-  *bytes_out = image_bytes(pool, len);
-  return PA_OK;
+  return guarded("swap_bytes", [&]() -> pa_status {
+    if (pool == nullptr || bytes_out == nullptr) return fail(PA_ERR_INVALID_ARG, "swap_bytes: null argument");
+    int32_t len = 0;
+    pa_status st = swap_length(pool, req_id, "swap_bytes", &len);
+    if (st != PA_OK) return st;
+    *bytes_out = image_bytes(pool, len);
+    return PA_OK;
+  });
 }
 
 pa_status pa_swap_out(pa_pool* pool, int32_t req_id, void* d_image, size_t image_bytes_cap,
                       void* stream) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "swap_out: null pool");
-  std::vector<int32_t> blocks;
-  int32_t len = 0;
-  std::string err;
-  pa::Status s = pool->alloc.swap_out_blocks(req_id, &blocks, &len, &err);
-  if (s != pa::kOk) return fail(static_cast<pa_status>(s), "swap_out: " + err);
-  char* dev = nullptr;
-  pa_status st = check_image(pool, d_image, image_bytes_cap, len, "swap_out", &dev);
-  if (st != PA_OK) return st;
-  if (dev != nullptr) {
-    hipError_t e = pa::launch_swap(pool->geom, blocks.data(), static_cast<int32_t>(blocks.size()),
-                                   dev, true, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("swap_out: ") + hipGetErrorString(e));
-  }
-  s = pool->alloc.swap_out(req_id, &err);
-  if (s != pa::kOk) return fail(static_cast<pa_status>(s), "swap_out: " + err);
-  return PA_OK;
+  return guarded("swap_out", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "swap_out: null pool");
+    std::vector<int32_t> blocks;
+    int32_t len = 0;
+    std::string err;
+    pa::Status s = pool->alloc.swap_out_blocks(req_id, &blocks, &len, &err);
+    if (s != pa::kOk) return fail(static_cast<pa_status>(s), "swap_out: " + err);
+    char* dev = nullptr;
+    pa_status st = check_image(pool, d_image, image_bytes_cap, len, "swap_out", &dev);
+    if (st != PA_OK) return st;
+    if (dev != nullptr) {
+      hipError_t e = pa::launch_swap(pool->geom, blocks.data(), static_cast<int32_t>(blocks.size()),
+                                     dev, true, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("swap_out: ") + hipGetErrorString(e));
+    }
+    s = pool->alloc.swap_out(req_id, &err);
+    if (s != pa::kOk) return fail(static_cast<pa_status>(s), "swap_out: " + err);
+    return PA_OK;
+  });
 }
 
 pa_status pa_swap_in(pa_pool* pool, int32_t req_id, const void* d_image, size_t image_bytes_cap,
                      void* stream) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "swap_in: null pool");
-  int32_t len = 0;
-  pa_status st = swap_length(pool, req_id, "swap_in", &len);
-  if (st != PA_OK) return st;
-  if (!pool->alloc.swapped(req_id))
-    return fail(PA_ERR_INVALID_ARG, "swap_in: request " + std::to_string(req_id) + " is not swapped out");
-  char* dev = nullptr;
-  st = check_image(pool, d_image, image_bytes_cap, len, "swap_in", &dev);
-  if (st != PA_OK) return st;
-  std::vector<int32_t> blocks;
-  std::string err;
-  pa::Status s = pool->alloc.swap_in(req_id, &blocks, &err);
-  if (s != pa::kOk) return fail(static_cast<pa_status>(s), "swap_in: " + err);
-  if (dev != nullptr) {
-    hipError_t e = pa::launch_swap(pool->geom, blocks.data(), static_cast<int32_t>(blocks.size()),
-                                   dev, false, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) {
-      pool->alloc.swap_in_undo(req_id);
-      return fail(PA_ERR_HIP, std::string("swap_in: ") + hipGetErrorString(e));
+  return guarded("swap_in", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "swap_in: null pool");
+    int32_t len = 0;
+    pa_status st = swap_length(pool, req_id, "swap_in", &len);
+    if (st != PA_OK) return st;
+    if (!pool->alloc.swapped(req_id))
+      return fail(PA_ERR_INVALID_ARG, "swap_in: request " + std::to_string(req_id) + " is not swapped out");
+    char* dev = nullptr;
+    st = check_image(pool, d_image, image_bytes_cap, len, "swap_in", &dev);
+    if (st != PA_OK) return st;
+    std::vector<int32_t> blocks;
+    std::string err;
+    pa::Status s = pool->alloc.swap_in(req_id, &blocks, &err);
+    if (s != pa::kOk) return fail(static_cast<pa_status>(s), "swap_in: " + err);
+    if (dev != nullptr) {
+      hipError_t e = pa::launch_swap(pool->geom, blocks.data(), static_cast<int32_t>(blocks.size()),
+                                     dev, false, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) {
+        pool->alloc.swap_in_undo(req_id);
+        return fail(PA_ERR_HIP, std::string("swap_in: ") + hipGetErrorString(e));
+      }
     }
-  }
-  return PA_OK;
+    return PA_OK;
+  });
 }
 
 pa_status pa_copy_blocks(pa_pool* pool, const int32_t* d_pairs, int32_t n, void* stream) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "copy_blocks: null pool");
-  if (n < 0) return fail(PA_ERR_INVALID_ARG, "copy_blocks: negative pair count");
-  if (n == 0) return PA_OK;
-  if (!pool->geom.paged) return fail(PA_ERR_INVALID_ARG, "copy_blocks: contiguous pool has no blocks");
-  if (d_pairs == nullptr) return fail(PA_ERR_INVALID_ARG, "copy_blocks: null pairs");
-  hipError_t e = pa::launch_copy_blocks(pool->geom, d_pairs, n, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("copy_blocks: ") + hipGetErrorString(e));
-  return PA_OK;
+  return guarded("copy_blocks", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "copy_blocks: null pool");
+    if (n < 0) return fail(PA_ERR_INVALID_ARG, "copy_blocks: negative pair count");
+    if (n == 0) return PA_OK;
+    if (!pool->geom.paged) return fail(PA_ERR_INVALID_ARG, "copy_blocks: contiguous pool has no blocks");
+    if (d_pairs == nullptr) return fail(PA_ERR_INVALID_ARG, "copy_blocks: null pairs");
+    hipError_t e = pa::launch_copy_blocks(pool->geom, d_pairs, n, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("copy_blocks: ") + hipGetErrorString(e));
+    return PA_OK;
+  });
 }
 
 pa_status pa_append_kv(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
                        const int32_t* d_slots, int32_t n, void* stream) {
-  if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "append_kv: null pool");
-  if (layer < 0 || layer >= pool->desc.num_layers)
-    return fail(PA_ERR_INVALID_ARG, "append_kv: layer out of range");
-  if (n < 0) return fail(PA_ERR_INVALID_ARG, "append_kv: negative token count");
-  if (n == 0) return PA_OK;
-  if (d_k == nullptr || d_v == nullptr || d_slots == nullptr)
-    return fail(PA_ERR_INVALID_ARG, "append_kv: null device pointer");
-  if ((reinterpret_cast<uintptr_t>(d_k) | reinterpret_cast<uintptr_t>(d_v)) & 15)
-    return fail(PA_ERR_INVALID_ARG, "append_kv: k and v must be 16-byte aligned");
-  hipError_t e = pa::launch_append(pool->geom, layer, d_k, d_v, d_slots, n,
-                                   static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("append_kv: ") + hipGetErrorString(e));
-  return PA_OK;
+  return guarded("append_kv", [&]() -> pa_status {
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, "append_kv: null pool");
+    if (layer < 0 || layer >= pool->desc.num_layers)
+      return fail(PA_ERR_INVALID_ARG, "append_kv: layer out of range");
+    if (n < 0) return fail(PA_ERR_INVALID_ARG, "append_kv: negative token count");
+    if (n == 0) return PA_OK;
+    if (d_k == nullptr || d_v == nullptr || d_slots == nullptr)
+      return fail(PA_ERR_INVALID_ARG, "append_kv: null device pointer");
+    if ((reinterpret_cast<uintptr_t>(d_k) | reinterpret_cast<uintptr_t>(d_v)) & 15)
+      return fail(PA_ERR_INVALID_ARG, "append_kv: k and v must be 16-byte aligned");
+    hipError_t e = pa::launch_append(pool->geom, layer, d_k, d_v, d_slots, n,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, std::string("append_kv: ") + hipGetErrorString(e));
+    return PA_OK;
+  });
 }
 
 int32_t pa_decode_partition_tokens(const pa_pool* pool, int32_t num_seqs, int32_t max_context,
@@ -581,9 +632,11 @@ pa_status pa_decode(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dt
                     const int32_t* d_context_lens, int32_t num_seqs, int32_t max_context,
                     int32_t partition_tokens, float* d_out, void* d_workspace,
                     size_t workspace_bytes, void* stream) {
-  return decode_impl("decode", pool, layer, nullptr, nullptr, nullptr, d_q, q_dtype, num_q_heads,
-                     scale, d_block_tables, table_stride, d_req_ids, d_context_lens, num_seqs,
-                     max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream);
+  return guarded("decode", [&]() -> pa_status {
+    return decode_impl("decode", pool, layer, nullptr, nullptr, nullptr, d_q, q_dtype, num_q_heads,
+                       scale, d_block_tables, table_stride, d_req_ids, d_context_lens, num_seqs,
+                       max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream);
+  });
 }
 
 pa_status pa_append_decode(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
@@ -593,28 +646,32 @@ pa_status pa_append_decode(pa_pool* pool, int32_t layer, const void* d_k, const 
                            const int32_t* d_context_lens, int32_t num_seqs, int32_t max_context,
                            int32_t partition_tokens, float* d_out, void* d_workspace,
                            size_t workspace_bytes, void* stream) {
-  if (d_k == nullptr || d_v == nullptr || d_slots == nullptr)
-    return fail(PA_ERR_INVALID_ARG, "append_decode: null k, v or slots");
-  if ((reinterpret_cast<uintptr_t>(d_k) | reinterpret_cast<uintptr_t>(d_v)) & 15)
-    return fail(PA_ERR_INVALID_ARG, "append_decode: k and v must be 16-byte aligned");
-  return decode_impl("append_decode", pool, layer, d_k, d_v, d_slots, d_q, q_dtype, num_q_heads,
-                     scale, d_block_tables, table_stride, d_req_ids, d_context_lens, num_seqs,
-                     max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream);
+  return guarded("append_decode", [&]() -> pa_status {
+    if (d_k == nullptr || d_v == nullptr || d_slots == nullptr)
+      return fail(PA_ERR_INVALID_ARG, "append_decode: null k, v or slots");
+    if ((reinterpret_cast<uintptr_t>(d_k) | reinterpret_cast<uintptr_t>(d_v)) & 15)
+      return fail(PA_ERR_INVALID_ARG, "append_decode: k and v must be 16-byte aligned");
+    return decode_impl("append_decode", pool, layer, d_k, d_v, d_slots, d_q, q_dtype, num_q_heads,
+                       scale, d_block_tables, table_stride, d_req_ids, d_context_lens, num_seqs,
+                       max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream);
+  });
 }
 
 pa_status pa_shared_groups(const pa_pool* pool, const int32_t* req_ids, int32_t n,
                            int32_t partition_tokens, int32_t* seq_shared_out, int32_t* groups_out,
                            int32_t* n_groups_out, int32_t* max_members_out, int32_t* max_shared_out) {
-  if (pool == nullptr || seq_shared_out == nullptr || groups_out == nullptr || n_groups_out == nullptr ||
-      max_members_out == nullptr || max_shared_out == nullptr)
-    return fail(PA_ERR_INVALID_ARG, "shared_groups: null argument");
-  if (!pool->geom.paged) return fail(PA_ERR_INVALID_ARG, "shared_groups: sharing needs the paged layout");
-  if (bad_partition(pool, partition_tokens) || partition_tokens <= 0)
-    return fail(PA_ERR_INVALID_ARG, "shared_groups: partition_tokens must be a positive multiple of 16 and of block_size");
-  std::string err;
-  pa::Status st = pool->alloc.shared_groups(req_ids, n, partition_tokens, seq_shared_out, groups_out,
-                                            n_groups_out, max_members_out, max_shared_out, &err);
-  return from_alloc(st, err);
+  return guarded("shared_groups", [&]() -> pa_status {
+    if (pool == nullptr || seq_shared_out == nullptr || groups_out == nullptr || n_groups_out == nullptr ||
+        max_members_out == nullptr || max_shared_out == nullptr)
+      return fail(PA_ERR_INVALID_ARG, "shared_groups: null argument");
+    if (!pool->geom.paged) return fail(PA_ERR_INVALID_ARG, "shared_groups: sharing needs the paged layout");
+    if (bad_partition(pool, partition_tokens) || partition_tokens <= 0)
+      return fail(PA_ERR_INVALID_ARG, "shared_groups: partition_tokens must be a positive multiple of 16 and of block_size");
+    std::string err;
+    pa::Status st = pool->alloc.shared_groups(req_ids, n, partition_tokens, seq_shared_out, groups_out,
+                                              n_groups_out, max_members_out, max_shared_out, &err);
+    return from_alloc(st, err);
+  });
 }
 
 pa_status pa_decode_shared(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
@@ -624,11 +681,13 @@ pa_status pa_decode_shared(pa_pool* pool, int32_t layer, const void* d_q, pa_dty
                            const int32_t* d_groups, int32_t num_groups, int32_t max_members,
                            int32_t max_shared, float* d_out, void* d_workspace,
                            size_t workspace_bytes, void* stream) {
-  if (d_seq_shared == nullptr) return fail(PA_ERR_INVALID_ARG, "decode_shared: null seq_shared");
-  return decode_impl("decode_shared", pool, layer, nullptr, nullptr, nullptr, d_q, q_dtype, num_q_heads,
-                     scale, d_block_tables, table_stride, nullptr, d_context_lens, num_seqs,
-                     max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream,
-                     d_seq_shared, d_groups, num_groups, max_members, max_shared);
+  return guarded("decode_shared", [&]() -> pa_status {
+    if (d_seq_shared == nullptr) return fail(PA_ERR_INVALID_ARG, "decode_shared: null seq_shared");
+    return decode_impl("decode_shared", pool, layer, nullptr, nullptr, nullptr, d_q, q_dtype, num_q_heads,
+                       scale, d_block_tables, table_stride, nullptr, d_context_lens, num_seqs,
+                       max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream,
+                       d_seq_shared, d_groups, num_groups, max_members, max_shared);
+  });
 }
 
 const char* pa_last_error(void) { return g_err.c_str(); }
