@@ -711,6 +711,9 @@ def main():
             res["roofline"]["frac_of_probe_best"] = round(achieved / max(probe.values()), 4)
             if "decode_pattern" in probe:
                 res["roofline"]["frac_of_decode_pattern"] = round(achieved / probe["decode_pattern"], 4)
+            if "decode_mapped" in probe and args.config == 2 and as_counted:
+                # the same tiles in the decode's own order, no arithmetic
+                res["roofline"]["frac_of_decode_mapped"] = round(achieved / probe["decode_mapped"], 4)
     print(json.dumps(res), flush=True)
 
 

@@ -1,6 +1,7 @@
 // Achievable HBM read rate of the GPU, next to the datasheet peak: a plain
-// streaming read and a read of 4 KiB tiles (the size of one bf16 cache tile of
-// 16 tokens x 128 dims) in order and in a random order.  Prints one line per
+// streaming read, a read of 4 KiB tiles (the size of one bf16 cache tile of
+// 16 tokens x 128 dims) in order and in a random order, and the decode's own
+// read patterns without their arithmetic.  Prints one line per
 // case, "<case> <workgroups> <GB/s>", for bench.py.  Every index is < n
 // (grid-stride loops; tile ids are a permutation of all tiles).
 #include <hip/hip_runtime.h>
@@ -42,6 +43,33 @@ __global__ void kv_pattern(const char* __restrict__ K, const char* __restrict__ 
   u32x4 acc = {0, 0, 0, 0};
   for (int i = 0; i < per_wave; ++i) {
     const long tile = (long)ids[gw * per_wave + i] * 4096;
+    u32x4 k[4];
+    u32x2 v[8];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) k[x] = __builtin_nontemporal_load((const u32x4*)(K + tile + x * 1024 + lane * 16));
+#pragma unroll
+    for (int x = 0; x < 8; ++x) v[x] = __builtin_nontemporal_load((const u32x2*)(V + tile + x * 512 + lane * 8));
+#pragma unroll
+    for (int x = 0; x < 4; ++x) acc ^= k[x];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) { acc.x ^= v[x].x; acc.y ^= v[x].y; }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+// The decode's exact mapping on the Llama-3-8B batch-64 layer, without its
+// arithmetic: K and V pools of [4096 blocks][8 heads][4 KiB tile] per layer,
+// 64 sequences of 64 blocks each (a seeded permutation), workgroup
+// s * 8 + h of 4 waves, wave w reading chunks 63 - w, 59 - w, ... down to 0.
+// table[] holds block ids < 4096, so every tile lies inside its pool.
+__global__ void decode_mapped(const char* __restrict__ K, const char* __restrict__ V,
+                              const int* __restrict__ table, unsigned* out) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s = blockIdx.x / 8, h = blockIdx.x % 8;
+  u32x4 acc = {0, 0, 0, 0};
+  for (int c = 63 - wave; c >= 0; c -= 4) {
+    const long tile = ((long)table[s * 64 + c] * 8 + h) * 4096;
     u32x4 k[4];
     u32x2 v[8];
 #pragma unroll
@@ -107,6 +135,37 @@ int main() {
     const double moved = (double)waves * per_wave * 8192;
     printf("decode_pattern %d %.0f\n", wg, moved * 20 / (ms / 1e3) / 1e9);
     printf("decode_pattern_us %d %.2f\n", wg, ms * 1e3 / 20);
+  }
+  {
+    // the decode's exact mapping, 8 layer pools rotated as the benchmark
+    // rotates them (2 GiB of the 4 GiB buffer)
+    const size_t pool = (size_t)4096 * 8 * 4096;
+    const int layers = 8;
+    std::vector<int> blocks(4096);
+    for (int i = 0; i < 4096; ++i) blocks[i] = i;
+    std::mt19937 g(2412);
+    std::shuffle(blocks.begin(), blocks.end(), g);
+    int* table;
+    CK(hipMalloc(&table, 4096 * 4));
+    CK(hipMemcpy(table, blocks.data(), 4096 * 4, hipMemcpyHostToDevice));
+    const char* base = reinterpret_cast<const char*>(b);
+    for (int l = 0; l < layers; ++l)
+      hipLaunchKernelGGL(decode_mapped, dim3(512), dim3(256), 0, 0, base + l * 2 * pool, base + l * 2 * pool + pool,
+                         table, out);
+    CK(hipGetLastError());
+    CK(hipDeviceSynchronize());
+    CK(hipEventRecord(ev0));
+    for (int r = 0; r < 5; ++r)
+      for (int l = 0; l < layers; ++l)
+        hipLaunchKernelGGL(decode_mapped, dim3(512), dim3(256), 0, 0, base + l * 2 * pool,
+                           base + l * 2 * pool + pool, table, out);
+    CK(hipEventRecord(ev1));
+    CK(hipEventSynchronize(ev1));
+    float ms;
+    CK(hipEventElapsedTime(&ms, ev0, ev1));
+    const double moved = 512.0 * 64 * 8192;
+    printf("decode_mapped 512 %.0f\n", moved * 5 * layers / (ms / 1e3) / 1e9);
+    printf("decode_mapped_us 512 %.2f\n", ms * 1e3 / (5 * layers));
   }
   return 0;
 }
