@@ -496,57 +496,108 @@ def algorithmic_bytes(cfg, lens, fused_append: bool, kv_fraction: float = 1.0) -
     return total
 
 
-def cpu_baseline(bench, seconds: float) -> dict:
-    """The oracle (fp64 gather + attend) on host cores over a bounded sample."""
-    import torch
+def _oracle_slice(job: dict) -> tuple:
+    """One host core's share of the oracle baseline, run in a child process:
+    gather through the block table (or at reqId x S) + fp64 attention, cycling
+    over its sequences until `seconds` have passed.  BLAS is held to one
+    thread.  Returns (KV bytes attended, sequence-decodes, seconds)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as A
 
+    conv = A.bf16_bits_to_f64 if job["bf16"] else A.f32_to_f64
+    kb, vb, lens, q, bs = job["kb"], job["vb"], job["lens"], job["q"], job["bs"]
+    done = n = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            for i, length in enumerate(lens):
+                length = int(length)
+                blocks = job["blocks"][i][: -(-length // bs)]
+                kr, vr = conv(A.k_rows(kb[blocks])), conv(A.v_rows(vb[blocks]))
+                if job["paged"]:
+                    local = range(len(blocks))
+                    k = A.gather_paged(kr, local, length, bs)
+                    v = A.gather_paged(vr, local, length, bs)
+                else:
+                    span = len(blocks) * bs
+                    k = A.gather_contiguous(A.contiguous_rows(kr, 1, span), 0, length)
+                    v = A.gather_contiguous(A.contiguous_rows(np.ascontiguousarray(vr), 1, span), 0, length)
+                A.attend(q[i], k, v, job["scale"])
+                done += length * job["token_bytes"]
+                n += 1
+                if time.perf_counter() - t0 >= job["seconds"]:
+                    return done, n, time.perf_counter() - t0
+
+
+# host cores a GPU box gives one GPU's jobs
+CPU_SHARE = 16
+
+
+def cpu_baseline(bench, seconds: float) -> dict | None:
+    """The oracle (fp64 gather + attend) on the host's cores over a bounded
+    sample of the workload's first layer: one child process per core, each
+    cycling over its slice of the sequences for `seconds` seconds with BLAS
+    held to one thread, then the same on one core alone.  The value is the
+    sum of the processes' rates."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    import torch
+
     cfg = bench.cfg
     pool = bench.pool
-    with threadpool_limits(limits=1):
-        kc = pool.k_cache[0]
-        vc = pool.v_cache[0]
-        if cfg.kv_dtype == "bf16":
-            kb = kc.view(torch.int16).cpu().numpy().view(np.uint16)
-            vb = vc.view(torch.int16).cpu().numpy().view(np.uint16)
-            conv = A.bf16_bits_to_f64
-        else:
-            kb = kc.cpu().numpy()
-            vb = vc.cpu().numpy()
-            conv = A.f32_to_f64
-        q = bench.q[0].float().cpu().numpy().astype(np.float64)
-        if bench.layout == "paged":
-            tables, lens = pool.block_tables(bench.rids_np)
-        else:
-            _, lens = pool.block_tables(bench.rids_np, 1)
-        done_bytes = 0
-        n = 0
-        t0 = time.perf_counter()
-        for i in range(1 << 30):
-            s = i % len(lens)
-            length = int(lens[s])
-            if bench.layout == "paged":
-                t = tables[s][: -(-length // cfg.block_size)]
-                k = A.gather_paged(conv(A.k_rows(kb[t])), range(len(t)), length, cfg.block_size)
-                v = A.gather_paged(conv(A.v_rows(vb[t])), range(len(t)), length, cfg.block_size)
-            else:
-                r = bench.batch[s]
-                per = cfg.max_seq_len // cfg.block_size
-                kr = A.contiguous_rows(conv(A.k_rows(kb[r * per:(r + 1) * per])), 1, cfg.max_seq_len)
-                vr = A.contiguous_rows(conv(A.v_rows(vb[r * per:(r + 1) * per])), 1, cfg.max_seq_len)
-                k = A.gather_contiguous(kr, 0, length)
-                v = A.gather_contiguous(vr, 0, length)
-            A.attend(q[s], k, v, bench.scale)
-            done_bytes += kv_bytes(cfg, np.array([length]))
-            n += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} sequence-decodes (cycling over the {len(lens)} sequences of one layer: "
-                      f"gather through the block table + fp64 attention), {dt:.1f} s, single thread"}
+    if pool.k_cache is None:   # a demand-paged pool's caches cannot be read back
+        return None
+    paged = bench.layout == "paged"
+    if cfg.kv_dtype == "bf16":
+        kb = pool.k_cache[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        vb = pool.v_cache[0].view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        kb = pool.k_cache[0].cpu().numpy()
+        vb = pool.v_cache[0].cpu().numpy()
+    q = bench.q[0].float().cpu().numpy().astype(np.float64)
+    if paged:
+        tables, lens = pool.block_tables(bench.rids_np)
+    else:
+        _, lens = pool.block_tables(bench.rids_np, 1)
+    bs = cfg.block_size
+    per = cfg.max_seq_len // bs
+    elt = 2 if cfg.kv_dtype == "bf16" else 4
+    cores = max(1, min(len(os.sched_getaffinity(0)), CPU_SHARE))
+
+    def job(seqs, secs):
+        # the slice's blocks copied out of the layer, renumbered in order
+        blocks, kparts, vparts, off = [], [], [], 0
+        for s in seqs:
+            nblk = -(-int(lens[s]) // bs)
+            ids = (tables[s][:nblk] if paged else
+                   np.arange(bench.batch[s] * per, bench.batch[s] * per + nblk))
+            kparts.append(kb[ids])
+            vparts.append(vb[ids])
+            blocks.append(np.arange(off, off + nblk))
+            off += nblk
+        return {"kb": np.concatenate(kparts), "vb": np.concatenate(vparts), "blocks": blocks,
+                "lens": [int(lens[s]) for s in seqs], "q": q[list(seqs)], "bs": bs, "paged": paged,
+                "bf16": cfg.kv_dtype == "bf16", "scale": bench.scale, "seconds": secs,
+                "token_bytes": cfg.num_kv_heads * cfg.head_dim * elt * 2}
+
+    b = len(lens)
+    slices = [list(range(i, b, cores)) for i in range(min(cores, b))]
+    with ProcessPoolExecutor(max_workers=len(slices), mp_context=mp.get_context("spawn")) as ex:
+        parts = list(ex.map(_oracle_slice, [job(sl, seconds) for sl in slices]))
+    rate = sum(d / t for d, _, t in parts)
+    n_all = sum(n for _, n, _ in parts)
+    one_d, one_n, one_t = _oracle_slice(job(list(range(b)), seconds / 2))
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": len(slices), "kind": "oracle",
+            "sample": f"{n_all} sequence-decodes of one layer ({b} sequences dealt round-robin to "
+                      f"{len(slices)} processes, one per host core, each cycling over its share for "
+                      f"{seconds:.0f} s: gather through the block table + fp64 attention, BLAS "
+                      f"threads 1 per process); affinity {len(os.sched_getaffinity(0))} cores, "
+                      f"at most {CPU_SHARE} used",
+            "single_core": {"value": round(one_d / one_t / 1e9, 4), "unit": "GB/s",
+                            "sample": f"{one_n} sequence-decodes in {one_t:.1f} s, one process, "
+                                      "BLAS threads 1"}}
 
 
 def main():
@@ -692,7 +743,9 @@ def main():
         res["roofline"]["traffic"] = measured_traffic(
             "cfg2-paged" + ("" if args.separate_append else "-fused"))
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(bench, args.cpu_seconds)
+        cpu = cpu_baseline(bench, args.cpu_seconds)
+        if cpu is not None:
+            res["cpu_baseline"] = cpu
     if args.swap_seqs:
         res["swap"] = swap_probe(bench, args.swap_seqs)
     if bench.vmm:

@@ -58,7 +58,8 @@
  *   all-or-nothing) and pa_last_error() gives a message for the calling thread.
  * Validation: host-visible arguments are checked on the host.  Device arrays
  *   (tables, lengths, slots, pairs) are trusted: their entries must be in
- *   range; out-of-range entries give undefined results.
+ *   range; out-of-range entries give undefined results.  pa_check_decode_args,
+ *   pa_check_slots and pa_check_block_pairs check host copies of them.
  * Threads and streams: a pool is not thread-safe.  Device calls only enqueue
  *   work on the given stream (hipStream_t passed as void*, NULL = the default
  *   stream) and never synchronise; the caller orders them.
@@ -394,6 +395,40 @@ pa_status pa_append_decode(pa_pool* pool, int32_t layer, const void* d_k, const 
                            const int32_t* d_context_lens, int32_t num_seqs, int32_t max_context,
                            int32_t partition_tokens, float* d_out, void* d_workspace,
                            size_t workspace_bytes, void* stream);
+
+/* ---- host-side checks of the device arrays (debugging aids) ---------------
+ * The device calls trust their device arrays (see Validation above): an entry
+ * out of range makes a kernel read or write outside the caches.  These calls
+ * take HOST copies of those arrays and check them against the pool, on the
+ * CPU; they launch nothing and change nothing.  PA_OK, or PA_ERR_INVALID_ARG
+ * with the first offending entry in pa_last_error(). */
+
+/* The arrays of a pa_decode / pa_append_decode call (same meaning, same
+ * num_seqs and max_context; host int32):
+ *   h_context_lens[s] in [0, max_context], max_context <= max_seq_len;
+ *   paged: table_stride >= ceil(max_context / block_size) and entries j <
+ *     ceil(L_s / block_size) of row s of h_block_tables are blocks of the
+ *     pool ([ROC] Terms: the table maps a sequence's logical blocks to
+ *     physical ones);
+ *   contiguous: request ids (h_req_ids[s], or s if NULL) in [0, max_seqs),
+ *     and for a demand-paged pool the first ceil(L_s / block_size) blocks of
+ *     each request mapped;
+ *   h_slots (NULL: no append): each slot >= 0 is the slot of position L_s - 1
+ *     (L_s >= 1) and no two sequences append to the same slot. */
+pa_status pa_check_decode_args(const pa_pool* pool, const int32_t* h_block_tables,
+                               int32_t table_stride, const int32_t* h_req_ids,
+                               const int32_t* h_context_lens, const int32_t* h_slots,
+                               int32_t num_seqs, int32_t max_context);
+
+/* The slots of a pa_append_kv call: each slot >= 0 names a row of the pool
+ * (of a mapped page, for a demand-paged pool) and no slot appears twice. */
+pa_status pa_check_slots(const pa_pool* pool, const int32_t* h_slots, int32_t n);
+
+/* The pairs of a pa_copy_blocks call: both blocks of every pair belong to the
+ * pool and differ, no block is the destination of two pairs, and no
+ * destination is also a source ([PAS] Summary: a shared block is copied
+ * before a sharer writes into it).  Paged only. */
+pa_status pa_check_block_pairs(const pa_pool* pool, const int32_t* h_pairs, int32_t n);
 
 /* Message of the calling thread's last error ("" if none). */
 const char* pa_last_error(void);

@@ -548,6 +548,11 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
     if (d_block_tables == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null block tables");
     if (table_stride < nblk)
       return fail(PA_ERR_INVALID_ARG, w + ": table_stride is shorter than ceil(max_context / block_size)");
+  } else if (d_req_ids == nullptr && num_seqs > d.max_seqs) {
+    // without request ids sequence s reads request s's sub-tensor, which
+    // exists for s < max_seqs only
+    return fail(PA_ERR_INVALID_ARG, w + ": num_seqs " + std::to_string(num_seqs) + " exceeds max_seqs " +
+                                        std::to_string(d.max_seqs) + " and no request ids are given");
   }
   if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, w + ": scale is NaN");
   if (shared) {
@@ -687,6 +692,139 @@ pa_status pa_decode_shared(pa_pool* pool, int32_t layer, const void* d_q, pa_dty
                        scale, d_block_tables, table_stride, nullptr, d_context_lens, num_seqs,
                        max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream,
                        d_seq_shared, d_groups, num_groups, max_members, max_shared);
+  });
+}
+
+// ---- host-side checks of device arrays (nothing is launched) -------------
+
+pa_status pa_check_decode_args(const pa_pool* pool, const int32_t* h_block_tables,
+                               int32_t table_stride, const int32_t* h_req_ids,
+                               const int32_t* h_context_lens, const int32_t* h_slots,
+                               int32_t num_seqs, int32_t max_context) {
+  return guarded("check_decode_args", [&]() -> pa_status {
+    const std::string w = "check_decode_args";
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null pool");
+    const pa_pool_desc& d = pool->desc;
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, w + ": negative num_seqs");
+    if (max_context < 0 || max_context > d.max_seq_len)
+      return fail(PA_ERR_INVALID_ARG, w + ": max_context must be in [0, max_seq_len]");
+    if (num_seqs == 0) return PA_OK;
+    if (h_context_lens == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null lengths");
+    const int32_t bs = d.block_size;
+    const bool paged = d.layout == PA_PAGED;
+    if (paged) {
+      if (h_block_tables == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null block tables");
+      if (table_stride < (max_context + bs - 1) / bs)
+        return fail(PA_ERR_INVALID_ARG, w + ": table_stride is shorter than ceil(max_context / block_size)");
+    } else if (h_req_ids == nullptr && num_seqs > d.max_seqs) {
+      return fail(PA_ERR_INVALID_ARG, w + ": num_seqs exceeds max_seqs and no request ids are given");
+    }
+    std::vector<int64_t> taken;  // slots appended to, to find repeats
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      const std::string at = w + ": sequence " + std::to_string(s);
+      const int32_t L = h_context_lens[s];
+      if (L < 0 || L > max_context)
+        return fail(PA_ERR_INVALID_ARG, at + ": length " + std::to_string(L) + " outside [0, max_context]");
+      const int32_t nblk = (L + bs - 1) / bs;
+      int64_t last_slot = -1;  // slot of position L - 1
+      if (paged) {
+        const int32_t* row = h_block_tables + static_cast<int64_t>(s) * table_stride;
+        for (int32_t j = 0; j < nblk; ++j) {
+          if (row[j] < 0 || row[j] >= d.num_blocks)
+            return fail(PA_ERR_INVALID_ARG, at + ": block table entry " + std::to_string(j) + " = " +
+                                                std::to_string(row[j]) + " is not a block of the pool");
+        }
+        if (L > 0) last_slot = static_cast<int64_t>(row[(L - 1) / bs]) * bs + (L - 1) % bs;
+      } else {
+        const int32_t rid = h_req_ids ? h_req_ids[s] : s;
+        if (rid < 0 || rid >= d.max_seqs)
+          return fail(PA_ERR_INVALID_ARG, at + ": request id " + std::to_string(rid) + " outside [0, max_seqs)");
+        if (pool->vmm != nullptr) {
+          const int64_t unit = static_cast<int64_t>(d.num_kv_heads) * d.head_dim * bs * elt_bytes(d.kv_dtype);
+          if (nblk * unit > pool->vmm->region_mapped(rid))
+            return fail(PA_ERR_INVALID_ARG, at + ": length " + std::to_string(L) + " reaches past the pages mapped for request " +
+                                                std::to_string(rid));
+        }
+        if (L > 0) last_slot = static_cast<int64_t>(rid) * d.max_seq_len + L - 1;
+      }
+      if (h_slots != nullptr && h_slots[s] >= 0) {
+        if (L < 1) return fail(PA_ERR_INVALID_ARG, at + ": appends a token but its length is 0");
+        if (h_slots[s] != last_slot)
+          return fail(PA_ERR_INVALID_ARG, at + ": slot " + std::to_string(h_slots[s]) + " is not the slot of position L-1 (" +
+                                              std::to_string(last_slot) + ")");
+        taken.push_back(h_slots[s]);
+      }
+    }
+    std::sort(taken.begin(), taken.end());
+    if (std::adjacent_find(taken.begin(), taken.end()) != taken.end())
+      return fail(PA_ERR_INVALID_ARG, w + ": two sequences append to the same slot");
+    return PA_OK;
+  });
+}
+
+pa_status pa_check_slots(const pa_pool* pool, const int32_t* h_slots, int32_t n) {
+  return guarded("check_slots", [&]() -> pa_status {
+    const std::string w = "check_slots";
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null pool");
+    if (n < 0) return fail(PA_ERR_INVALID_ARG, w + ": negative count");
+    if (n == 0) return PA_OK;
+    if (h_slots == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null slots");
+    const pa_pool_desc& d = pool->desc;
+    const int64_t rows = d.layout == PA_PAGED ? static_cast<int64_t>(d.num_blocks) * d.block_size
+                                              : static_cast<int64_t>(d.max_seqs) * d.max_seq_len;
+    std::vector<int32_t> taken;
+    taken.reserve(n);
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t slot = h_slots[i];
+      if (slot < 0) continue;
+      if (slot >= rows)
+        return fail(PA_ERR_INVALID_ARG, w + ": slot " + std::to_string(slot) + " (token " + std::to_string(i) +
+                                            ") is not a row of the pool");
+      if (pool->vmm != nullptr) {
+        const int64_t unit = static_cast<int64_t>(d.num_kv_heads) * d.head_dim * d.block_size * elt_bytes(d.kv_dtype);
+        const int32_t rid = slot / d.max_seq_len;
+        const int64_t pos = slot % d.max_seq_len;
+        if ((pos / d.block_size + 1) * unit > pool->vmm->region_mapped(rid))
+          return fail(PA_ERR_INVALID_ARG, w + ": slot " + std::to_string(slot) + " lies in an unmapped page");
+      }
+      taken.push_back(slot);
+    }
+    std::sort(taken.begin(), taken.end());
+    if (std::adjacent_find(taken.begin(), taken.end()) != taken.end())
+      return fail(PA_ERR_INVALID_ARG, w + ": a slot appears twice");
+    return PA_OK;
+  });
+}
+
+pa_status pa_check_block_pairs(const pa_pool* pool, const int32_t* h_pairs, int32_t n) {
+  return guarded("check_block_pairs", [&]() -> pa_status {
+    const std::string w = "check_block_pairs";
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null pool");
+    if (n < 0) return fail(PA_ERR_INVALID_ARG, w + ": negative count");
+    if (n == 0) return PA_OK;
+    if (pool->desc.layout != PA_PAGED) return fail(PA_ERR_INVALID_ARG, w + ": contiguous pool has no blocks");
+    if (h_pairs == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null pairs");
+    std::vector<int32_t> srcs, dsts;
+    for (int32_t i = 0; i < n; ++i) {
+      for (int k = 0; k < 2; ++k) {
+        const int32_t b = h_pairs[2 * i + k];
+        if (b < 0 || b >= pool->desc.num_blocks)
+          return fail(PA_ERR_INVALID_ARG, w + ": pair " + std::to_string(i) + " names block " + std::to_string(b) +
+                                              ", not a block of the pool");
+      }
+      if (h_pairs[2 * i] == h_pairs[2 * i + 1])
+        return fail(PA_ERR_INVALID_ARG, w + ": pair " + std::to_string(i) + " copies a block onto itself");
+      srcs.push_back(h_pairs[2 * i]);
+      dsts.push_back(h_pairs[2 * i + 1]);
+    }
+    std::sort(srcs.begin(), srcs.end());
+    std::sort(dsts.begin(), dsts.end());
+    if (std::adjacent_find(dsts.begin(), dsts.end()) != dsts.end())
+      return fail(PA_ERR_INVALID_ARG, w + ": a block is the destination of two pairs");
+    for (int32_t b : dsts)
+      if (std::binary_search(srcs.begin(), srcs.end(), b))
+        return fail(PA_ERR_INVALID_ARG, w + ": block " + std::to_string(b) + " is both a source and a destination");
+    return PA_OK;
   });
 }
 

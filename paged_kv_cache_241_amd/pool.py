@@ -266,6 +266,35 @@ class Pool:
         capi.check(self.lib.pa_get_stats(self.handle, ctypes.byref(st)), "pa_get_stats")
         return {name: getattr(st, name) for name, _ in capi.pa_stats._fields_}
 
+    # -- host-side checks of device arrays (host copies; nothing is launched) ---
+    def check_decode_args(self, block_tables, context_lens, max_context: int, req_ids=None,
+                          slots=None) -> None:
+        """pa_check_decode_args on host int32 arrays: tables [B][stride]
+        (paged), lengths [B], request ids [B] (contiguous; None: s), the fused
+        append's slots [B] (None: no append)."""
+        lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+        b = len(lens)
+        tables, stride = None, 0
+        if self.layout == "paged" and block_tables is not None:
+            tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+            stride = int(tables.shape[1]) if tables.ndim == 2 else 0
+        rids = None if req_ids is None else np.ascontiguousarray(req_ids, dtype=np.int32)
+        sl = None if slots is None else np.ascontiguousarray(slots, dtype=np.int32)
+        capi.check(self.lib.pa_check_decode_args(
+            self.handle, _ptr32(tables) if tables is not None else None, stride,
+            _ptr32(rids) if rids is not None else None, _ptr32(lens) if b else None,
+            _ptr32(sl) if sl is not None else None, b, int(max_context)), "pa_check_decode_args")
+
+    def check_slots(self, slots) -> None:
+        sl = np.ascontiguousarray(slots, dtype=np.int32)
+        capi.check(self.lib.pa_check_slots(self.handle, _ptr32(sl) if len(sl) else None, len(sl)),
+                   "pa_check_slots")
+
+    def check_block_pairs(self, pairs) -> None:
+        pr = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+        capi.check(self.lib.pa_check_block_pairs(self.handle, _ptr32(pr) if len(pr) else None, len(pr)),
+                   "pa_check_block_pairs")
+
     # -- device ----------------------------------------------------------------
     def copy_blocks(self, pairs, stream=None) -> None:
         """pairs: device int32 tensor [n][2] of (src, dst) blocks."""

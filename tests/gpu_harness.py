@@ -59,17 +59,28 @@ class Case:
     def __init__(self, cfg: W.Config, layout: str = "paged", layers=(0,), num_layers=None,
                  free_seed=None, fill=None, values=None, init=None, step_append=True,
                  device="cuda"):
+        """layout: "paged", "contiguous", or "vmm" (the contiguous layout with
+        caches the library maps on demand; its caches cannot be read back)."""
         self.cfg = cfg
         self.pl = pl = W.plan(cfg)
         self.layers = tuple(layers)
         nl = num_layers or (max(self.layers) + 1)
+        self.vmm = layout == "vmm"
+        layout = "contiguous" if self.vmm else layout
         self.layout = layout
         # a contiguous pool reserves max_seq_len tokens per request id: size it
         # for the batch only
         self.max_seqs = max(4096, cfg.batch) if layout == "paged" else cfg.batch
+        vmm_bytes = None
+        if self.vmm:
+            assert fill is None and init is None, "a demand-paged pool's caches are the library's"
+            elt = 2 if cfg.kv_dtype == "bf16" else 4
+            vmm_bytes = (2 * nl * self.max_seqs * cfg.max_seq_len * cfg.num_kv_heads *
+                         cfg.head_dim * elt)
         self.pool = Pool(nl, pl.num_blocks, cfg.block_size, cfg.num_kv_heads, cfg.head_dim,
                          cfg.kv_dtype, layout, max_seqs=self.max_seqs,
-                         max_seq_len=cfg.max_seq_len, device=device, fill=fill)
+                         max_seq_len=cfg.max_seq_len, device=device, fill=fill,
+                         vmm_bytes=vmm_bytes)
         if init is not None:
             init(self.pool)
         if layout == "paged":
@@ -107,8 +118,9 @@ class Case:
 
     def _on_reserve(self, handles, counts, slots, pairs):
         self.log.append((np.array(slots, copy=True), np.array(pairs, copy=True)))
-        dev = self.pool.k_cache.device
+        dev = torch.device("cuda")
         if len(pairs):
+            self.pool.check_block_pairs(pairs)
             self.pool.copy_blocks(torch.from_numpy(np.ascontiguousarray(pairs)).to(dev))
         idx, sl = [], []
         k = 0
@@ -125,6 +137,7 @@ class Case:
             return
         if not idx:
             return
+        self.pool.check_slots(np.array(sl, dtype=np.int32))
         idx_t = torch.tensor(idx, dtype=torch.int64, device=dev)
         sl_t = torch.tensor(sl, dtype=torch.int32, device=dev)
         for l in self.layers:
@@ -135,6 +148,11 @@ class Case:
     def decode(self, layer=None, partition_tokens=0, q=None, req_ids=True, append=None):
         layer = self.layers[0] if layer is None else layer
         q = self.vals[layer][0] if q is None else q
+        # the device arrays, checked on host copies before the launch
+        self.pool.check_decode_args(
+            self.tables_np, self.lens_np, self.max_context,
+            req_ids=self.batch_rids if (self.layout != "paged" and req_ids) else None,
+            slots=append[2].cpu().numpy() if append is not None else None)
         out = self.pool.decode(layer, q, self.scale, self.tables, self.lens, self.max_context,
                                partition_tokens=partition_tokens,
                                req_ids=self.req_ids if (self.layout != "paged" and req_ids) else None,
@@ -167,23 +185,38 @@ class Case:
         return out
 
     def gathered(self, s: int, layer=None):
-        """Oracle gather of sequence s's K and V out of the device cache."""
+        """Oracle gather of sequence s's K and V out of the device cache.
+
+        Only the blocks holding its n tokens are read back, and rows at or past
+        n (never written: whatever bits the memory held, signalling NaN
+        patterns included) are zeroed in the raw bits before conversion; the
+        gather reads rows below n only."""
+        assert not self.vmm, "a demand-paged pool's caches cannot be read back"
         layer = self.layers[0] if layer is None else layer
         n = int(self.pl.lengths[s])
         bs = self.cfg.block_size
+        nblk = -(-n // bs)
         if self.layout == "paged":
-            t = self.tables_np[s][: -(-n // bs)]
+            t = self.tables_np[s][:nblk]
             tt = torch.from_numpy(np.ascontiguousarray(t)).long().to(self.pool.k_cache.device)
-            kb = A.k_rows(to_f64(self.pool.k_cache[layer].index_select(0, tt)))
-            vb = A.v_rows(to_f64(self.pool.v_cache[layer].index_select(0, tt)))
-            local = list(range(len(t)))
+            kt = self.pool.k_cache[layer].index_select(0, tt)
+            vt = self.pool.v_cache[layer].index_select(0, tt)
+        else:
+            r = self.batch_rids[s]
+            per = self.cfg.max_seq_len // bs
+            kt = self.pool.k_cache[layer][r * per:r * per + nblk]
+            vt = self.pool.v_cache[layer][r * per:r * per + nblk]
+        tail = n - (nblk - 1) * bs if nblk else bs   # rows written in the last block
+        kt, vt = kt.clone(), vt.clone()
+        if nblk and tail < bs:
+            kt[nblk - 1, :, :, tail:, :] = 0          # K tile [d/VE][BS][VE]
+            vt[nblk - 1, :, :, tail:] = 0             # V tile [d][BS]
+        kb, vb = A.k_rows(to_f64(kt)), A.v_rows(to_f64(vt))
+        if self.layout == "paged":
+            local = list(range(nblk))
             return A.gather_paged(kb, local, n, bs), A.gather_paged(vb, local, n, bs)
-        r = self.batch_rids[s]
-        per = self.cfg.max_seq_len // bs
-        kb = A.k_rows(to_f64(self.pool.k_cache[layer][r * per:(r + 1) * per]))
-        vb = A.v_rows(to_f64(self.pool.v_cache[layer][r * per:(r + 1) * per]))
-        kc = A.contiguous_rows(kb, 1, self.cfg.max_seq_len)
-        vc = A.contiguous_rows(np.ascontiguousarray(vb), 1, self.cfg.max_seq_len)
+        kc = A.contiguous_rows(kb, 1, nblk * bs)
+        vc = A.contiguous_rows(np.ascontiguousarray(vb), 1, nblk * bs)
         return A.gather_contiguous(kc, 0, n), A.gather_contiguous(vc, 0, n)
 
     def replay_on_oracle(self):
@@ -208,6 +241,30 @@ class Case:
 
         W.run_ops(pl.ops + [pl.step], ref, rids, on_reserve=record)
         return ref, rids, log
+
+
+# Decode tolerances: fp32 caches elementwise; bf16 caches per output row,
+# the stated 2e-2 and, since bf16 inputs are exact in fp64 and the kernel
+# accumulates in fp32, 1e-4 as well (2e-2 alone could not see a dropped token
+# at 1024 tokens).
+F32_ABS = 1e-5
+BF16_STATED = 2e-2
+BF16_INTERNAL = 1e-4
+
+
+def check_rows(case: "Case", out: torch.Tensor, seqs, layer=None) -> np.ndarray:
+    """Decode output rows of the listed sequences against the oracle."""
+    got = to_f64(out)
+    ref = case.reference(seqs, layer)
+    for s in seqs:
+        if case.cfg.kv_dtype == "f32":
+            err = float(np.max(np.abs(got[s] - ref[s]))) if ref[s].size else 0.0
+            assert err <= F32_ABS, (s, err)
+        else:
+            err = row_rel_err(got[s], ref[s])
+            assert err <= BF16_STATED, (s, err)
+            assert err <= BF16_INTERNAL, (s, err)
+    return got
 
 
 def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:

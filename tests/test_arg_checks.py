@@ -1,0 +1,138 @@
+"""Host-side checks (CPU only): nothing reaches a kernel with arguments that
+would make it read or write outside the caches.
+
+* pa_decode on a contiguous pool without request ids reads request s's
+  sub-tensor for sequence s: more sequences than max_seqs is refused on the
+  host, before any launch;
+* pa_check_decode_args / pa_check_slots / pa_check_block_pairs take host
+  copies of the device arrays and refuse every planted bad entry (block ids
+  outside the pool, lengths past max_context, short tables, request ids out
+  of range, append slots that are not position L-1's or that repeat, copy
+  pairs that overlap), and accept what the allocator hands out.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_241_amd import capi
+from paged_kv_cache_241_amd.pool import Pool
+
+
+def _fake(n=64):
+    """A 16-byte aligned address that no call below dereferences."""
+    buf = (ctypes.c_uint8 * (n + 16))()
+    return buf, (ctypes.addressof(buf) + 15) // 16 * 16
+
+
+def _paged():
+    p = Pool(host_only=True, num_layers=2, num_blocks=40, block_size=16, num_kv_heads=2,
+             head_dim=64, kv_dtype="bf16", layout="paged", max_seqs=8, max_seq_len=256)
+    p.set_free_order(np.random.default_rng(5).permutation(40).astype(np.int32))
+    rids = [p.add() for _ in range(4)]
+    p.reserve(rids, [15, 16, 40, 1])        # prefill
+    slots, pairs = p.reserve(rids)          # the decode step's token
+    assert len(pairs) == 0
+    tables, lens = p.block_tables(rids, 256 // 16)
+    return p, rids, tables, lens, slots
+
+
+def _refused(fn, *a, **kw):
+    with pytest.raises(capi.PaError) as e:
+        fn(*a, **kw)
+    assert e.value.status == capi.PA_ERR_INVALID_ARG
+    return str(e.value)
+
+
+def test_contiguous_decode_without_req_ids_refuses_more_sequences_than_max_seqs():
+    lib = capi.load()
+    p = Pool(host_only=True, num_layers=1, num_blocks=0, block_size=16, num_kv_heads=1,
+             head_dim=64, kv_dtype="f32", layout="contiguous", max_seqs=4, max_seq_len=64)
+    keep, addr = _fake(1 << 12)
+    for fn, extra in ((lib.pa_decode, ()), (lib.pa_append_decode, (addr, addr, addr))):
+        args = (p.handle, 0, *extra, addr, capi.PA_F32, 2, ctypes.c_float(0.125), None, 0, None,
+                addr, 5, 64, 0, addr, None, 0, None)
+        st = fn(*args)
+        assert st == capi.PA_ERR_INVALID_ARG, lib.pa_last_error()
+        assert b"max_seqs" in lib.pa_last_error()
+    # (no call here may get past the host checks: the addresses are fake)
+    p.check_decode_args(None, np.full(4, 64, np.int32), 64)
+    _refused(p.check_decode_args, None, np.full(5, 64, np.int32), 64)
+    p.check_decode_args(None, np.full(5, 64, np.int32), 64, req_ids=[0, 1, 2, 3, 0])
+    _refused(p.check_decode_args, None, np.full(2, 64, np.int32), 64, req_ids=[0, 4])
+    _refused(p.check_decode_args, None, np.full(2, 64, np.int32), 64, req_ids=[-1, 0])
+
+
+def test_decode_args_from_the_allocator_pass():
+    p, rids, tables, lens, slots = _paged()
+    assert lens.tolist() == [16, 17, 41, 2]
+    p.check_decode_args(tables, lens, int(lens.max()))
+    p.check_decode_args(tables, lens, 256, slots=slots)
+    # a sequence that appends nothing
+    sl = slots.copy()
+    sl[2] = -1
+    p.check_decode_args(tables, lens, 256, slots=sl)
+    # shorter lengths read fewer table entries; an empty context reads none
+    p.check_decode_args(tables, np.array([0, 1, 16, 2], np.int32), 256)
+
+
+@pytest.mark.parametrize("plant", [
+    "block_past_pool", "block_negative", "length_past_max", "length_negative", "stride_short",
+    "slot_not_last", "slot_repeated", "slot_on_empty",
+])
+def test_planted_bad_decode_args_are_refused(plant):
+    p, rids, tables, lens, slots = _paged()
+    t, ln, sl, mc = tables.copy(), lens.copy(), slots.copy(), 256
+    if plant == "block_past_pool":
+        t[2, 2] = 40                        # entry 2 of a 41-token context
+    elif plant == "block_negative":
+        t[1, 1] = -1
+    elif plant == "length_past_max":
+        mc = 40
+    elif plant == "length_negative":
+        ln[0] = -3
+    elif plant == "stride_short":
+        t = t[:, :2]
+    elif plant == "slot_not_last":
+        sl[1] = sl[1] - 1
+    elif plant == "slot_repeated":
+        # sequence 3 made a copy of sequence 0: same table, length and slot
+        sl[3] = sl[0]
+        ln[3] = ln[0]
+        t[3, :2] = t[0, :2]
+    elif plant == "slot_on_empty":
+        ln[3] = 0
+    msg = _refused(p.check_decode_args, t, ln, mc, slots=sl)
+    assert "check_decode_args" in msg
+    # a planted entry past what a context reads is not looked at
+    t2 = tables.copy()
+    t2[3, 5] = 10 ** 6
+    p.check_decode_args(t2, lens, 256, slots=slots)
+
+
+def test_slots_and_pairs():
+    p, rids, tables, lens, slots = _paged()
+    p.check_slots(slots)
+    p.check_slots(np.array([-1, 5, -7, 639], np.int32))
+    p.check_slots(np.zeros(0, np.int32))
+    _refused(p.check_slots, np.array([3, 640], np.int32))       # 40 blocks x 16 rows
+    _refused(p.check_slots, np.array([3, 9, 3], np.int32))
+    # copy-on-write pairs from a fork and a write into the shared last block
+    child = p.fork(rids[3])
+    _, pairs = p.reserve([child])
+    assert len(pairs) == 1
+    p.check_block_pairs(pairs)
+    p.check_block_pairs(np.zeros((0, 2), np.int32))
+    for bad in ([[1, 40]], [[-1, 2]], [[3, 3]], [[1, 2], [4, 2]], [[1, 2], [2, 5]]):
+        _refused(p.check_block_pairs, np.array(bad, np.int32))
+    c = Pool(host_only=True, num_layers=1, num_blocks=0, block_size=16, num_kv_heads=1,
+             head_dim=64, kv_dtype="f32", layout="contiguous", max_seqs=2, max_seq_len=64)
+    _refused(c.check_block_pairs, np.array([[0, 1]], np.int32))
+    c.check_slots(np.array([0, 127], np.int32))
+    _refused(c.check_slots, np.array([128], np.int32))
+    r = c.add()
+    s, _ = c.reserve([r], [10])
+    _, ln = c.block_tables([r], 1)
+    c.check_decode_args(None, ln, 64, req_ids=[r], slots=s[-1:])
+    _refused(c.check_decode_args, None, ln, 64, req_ids=[r], slots=s[-2:-1])

@@ -50,3 +50,27 @@ def test_algorithmic_bytes_of_the_llama_decode_launch():
     # fused: the new K and V rows read and written, plus the slots
     assert bench.algorithmic_bytes(cfg, lens, True) == kv + other + 64 * 8 * 128 * 2 * 2 * 2 + 64 * 4
     assert bench.algorithmic_bytes(cfg, lens, False, 0.5) == kv // 2 + other
+
+
+def test_cpu_baseline_spreads_the_oracle_over_host_cores():
+    # a host copy of a small bf16 layer stands in for the device cache
+    import torch
+
+    pool = _pool(16)
+    rids = [pool.add() for _ in range(6)]
+    pool.reserve(rids, [17, 40, 1, 33, 64, 5])
+    g = torch.Generator().manual_seed(3)
+    k = torch.randn((64, 2, 8, 16, 8), generator=g).to(torch.bfloat16)
+    v = torch.randn((64, 2, 64, 16), generator=g).to(torch.bfloat16)
+    fake = SimpleNamespace(
+        cfg=SimpleNamespace(block_size=16, max_seq_len=256, kv_dtype="bf16", num_kv_heads=2,
+                            head_dim=64),
+        pool=SimpleNamespace(k_cache=k[None], v_cache=v[None], block_tables=pool.block_tables),
+        q=[torch.randn((6, 4, 64), generator=g).to(torch.bfloat16)], layout="paged",
+        rids_np=np.array(rids, np.int32), batch=rids, scale=0.125)
+    res = bench.cpu_baseline(fake, 0.3)
+    cores = min(len(os.sched_getaffinity(0)), bench.CPU_SHARE, 6)
+    assert res["cores"] == cores and res["kind"] == "oracle" and res["value"] > 0
+    assert res["single_core"]["value"] > 0
+    if cores > 1:
+        assert res["value"] > res["single_core"]["value"]

@@ -22,13 +22,9 @@ import torch
 import workloads as W
 from oracle import attention as A
 
-from gpu_harness import Case, row_rel_err, to_f64
+from gpu_harness import Case, check_rows, row_rel_err, to_f64
 
 pytestmark = pytest.mark.gpu
-
-F32_ABS = 1e-5
-BF16_STATED = 2e-2
-BF16_INTERNAL = 1e-4
 
 
 def _need_gpu():
@@ -43,18 +39,7 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _check(case: Case, out: torch.Tensor, seqs, layer=None):
-    got = to_f64(out)
-    ref = case.reference(seqs, layer)
-    for s in seqs:
-        if case.cfg.kv_dtype == "f32":
-            err = float(np.max(np.abs(got[s] - ref[s]))) if ref[s].size else 0.0
-            assert err <= F32_ABS, (s, err)
-        else:
-            err = row_rel_err(got[s], ref[s])
-            assert err <= BF16_STATED, (s, err)
-            assert err <= BF16_INTERNAL, (s, err)
-    return got
+_check = check_rows
 
 
 # --------------------------------------------------------------------------
@@ -198,6 +183,28 @@ def test_full_size_sampled_rows(cid, over, layout):
         k, v = case.gathered(s)
         _, kl, vl = case.logical(s)
         assert np.array_equal(k, kl) and np.array_equal(v, vl)
+
+
+@pytest.mark.parametrize("cid,layers", [(2, (0, 7)), (3, (0,))])
+def test_full_size_fused_step_all_rows(cid, layers):
+    # The benchmark's own call at full size, every row against the oracle:
+    # pa_append_decode with the library's partition choice.  Workload 2 (64
+    # sequences x 8 KV heads, 1024 tokens: one partition each, the balanced
+    # start) on layers 0 and 7 of 8 pools; workload 3 (the ragged mix, 256
+    # sequences up to 8192 tokens: 1024-token partitions run from a work plan,
+    # then merged).  The appended rows land in the cache as well.
+    cfg = W.get(cid)
+    case = Case(cfg, layers=layers, num_layers=max(layers) + 1, step_append=False)
+    for layer in layers:
+        k, v = case.step_kv(layer)
+        out = case.decode(layer=layer, append=(k, v, case.step_slots))
+        assert torch.isfinite(out).all()
+        _check(case, out, range(cfg.batch), layer=layer)
+        lens = case.pl.lengths
+        for s in sorted({0, int(np.argmax(lens)), int(np.argmin(lens)), cfg.batch - 1}):
+            kk, vv = case.gathered(s, layer)
+            _, kl, vl = case.logical(s, layer)
+            assert np.array_equal(kk, kl) and np.array_equal(vv, vl), s
 
 
 # --------------------------------------------------------------------------
