@@ -396,6 +396,28 @@ pa_status pa_append_decode(pa_pool* pool, int32_t layer, const void* d_k, const 
                            int32_t partition_tokens, float* d_out, void* d_workspace,
                            size_t workspace_bytes, void* stream);
 
+/* pa_append_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace; the split-K partials
+ * and the work plan go to a device array the library holds, 64 MiB
+ * (PA_NOALLOC_SCRATCH_BYTES) on each GPU it runs on, until the process ends.
+ * Calls whose pa_decode_workspace_bytes(...) exceeds that fail with
+ * PA_ERR_WORKSPACE before anything is launched.  The call allocates nothing:
+ * no hipMalloc, no hipFree; its first call on a device looks up the array's
+ * address there.  The array keeps the last call's contents; every byte a call
+ * reads from it, the same call wrote first, so nothing needs clearing.  All
+ * calls on one GPU share the array: calls that may overlap (other streams,
+ * other threads) race and must be ordered by the caller.  Result and cache
+ * bytes are pa_append_decode's, bit for bit. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_append_decode_noalloc(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                                   const int32_t* d_slots, const void* d_q, pa_dtype q_dtype,
+                                   int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                                   int32_t table_stride, const int32_t* d_req_ids,
+                                   const int32_t* d_context_lens, int32_t num_seqs,
+                                   int32_t max_context, int32_t partition_tokens, float* d_out,
+                                   void* stream);
+
 /* ---- host-side checks of the device arrays (debugging aids) ---------------
  * The device calls trust their device arrays (see Validation above): an entry
  * out of range makes a kernel read or write outside the caches.  These calls

@@ -45,8 +45,11 @@ EXPORTS = (
     "pa_decode_partition_tokens", "pa_decode_workspace_bytes", "pa_decode", "pa_append_decode",
     "pa_swap_bytes", "pa_swap_out", "pa_swap_in", "pa_create_pool_vmm", "pa_vmm_info",
     "pa_vmm_trim", "pa_shared_groups", "pa_decode_shared", "pa_check_decode_args",
-    "pa_check_slots", "pa_check_block_pairs", "pa_last_error",
+    "pa_check_slots", "pa_check_block_pairs", "pa_append_decode_noalloc", "pa_last_error",
 )
+
+# bytes of the device scratch pa_append_decode_noalloc holds on each GPU
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class pa_pool_desc(ctypes.Structure):
@@ -136,6 +139,9 @@ def load() -> ctypes.CDLL:
         "pa_check_decode_args": (ctypes.c_int, [_vp, _p32, _i32, _p32, _p32, _p32, _i32, _i32]),
         "pa_check_slots": (ctypes.c_int, [_vp, _p32, _i32]),
         "pa_check_block_pairs": (ctypes.c_int, [_vp, _p32, _i32]),
+        "pa_append_decode_noalloc": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
+                                                    ctypes.c_float, _vp, _i32, _vp, _vp, _i32, _i32,
+                                                    _i32, _vp, _vp]),
         "pa_last_error": (ctypes.c_char_p, []),
     }
     assert set(sig) == set(EXPORTS)

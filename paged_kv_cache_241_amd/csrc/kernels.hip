@@ -53,11 +53,17 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "decode_common.hpp"
 #include "decode_partition.hpp"
 #include "kernels.hpp"
+
+// Split-K partials and the work plan of pa_append_decode_noalloc, for callers
+// that cannot allocate.  In host code `scratch` names a host-side stand-in,
+// not device memory: only the address static_scratch() looks up is passed on.
+static __device__ __align__(256) unsigned char scratch[pa::kStaticScratchBytes];
 
 namespace pa {
 namespace {
@@ -423,6 +429,28 @@ hipError_t launch_decode_bs(const CacheGeom& g, const DecodeArgs& a, bool* ok, h
 }
 
 }  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  // one lookup per device, with that device current; each GPU holds its own
+  // copy of the array at its own address
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_append(const CacheGeom& g, int32_t layer, const void* k, const void* v,
                          const int32_t* slots, int32_t n, hipStream_t stream) {

@@ -102,6 +102,15 @@ hipError_t launch_merge(const CacheGeom& g, const DecodeArgs& a, hipStream_t str
 hipError_t launch_decode_shared(const CacheGeom& g, int kind, const DecodeArgs& a,
                                 const SharedArgs& sh, bool* supported, hipStream_t stream);
 
+// Device scratch of the allocation-free decode entry point
+// (pa_append_decode_noalloc): a file-scope __device__ array in kernels.hip,
+// one copy per GPU, held until the process ends.
+constexpr size_t kStaticScratchBytes = static_cast<size_t>(64) << 20;
+
+// Device address of that array on the current device, looked up with
+// hipGetSymbolAddress on the first call per device and kept.
+hipError_t static_scratch(void** ptr);
+
 // Bytes of decode partials for these sizes, then the work plan (one int2
 // per (sequence, partition)).
 inline size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,

@@ -14,6 +14,9 @@
 #include "kernels.hpp"
 #include "vmm.hpp"
 
+static_assert(PA_NOALLOC_SCRATCH_BYTES == pa::kStaticScratchBytes,
+              "pa.h states the scratch size of pa_append_decode_noalloc");
+
 struct pa_pool {
   pa_pool_desc desc;
   pa::CacheGeom geom;
@@ -520,7 +523,8 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
                       int32_t max_context, int32_t partition_tokens, float* d_out,
                       void* d_workspace, size_t workspace_bytes, void* stream,
                       const int32_t* d_seq_shared = nullptr, const int32_t* d_groups = nullptr,
-                      int32_t num_groups = 0, int32_t max_members = 0, int32_t max_shared = 0) {
+                      int32_t num_groups = 0, int32_t max_members = 0, int32_t max_shared = 0,
+                      bool static_workspace = false) {
   const std::string w(who);
   const bool shared = d_seq_shared != nullptr;
   if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null pool");
@@ -594,7 +598,20 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
   a.scale = scale;
   if (grid * a.num_partitions > INT32_MAX) return fail(PA_ERR_INVALID_ARG, w + ": launch too large");
   const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, d.head_dim, a.num_partitions);
-  if (need > 0) {
+  if (need > 0 && static_workspace) {
+    // the library's own device array instead of a caller's workspace
+    if (need > pa::kStaticScratchBytes)
+      return fail(PA_ERR_WORKSPACE, w + ": the split-K partials need " + std::to_string(need) +
+                                        " bytes, more than the " + std::to_string(pa::kStaticScratchBytes) +
+                                        " bytes of the library's scratch (use pa_append_decode with a workspace)");
+    void* p = nullptr;
+    const hipError_t e = pa::static_scratch(&p);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_HIP, w + ": scratch address: " + hipGetErrorString(e));
+    }
+    a.ws = static_cast<float*>(p);
+  } else if (need > 0) {
     if (d_workspace == nullptr || workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, w + ": workspace needs " + std::to_string(need) + " bytes, got " +
                                         std::to_string(d_workspace ? workspace_bytes : 0));
@@ -659,6 +676,25 @@ pa_status pa_append_decode(pa_pool* pool, int32_t layer, const void* d_k, const 
     return decode_impl("append_decode", pool, layer, d_k, d_v, d_slots, d_q, q_dtype, num_q_heads,
                        scale, d_block_tables, table_stride, d_req_ids, d_context_lens, num_seqs,
                        max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream);
+  });
+}
+
+pa_status pa_append_decode_noalloc(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                                   const int32_t* d_slots, const void* d_q, pa_dtype q_dtype,
+                                   int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                                   int32_t table_stride, const int32_t* d_req_ids,
+                                   const int32_t* d_context_lens, int32_t num_seqs,
+                                   int32_t max_context, int32_t partition_tokens, float* d_out,
+                                   void* stream) {
+  return guarded("append_decode_noalloc", [&]() -> pa_status {
+    if (d_k == nullptr || d_v == nullptr || d_slots == nullptr)
+      return fail(PA_ERR_INVALID_ARG, "append_decode_noalloc: null k, v or slots");
+    if ((reinterpret_cast<uintptr_t>(d_k) | reinterpret_cast<uintptr_t>(d_v)) & 15)
+      return fail(PA_ERR_INVALID_ARG, "append_decode_noalloc: k and v must be 16-byte aligned");
+    return decode_impl("append_decode_noalloc", pool, layer, d_k, d_v, d_slots, d_q, q_dtype,
+                       num_q_heads, scale, d_block_tables, table_stride, d_req_ids, d_context_lens,
+                       num_seqs, max_context, partition_tokens, d_out, nullptr, 0, stream, nullptr,
+                       nullptr, 0, 0, 0, /*static_workspace=*/true);
   });
 }
 

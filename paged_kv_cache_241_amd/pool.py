@@ -374,3 +374,37 @@ class Pool:
             capi.check(self.lib.pa_append_decode(self.handle, layer, k.data_ptr(), v.data_ptr(),
                                                  slots.data_ptr(), *args), "pa_append_decode")
         return out
+
+    def append_decode_noalloc(self, layer: int, q, scale: float, block_tables, context_lens,
+                              max_context: int, k, v, slots, out=None, partition_tokens: int = 0,
+                              req_ids=None, stream=None):
+        """pa_append_decode_noalloc: pa_append_decode without a workspace (the
+        split-K partials go to the library's own device scratch)."""
+        import torch
+
+        assert self._device, "host-only pool"
+        b, hq, d = q.shape
+        assert q.is_cuda and q.is_contiguous() and q.dtype == self.torch_dtype and d == self.head_dim
+        assert context_lens.is_cuda and context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (b,)
+        stride = 0
+        if self.layout == "paged":
+            assert block_tables.is_cuda and block_tables.dtype == torch.int32
+            assert block_tables.is_contiguous() and block_tables.shape[0] == b
+            stride = int(block_tables.shape[1])
+        if req_ids is not None:
+            assert req_ids.is_cuda and req_ids.dtype == torch.int32 and tuple(req_ids.shape) == (b,)
+        for t in (k, v):
+            assert t.is_cuda and t.is_contiguous() and t.dtype == self.torch_dtype
+            assert tuple(t.shape) == (b, self.num_kv_heads, self.head_dim)
+        assert slots.is_cuda and slots.dtype == torch.int32 and tuple(slots.shape) == (b,)
+        if out is None:
+            out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
+        assert out.is_contiguous() and out.dtype == torch.float32 and tuple(out.shape) == (b, hq, d)
+        capi.check(self.lib.pa_append_decode_noalloc(
+            self.handle, layer, k.data_ptr(), v.data_ptr(), slots.data_ptr(), q.data_ptr(),
+            _DTYPES[self.kv_dtype], hq, float(scale),
+            block_tables.data_ptr() if self.layout == "paged" else None, stride,
+            req_ids.data_ptr() if req_ids is not None else None, context_lens.data_ptr(), b,
+            int(max_context), int(partition_tokens), out.data_ptr(), _stream_handle(stream)),
+            "pa_append_decode_noalloc")
+        return out

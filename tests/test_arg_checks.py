@@ -136,3 +136,19 @@ def test_slots_and_pairs():
     _, ln = c.block_tables([r], 1)
     c.check_decode_args(None, ln, 64, req_ids=[r], slots=s[-1:])
     _refused(c.check_decode_args, None, ln, 64, req_ids=[r], slots=s[-2:-1])
+
+
+def test_noalloc_decode_refuses_more_than_its_scratch_before_any_launch():
+    # 4096 sequences x 32 query heads x 32 partitions of split-K partials are
+    # far more than the library's 64 MiB: refused on the host
+    lib = capi.load()
+    p = Pool(host_only=True, num_layers=1, num_blocks=64, block_size=16, num_kv_heads=8,
+             head_dim=128, kv_dtype="bf16", layout="paged", max_seqs=4096, max_seq_len=8192)
+    need = p.workspace_bytes(4096, 32, 8192, 256)
+    assert need > capi.PA_NOALLOC_SCRATCH_BYTES
+    keep, addr = _fake(1 << 12)
+    st = lib.pa_append_decode_noalloc(p.handle, 0, addr, addr, addr, addr, capi.PA_BF16, 32,
+                                      ctypes.c_float(0.088), addr, 512, None, addr, 4096, 8192,
+                                      256, addr, None)
+    assert st == capi.PA_ERR_WORKSPACE, lib.pa_last_error()
+    assert str(capi.PA_NOALLOC_SCRATCH_BYTES).encode() in lib.pa_last_error()
