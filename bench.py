@@ -506,7 +506,7 @@ def _oracle_slice(job: dict) -> tuple:
     from oracle import attention as A
 
     conv = A.bf16_bits_to_f64 if job["bf16"] else A.f32_to_f64
-    kb, vb, lens, q, bs = job["kb"], job["vb"], job["lens"], job["q"], job["bs"]
+    kvb, lens, q, bs = job["kvb"], job["lens"], job["q"], job["bs"]
     done = n = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -514,7 +514,8 @@ def _oracle_slice(job: dict) -> tuple:
             for i, length in enumerate(lens):
                 length = int(length)
                 blocks = job["blocks"][i][: -(-length // bs)]
-                kr, vr = conv(A.k_rows(kb[blocks])), conv(A.v_rows(vb[blocks]))
+                kt, vt = A.pair_tiles(kvb[blocks], job["head_dim"], bs)
+                kr, vr = conv(A.k_rows(kt)), conv(A.v_rows(vt))
                 if job["paged"]:
                     local = range(len(blocks))
                     k = A.gather_paged(kr, local, length, bs)
@@ -547,15 +548,14 @@ def cpu_baseline(bench, seconds: float) -> dict | None:
 
     cfg = bench.cfg
     pool = bench.pool
-    if pool.k_cache is None:   # a demand-paged pool's caches cannot be read back
+    if pool.kv_cache is None:   # a demand-paged pool's cache cannot be read back
         return None
     paged = bench.layout == "paged"
+    # the layer's raw tile pairs [units][Hkv][2][d*BS]
     if cfg.kv_dtype == "bf16":
-        kb = pool.k_cache[0].view(torch.int16).cpu().numpy().view(np.uint16)
-        vb = pool.v_cache[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        kvb = pool.kv_cache[0].view(torch.int16).cpu().numpy().view(np.uint16)
     else:
-        kb = pool.k_cache[0].cpu().numpy()
-        vb = pool.v_cache[0].cpu().numpy()
+        kvb = pool.kv_cache[0].cpu().numpy()
     q = bench.q[0].float().cpu().numpy().astype(np.float64)
     if paged:
         tables, lens = pool.block_tables(bench.rids_np)
@@ -568,16 +568,15 @@ def cpu_baseline(bench, seconds: float) -> dict | None:
 
     def job(seqs, secs):
         # the slice's blocks copied out of the layer, renumbered in order
-        blocks, kparts, vparts, off = [], [], [], 0
+        blocks, parts, off = [], [], 0
         for s in seqs:
             nblk = -(-int(lens[s]) // bs)
             ids = (tables[s][:nblk] if paged else
                    np.arange(bench.batch[s] * per, bench.batch[s] * per + nblk))
-            kparts.append(kb[ids])
-            vparts.append(vb[ids])
+            parts.append(kvb[ids])
             blocks.append(np.arange(off, off + nblk))
             off += nblk
-        return {"kb": np.concatenate(kparts), "vb": np.concatenate(vparts), "blocks": blocks,
+        return {"kvb": np.concatenate(parts), "blocks": blocks, "head_dim": cfg.head_dim,
                 "lens": [int(lens[s]) for s in seqs], "q": q[list(seqs)], "bs": bs, "paged": paged,
                 "bf16": cfg.kv_dtype == "bf16", "scale": bench.scale, "seconds": secs,
                 "token_bytes": cfg.num_kv_heads * cfg.head_dim * elt * 2}

@@ -16,16 +16,20 @@
  * ---------------------------------------------------------------------------
  * Cache layout (device memory owned by the caller)
  * ---------------------------------------------------------------------------
- * The K cache and the V cache are two separate device arrays, element type
- * kv_dtype, for all layers.  Each layer is an array of tiles, one per (block,
- * KV head); VE = 16 / sizeof(element) (8 for bf16, 4 for fp32):
+ * One device array, element type kv_dtype, holds the K and V caches of all
+ * layers.  Each layer is an array of tile pairs, one pair per (block, KV
+ * head): the K tile of that block and head, then its V tile.  VE = 16 /
+ * sizeof(element) (8 for bf16, 4 for fp32):
  *
- *   K: [num_layers][units][num_kv_heads][head_dim/VE][block_size][VE]
- *   V: [num_layers][units][num_kv_heads][head_dim][block_size]
+ *   cache: [num_layers][units][num_kv_heads][2][tile]     (2: K, then V)
+ *   K tile [head_dim/VE][block_size][VE]
+ *   V tile [head_dim][block_size]
  *
  * The K tile keeps each token row in 16-byte chunks (chunk-major); the V tile
  * is dimension-major.  Both make the decode kernel's matrix-core operand
- * loads contiguous wave accesses.
+ * loads contiguous wave accesses, and a (block, head)'s K and V together are
+ * one contiguous run for the decode to read (8 KiB for bf16, 16 tokens,
+ * head_dim 128).
  *
  * PA_PAGED: units = num_blocks.  Block b holds, for every KV head,
  * block_size consecutive tokens; a sequence's blocks need not be adjacent and
@@ -40,15 +44,15 @@
  *
  * A "slot" names one token row: slot = u*block_size + o, u the block, o the
  * row in it (contiguous: slot = reqId*max_seq_len + position).  Element
- * (slot, head h, dim e) of layer l is, with tile = ((l*units + u)*num_kv_heads
- * + h) * head_dim * block_size:
- *   K: tile + ((e / VE) * block_size + o) * VE + e % VE
- *   V: tile + e * block_size + o
+ * (slot, head h, dim e) of layer l is, with pair = ((l*units + u)*num_kv_heads
+ * + h) * 2 * head_dim * block_size (in elements from the array's start):
+ *   K: pair + ((e / VE) * block_size + o) * VE + e % VE
+ *   V: pair + head_dim * block_size + e * block_size + o
  *
  * ---------------------------------------------------------------------------
  * Conventions
  * ---------------------------------------------------------------------------
- * Ownership: the caller owns all device memory (caches, q, out, tables, slots,
+ * Ownership: the caller owns all device memory (cache, q, out, tables, slots,
  *   workspace) and keeps it alive while the pool uses it.  The library owns
  *   only the opaque host-side pa_pool and frees it in pa_destroy_pool.  No
  *   function allocates device memory, except that a demand-paged pool
@@ -96,7 +100,7 @@ typedef struct pa_pool_desc {
   int32_t block_size;    /* tokens per block: 8, 16 (the pages' default) or 32 */
   int32_t num_kv_heads;  /* >= 1 */
   int32_t head_dim;      /* 64 or 128 */
-  pa_dtype kv_dtype;     /* element type of both caches */
+  pa_dtype kv_dtype;     /* element type of the cache (K and V) */
   pa_layout layout;
   int32_t max_seqs;      /* live requests at once; reqIds are 0 .. max_seqs-1 */
   int32_t max_seq_len;   /* S: most tokens per request; contiguous: multiple of block_size */
@@ -119,8 +123,8 @@ typedef struct pa_stats {
 
 typedef struct pa_pool pa_pool; /* opaque, host memory */
 
-/* Bytes of ONE of the two cache arrays (K or V) described by desc, or 0 if
- * desc is invalid.  The caller allocates two arrays of this size. */
+/* Bytes of the cache array (K and V of every layer) described by desc, or 0
+ * if desc is invalid. */
 size_t pa_cache_bytes(const pa_pool_desc* desc);
 
 /* KV bytes one token takes over all layers, K plus V:
@@ -129,39 +133,39 @@ size_t pa_cache_bytes(const pa_pool_desc* desc);
 size_t pa_bytes_per_token(const pa_pool_desc* desc);
 
 /* Create a cache of fixed-size blocks over caller memory ([ROC] paging
- * paragraph).  d_k_cache / d_v_cache: device arrays of pa_cache_bytes(desc)
- * bytes each, 16-byte aligned.  Host-only: touches no device memory.  All
- * blocks start free and are handed out in ascending id order; all request ids
- * start free, 0 first.  *out receives the handle. */
-pa_status pa_create_pool(const pa_pool_desc* desc, void* d_k_cache, void* d_v_cache,
-                         pa_pool** out);
+ * paragraph).  d_cache: device array of pa_cache_bytes(desc) bytes, 16-byte
+ * aligned.  Host-only: touches no device memory.  All blocks start free and
+ * are handed out in ascending id order; all request ids start free, 0 first.
+ * *out receives the handle. */
+pa_status pa_create_pool(const pa_pool_desc* desc, void* d_cache, pa_pool** out);
 
-/* Free the host handle.  The caches are the caller's (a demand-paged pool's
- * are the library's: they are unmapped and freed here, so no queued or
- * running work may still use them). */
+/* Free the host handle.  The cache is the caller's (a demand-paged pool's is
+ * the library's: it is unmapped and freed here, so no queued or running work
+ * may still use it). */
 pa_status pa_destroy_pool(pa_pool* pool);
 
 /* ---- demand-paged contiguous caches ([VAC] 5.2.1-5.2.3) -------------------
- * The contiguous layout with its K and V caches backed on demand: the library
- * reserves the virtual range of both caches (num_layers x max_seqs x S each,
- * request reqId's sub-range at reqId x S, as pa_create_pool lays them out)
- * without physical memory, and pa_reserve maps physical pages into a
- * request's sub-range of every layer, K and V, before it hands out slots
- * past the pages already there.  Pages are 2 MiB where one request's
- * sub-range, S x num_kv_heads x head_dim x elt bytes, is a multiple of that,
- * else the device's allocation granularity (which it must then be a multiple
- * of); each page is its own physical allocation.  physical_bytes caps the memory mapped: a pa_reserve that would pass
- * it fails with PA_ERR_NO_BLOCKS and changes nothing (PA_ERR_HIP from the
- * mapping calls may leave pages mapped but changes no length).  A freed
- * request's pages stay mapped for the next request given its id (ids are
- * reused last-freed first) until pa_vmm_trim.  Everything else is the
- * contiguous pool's.  PA_ERR_UNSUPPORTED: the device or the sizes do not
- * allow it. */
+ * The contiguous layout with its cache backed on demand: the library reserves
+ * the virtual range of the cache (num_layers x max_seqs x one request's
+ * sub-range, request reqId's sub-range at reqId x S, as pa_create_pool lays
+ * it out) without physical memory, and pa_reserve maps physical pages into a
+ * request's sub-range of every layer before it hands out slots past the pages
+ * already there.  A request's sub-range of one layer holds its S /
+ * block_size blocks, K and V: S x num_kv_heads x head_dim x elt x 2 bytes.
+ * Pages are 2 MiB where that is a multiple of 2 MiB, else the device's
+ * allocation granularity (which it must then be a multiple of); each page is
+ * its own physical allocation.  physical_bytes caps the memory mapped: a
+ * pa_reserve that would pass it fails with PA_ERR_NO_BLOCKS and changes
+ * nothing (PA_ERR_HIP from the mapping calls may leave pages mapped but
+ * changes no length).  A freed request's pages stay mapped for the next
+ * request given its id (ids are reused last-freed first) until pa_vmm_trim.
+ * Everything else is the contiguous pool's.  PA_ERR_UNSUPPORTED: the device
+ * or the sizes do not allow it. */
 typedef struct pa_vmm_stats {
   int64_t page_bytes;    /* physical page (allocation granularity) */
-  int64_t mapped_bytes;  /* physical memory mapped, all layers, K and V */
+  int64_t mapped_bytes;  /* physical memory mapped, all layers */
   int64_t budget_bytes;  /* physical_bytes rounded down to whole pages */
-  int64_t region_bytes;  /* one request's sub-range of one layer's K (or V) */
+  int64_t region_bytes;  /* one request's sub-range of one layer (K and V) */
 } pa_vmm_stats;
 
 pa_status pa_create_pool_vmm(const pa_pool_desc* desc, size_t physical_bytes, pa_pool** out);
@@ -275,9 +279,10 @@ pa_status pa_decode_shared(pa_pool* pool, int32_t layer, const void* d_q, pa_dty
  * grow (pa_reserve), fork, or have its table read (PA_ERR_INVALID_ARG) until
  * it is swapped in; pa_seq_free drops it.  Its image, in memory the caller
  * owns, holds every layer's copy of its blocks:
- *     image[layer][j][0 = K, 1 = V][num_kv_heads][tile]
- * for j < ceil(L / block_size) in logical order, each tile as the pool lays it
- * out (K [head_dim/VE][block_size][VE], V [head_dim][block_size]), i.e.
+ *     image[layer][j][num_kv_heads][0 = K, 1 = V][tile]
+ * for j < ceil(L / block_size) in logical order, each block's tile pairs as
+ * the pool lays them out (K [head_dim/VE][block_size][VE], then V
+ * [head_dim][block_size]), i.e.
  * num_layers * ceil(L/BS) * 2 * num_kv_heads * head_dim * BS * elt bytes.
  * Whole blocks are copied, rows past L included.  Sharing is not kept: blocks
  * the request shared are copied out in full and come back as its own.
@@ -420,7 +425,7 @@ pa_status pa_append_decode_noalloc(pa_pool* pool, int32_t layer, const void* d_k
 
 /* ---- host-side checks of the device arrays (debugging aids) ---------------
  * The device calls trust their device arrays (see Validation above): an entry
- * out of range makes a kernel read or write outside the caches.  These calls
+ * out of range makes a kernel read or write outside the cache.  These calls
  * take HOST copies of those arrays and check them against the pool, on the
  * CPU; they launch nothing and change nothing.  PA_OK, or PA_ERR_INVALID_ARG
  * with the first offending entry in pa_last_error(). */

@@ -6,11 +6,13 @@ nothing is blocked, fused or reordered beyond the definitions below.
 Cache layout.  The pages fix none; the C library documents this one, and the
 functions here read it as written there:
 
-* A layer's K (or V) cache is an array of tiles, one per (block, KV head):
-  shape ``[units][Hkv][tile]``.  The K tile is ``[d/VE][BS][VE]`` (the row of a
-  token cut into 16-byte chunks of ``VE`` elements, chunk-major), the V tile is
-  ``[d][BS]`` (dimension-major).  ``k_rows`` / ``v_rows`` turn tiles into plain
-  token rows ``[units][Hkv][BS][d]``, which is what the gathers read.
+* One array holds a layer's K and V: an array of tile pairs, one per (block,
+  KV head), shape ``[units][Hkv][pair]`` with ``pair`` = the K tile's
+  ``d*BS`` elements followed by the V tile's ``d*BS``.  ``pair_tiles`` splits
+  it.  The K tile is ``[d/VE][BS][VE]`` (the row of a token cut into 16-byte
+  chunks of ``VE`` elements, chunk-major), the V tile is ``[d][BS]``
+  (dimension-major).  ``k_rows`` / ``v_rows`` turn tiles into plain token rows
+  ``[units][Hkv][BS][d]``, which is what the gathers read.
 * paged: ``units`` are the physical blocks; block ``b`` holds BS consecutive
   token rows of every KV head.
 * contiguous: request ``r`` owns the ``S/BS`` consecutive blocks starting at
@@ -55,6 +57,28 @@ def f32_to_f64(x: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # reading the documented tile layout
 # --------------------------------------------------------------------------
+
+def pair_tiles(cache: np.ndarray, head_dim: int, block_size: int):
+    """K tiles and V tiles of a cache held as tile pairs.
+
+    ``cache`` holds raw elements (any dtype; VE = 16 bytes / element size),
+    shape ``[..., 2*d*BS]`` or ``[..., 2, d*BS]``: per (block, KV head) the K
+    tile's ``d*BS`` elements, then the V tile's.  Returns views
+    ``(k_tiles [..., d/VE, BS, VE], v_tiles [..., d, BS])``.
+    """
+    cache = np.asarray(cache)
+    n = head_dim * block_size
+    if cache.shape[-2:] == (2, n):
+        lead = cache.shape[:-2]
+    else:
+        assert cache.shape[-1] == 2 * n, "last axis must be one tile pair"
+        lead = cache.shape[:-1]
+    flat = cache.reshape(*lead, 2 * n)
+    ve = 16 // flat.itemsize
+    k = flat[..., :n].reshape(*lead, head_dim // ve, block_size, ve)
+    v = flat[..., n:].reshape(*lead, head_dim, block_size)
+    return k, v
+
 
 def k_rows(k_tiles: np.ndarray) -> np.ndarray:
     """K tiles ``[..., d/VE, BS, VE]`` as token rows ``[..., BS, d]``.

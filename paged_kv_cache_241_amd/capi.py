@@ -106,7 +106,7 @@ def load() -> ctypes.CDLL:
     sig = {
         "pa_cache_bytes": (ctypes.c_size_t, [ctypes.POINTER(pa_pool_desc)]),
         "pa_bytes_per_token": (ctypes.c_size_t, [ctypes.POINTER(pa_pool_desc)]),
-        "pa_create_pool": (ctypes.c_int, [ctypes.POINTER(pa_pool_desc), _vp, _vp, ctypes.POINTER(_vp)]),
+        "pa_create_pool": (ctypes.c_int, [ctypes.POINTER(pa_pool_desc), _vp, ctypes.POINTER(_vp)]),
         "pa_destroy_pool": (ctypes.c_int, [_vp]),
         "pa_set_free_order": (ctypes.c_int, [_vp, _p32, _i32]),
         "pa_seq_add": (ctypes.c_int, [_vp, _p32]),

@@ -1,6 +1,7 @@
 // Device helpers shared by the decode kernels (kernels.hip, decode_shared.hip):
 // wave constants, vector types, cache-read flavours, bf16 packing, and the
-// per-shape constants of the tile layout (K [D/VE][BS][VE], V [D][BS]).
+// per-shape constants of the tile layout (K [D/VE][BS][VE], then V [D][BS],
+// per (block, head)).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -88,7 +89,8 @@ struct Geo {
   static constexpr int VE = 16 / ELT;          // elements per 16-byte K chunk
   static constexpr int NX = D / (4 * VE);      // 16-byte K loads per lane per chunk
   static constexpr int NN = D / 16;            // 16-column output tiles
-  static constexpr int TILE = D * BS * ELT;    // bytes of one (block, head) tile
+  static constexpr int TILE = D * BS * ELT;    // bytes of one K (or V) tile of a (block, head)
+  static constexpr int PAIR = 2 * TILE;        // a (block, head)'s K tile, then its V tile
 };
 
 }  // namespace

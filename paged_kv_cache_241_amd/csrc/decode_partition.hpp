@@ -58,7 +58,7 @@ template <int KIND, int D, int BS, int W, bool NT, bool PIPE = false, bool BAL =
 __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, const DecodeArgs& a, int bid,
                                                       int nblocks, float* lds) {
   using GG = Geo<KIND, D, BS>;
-  constexpr int NX = GG::NX, NN = GG::NN, TILE = GG::TILE, ELT = GG::ELT;
+  constexpr int NX = GG::NX, NN = GG::NN, TILE = GG::TILE, PAIR = GG::PAIR, ELT = GG::ELT;
   constexpr int kWaves = W;
   constexpr int kThreads = W * kWave;
   // V operand per lane per output tile: 4 consecutive tokens of one dim
@@ -176,8 +176,9 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   }
   const float c2 = a.scale * kLog2e;
 
-  const char* kl = geo.k_base + static_cast<int64_t>(a.layer) * geo.layer_bytes;
-  const char* vl = geo.v_base + static_cast<int64_t>(a.layer) * geo.layer_bytes;
+  // K tiles of the layer; each V tile follows its K tile
+  const char* kl = geo.base + static_cast<int64_t>(a.layer) * geo.layer_bytes;
+  const char* vl = kl + TILE;
   const int32_t* table = nullptr;
   int64_t first_block = 0;
   if (geo.paged) {
@@ -186,12 +187,12 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
     const int rid = a.req_ids ? a.req_ids[s] : s;
     first_block = static_cast<int64_t>(rid) * geo.blocks_per_seq;
   }
-  // byte offset of tile (block of token t, kvh); t is clamped into the
-  // context so that every address stays inside a block the sequence owns
+  // byte offset of the tile pair (block of token t, kvh); t is clamped into
+  // the context so that every address stays inside a block the sequence owns
   auto tile_of = [&](int t) -> int64_t {
     t = min(t, L - 1);
     const int64_t u = geo.paged ? static_cast<int64_t>(table[t / BS]) : first_block + t / BS;
-    return (u * hkv + kvh) * TILE;
+    return (u * hkv + kvh) * PAIR;
   };
 
   float m = -INFINITY;  // running max of head n (log2 units)
@@ -214,7 +215,7 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
     if constexpr (BS >= kChunk) {
       // the chunk lies in one block: a wave-uniform tile base plus a 32-bit
       // lane offset (rows past the context stay inside the tile)
-      const int64_t tile = (u * hkv + kvh) * TILE;
+      const int64_t tile = (u * hkv + kvh) * PAIR;
       const char* kt = kl + tile;
       const char* vt = vl + tile;
       const int row0 = (c * kChunk) % BS;
@@ -247,6 +248,10 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
         else vv[nb] = kv16<NT>(vt + (nb * 16 + n) * BS * ELT);
       }
     }
+    // every load of the chunk issues before anything that waits for one:
+    // left to itself the scheduler slots the first score MFMAs (and their
+    // waits) between the K and the V loads, so V leaves for memory only
+    // after K has come back
   };
 
   // the new token's K and V replace what the cache holds at position L-1
@@ -529,17 +534,18 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
         const int64_t u = slot / BS;
         const int o = slot % BS;                 // row in the block
         const int row0 = o - o % kChunk;          // the chunk's first row
-        const int64_t tile = static_cast<int64_t>(a.layer) * geo.layer_bytes + (u * hkv + kvh) * TILE;
+        char* kt = geo.base + static_cast<int64_t>(a.layer) * geo.layer_bytes + (u * hkv + kvh) * PAIR;
+        char* vt = kt + TILE;
         constexpr int kVUnits = D * kChunk * ELT / 16;   // 16-byte units of the chunk's V
         constexpr int kPerRow = kChunk * ELT / 16;        // units per dim row
         for (int t = tid; t < kVUnits; t += kThreads) {
           const int e = t / kPerRow, q = t % kPerRow;
-          *reinterpret_cast<uint4*>(geo.v_base + tile + (e * BS + row0) * ELT + q * 16) =
+          *reinterpret_cast<uint4*>(vt + (e * BS + row0) * ELT + q * 16) =
               *reinterpret_cast<const uint4*>(stage_v + t * 16);
         }
         for (int t = tid; t < 2 * kRowVec; t += kThreads) {
           const int r = t / kRowVec, q = t % kRowVec;   // row (o & ~1) + r, piece q
-          *reinterpret_cast<uint4*>(geo.k_base + tile + (q * BS + (o & ~1) + r) * 16) =
+          *reinterpret_cast<uint4*>(kt + (q * BS + (o & ~1) + r) * 16) =
               *reinterpret_cast<const uint4*>(stage_k + r * D * ELT + q * 16);
         }
       }
@@ -553,10 +559,10 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
     const int q = lane;
     const int64_t u = slot / BS;
     const int o = slot % BS;
-    const int64_t tile = static_cast<int64_t>(a.layer) * geo.layer_bytes + (u * hkv + kvh) * TILE;
-    *reinterpret_cast<uint4*>(geo.k_base + tile + (q * BS + o) * 16) = sm_new[q];
+    char* kt = geo.base + static_cast<int64_t>(a.layer) * geo.layer_bytes + (u * hkv + kvh) * PAIR;
+    *reinterpret_cast<uint4*>(kt + (q * BS + o) * 16) = sm_new[q];
     const uint4 vw = sm_new[kRowVec + q];
-    char* vt = geo.v_base + tile;
+    char* vt = kt + TILE;
     const uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
     if constexpr (KIND == kBF16) {
 #pragma unroll

@@ -68,7 +68,7 @@ template <int KIND, int D, int BS>
 __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeArgs& a, const SharedArgs& g,
                                             int w, char* lds) {
   using GG = Geo<KIND, D, BS>;
-  constexpr int NX = GG::NX, NN = GG::NN, TILE = GG::TILE, ELT = GG::ELT;
+  constexpr int NX = GG::NX, NN = GG::NN, TILE = GG::TILE, PAIR = GG::PAIR, ELT = GG::ELT;
   constexpr int kThreads = kSharedWaves * kWave;
   constexpr int kUnits = D * ELT;  // 16-byte units of one chunk's K, and of its V
   // Stages of STEP consecutive chunks move through LDS (double buffered).
@@ -129,8 +129,9 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
   }
   const float c2 = a.scale * kLog2e;
 
-  const char* kl = geo.k_base + static_cast<int64_t>(a.layer) * geo.layer_bytes;
-  const char* vl = geo.v_base + static_cast<int64_t>(a.layer) * geo.layer_bytes;
+  // K tiles of the layer; each V tile follows its K tile
+  const char* kl = geo.base + static_cast<int64_t>(a.layer) * geo.layer_bytes;
+  const char* vl = kl + TILE;
   // the group's blocks are its first member's (all members hold the same ones)
   const const_i32_ptr table = reinterpret_cast<const_i32_ptr>(
       reinterpret_cast<uintptr_t>(a.tables + static_cast<int64_t>(first) * a.table_stride));
@@ -171,7 +172,7 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
       for (int j = 0; j < STEP; ++j) {
         const int c = min(cb + st * STEP + j, ce - 1);
         const int64_t blk = table[__builtin_amdgcn_readfirstlane((c * kChunk) / BS)];
-        const int64_t tile = (blk * hkv + kvh) * TILE;
+        const int64_t tile = (blk * hkv + kvh) * PAIR;
         kb[j] = kl + tile + ((c * kChunk) % BS) * 16;
         vb[j] = vl + tile + ((c * kChunk) % BS) * ELT;
       }
@@ -207,8 +208,8 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
           const int tv = c * kChunk + (uu % ELT) * (16 / ELT);
           const int32_t* trow = a.tables + static_cast<int64_t>(first) * a.table_stride;
           const int64_t bk = trow[t / BS], bv = trow[tv / BS];
-          sk[k] = kv16<true>(kl + (bk * hkv + kvh) * TILE + ((uu / 16) * BS + t % BS) * 16);
-          sv[k] = kv16<true>(vl + (bv * hkv + kvh) * TILE + ((uu / ELT) * BS + tv % BS) * ELT);
+          sk[k] = kv16<true>(kl + (bk * hkv + kvh) * PAIR + ((uu / 16) * BS + t % BS) * 16);
+          sv[k] = kv16<true>(vl + (bv * hkv + kvh) * PAIR + ((uu / ELT) * BS + tv % BS) * ELT);
         }
       }
     }

@@ -293,11 +293,10 @@ __device__ __forceinline__ void append_item(const CacheGeom& g, int32_t layer, c
   if (slot < 0) return;
   const int64_t u = slot / g.block_size;
   const int o = slot % g.block_size;
-  const int64_t tile = static_cast<int64_t>(layer) * g.layer_bytes +
-                       (u * g.num_kv_heads + h) * (static_cast<int64_t>(g.head_dim) * g.block_size * g.elt);
-  *reinterpret_cast<uint4*>(g.k_base + tile + (static_cast<int64_t>(q) * g.block_size + o) * 16) = k[idx];
+  char* kt = g.base + static_cast<int64_t>(layer) * g.layer_bytes + (u * g.num_kv_heads + h) * 2 * g.tile_bytes;
+  *reinterpret_cast<uint4*>(kt + (static_cast<int64_t>(q) * g.block_size + o) * 16) = k[idx];
   const uint4 w = v[idx];
-  char* vt = g.v_base + tile;
+  char* vt = kt + g.tile_bytes;
   const int d0 = q * ve;
   if (g.elt == 2) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -352,21 +351,18 @@ __global__ __launch_bounds__(256) void append_kv_bulk_kernel(CacheGeom g, int32_
   append_item(g, layer, k, v, slots, token * pieces + hp);
 }
 
+// Workgroup (pair, layer) copies block src's tile pairs of the layer (every
+// KV head, K and V: one contiguous run) onto block dst's.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CacheGeom g,
                                                           const int32_t* __restrict__ pairs) {
   const int pi = blockIdx.x;
   const int layer = blockIdx.y;
   const int64_t src = pairs[2 * pi], dst = pairs[2 * pi + 1];
-  const int64_t bb = static_cast<int64_t>(g.num_kv_heads) * g.block_size * g.head_dim * g.elt;
+  const int64_t bb = static_cast<int64_t>(g.num_kv_heads) * 2 * g.tile_bytes;
   const int64_t lb = static_cast<int64_t>(layer) * g.layer_bytes;
-  const uint4* ks = reinterpret_cast<const uint4*>(g.k_base + lb + src * bb);
-  const uint4* vs = reinterpret_cast<const uint4*>(g.v_base + lb + src * bb);
-  uint4* kd = reinterpret_cast<uint4*>(g.k_base + lb + dst * bb);
-  uint4* vd = reinterpret_cast<uint4*>(g.v_base + lb + dst * bb);
-  for (int64_t x = threadIdx.x; x < bb / 16; x += 256) {
-    kd[x] = ks[x];
-    vd[x] = vs[x];
-  }
+  const uint4* s = reinterpret_cast<const uint4*>(g.base + lb + src * bb);
+  uint4* d = reinterpret_cast<uint4*>(g.base + lb + dst * bb);
+  for (int64_t x = threadIdx.x; x < bb / 16; x += 256) d[x] = s[x];
 }
 
 template <int KIND, int D, int BS, bool PIPE, bool BAL = false>

@@ -13,18 +13,20 @@ enum Kind : int { kF32 = 0, kBF16 = 1 };
 // Waves per workgroup of the decode partition kernel.
 constexpr int kDecodeWaves = 4;
 
-// Cache geometry.  Per layer, K and V are arrays of tiles, one tile per
-// (block, KV head):
+// Cache geometry.  One array holds K and V of every layer.  Per layer it is
+// an array of tile pairs, one pair per (block, KV head): the K tile, then the
+// V tile of the same block and head, so that the two form one contiguous run
+// (2 x 4 KiB for bf16, 16 tokens, head_dim 128):
 //   K tile [head_dim/VE][block_size][VE]  (16-byte chunks, VE = 16/elt)
 //   V tile [head_dim][block_size]
-// Tile (u, h) starts at (u*num_kv_heads + h) * tile_bytes from the layer base.
-// Paged: u is the physical block.  Contiguous: request r owns blocks
-// r*blocks_per_seq .. r*blocks_per_seq + blocks_per_seq - 1.  A slot is
-// u*block_size + row.
+// Pair (u, h) of layer l starts at l*layer_bytes + (u*num_kv_heads + h) *
+// 2*tile_bytes from the base; its V tile tile_bytes further on.  Paged: u is
+// the physical block.  Contiguous: request r owns blocks r*blocks_per_seq ..
+// r*blocks_per_seq + blocks_per_seq - 1.  A slot is u*block_size + row.
 struct CacheGeom {
-  char* k_base = nullptr;      // layer 0 of the K cache
-  char* v_base = nullptr;
-  int64_t layer_bytes = 0;     // bytes of one layer of one cache
+  char* base = nullptr;        // layer 0, block 0, head 0, K tile
+  int64_t layer_bytes = 0;     // bytes of one layer (K and V)
+  int64_t tile_bytes = 0;      // bytes of one K (or V) tile: head_dim * block_size * elt
   int32_t num_layers = 0;
   int32_t num_kv_heads = 0;
   int32_t head_dim = 0;
@@ -40,8 +42,9 @@ hipError_t launch_append(const CacheGeom& g, int32_t layer, const void* k, const
 hipError_t launch_copy_blocks(const CacheGeom& g, const int32_t* pairs, int32_t n,
                               hipStream_t stream);
 
-// Swap image <-> blocks: blocks[j] (host array, n ids) in every layer, K and V,
-// to or from image[layer][j][K|V][num_kv_heads][tile] (device-addressable).
+// Swap image <-> blocks: blocks[j] (host array, n ids) in every layer, to or
+// from image[layer][j][num_kv_heads][K|V][tile] (device-addressable): each
+// block's tile pairs of a layer, as the cache holds them.
 hipError_t launch_swap(const CacheGeom& g, const int32_t* blocks, int32_t n, char* image,
                        bool to_image, hipStream_t stream);
 

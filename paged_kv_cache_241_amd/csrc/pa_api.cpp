@@ -89,10 +89,16 @@ std::string check_desc(const pa_pool_desc* d) {
   return "";
 }
 
+// Bytes of one block of one layer: every KV head's K and V tiles.
+int64_t block_bytes(const pa_pool_desc* d) {
+  return static_cast<int64_t>(d->num_kv_heads) * 2 * d->head_dim * d->block_size * elt_bytes(d->kv_dtype);
+}
+
+// Bytes of one layer of the cache (K and V).
 int64_t layer_bytes(const pa_pool_desc* d) {
-  const int64_t units = d->layout == PA_PAGED ? d->num_blocks : d->max_seqs;
-  const int64_t unit = d->layout == PA_PAGED ? d->block_size : d->max_seq_len;
-  return units * d->num_kv_heads * unit * d->head_dim * elt_bytes(d->kv_dtype);
+  const int64_t blocks = d->layout == PA_PAGED ? d->num_blocks
+                                               : static_cast<int64_t>(d->max_seqs) * (d->max_seq_len / d->block_size);
+  return blocks * block_bytes(d);
 }
 
 // Decode launch shape.  A workgroup of W waves handles one (sequence, KV
@@ -137,11 +143,11 @@ bool bad_partition(const pa_pool* p, int32_t partition_tokens) {
 
 int32_t num_queries_per_kv(int32_t num_q_heads, int32_t num_kv_heads) { return num_q_heads / num_kv_heads; }
 
-pa::CacheGeom make_geom(const pa_pool_desc* desc, void* k, void* v) {
+pa::CacheGeom make_geom(const pa_pool_desc* desc, void* cache) {
   pa::CacheGeom g;
-  g.k_base = static_cast<char*>(k);
-  g.v_base = static_cast<char*>(v);
+  g.base = static_cast<char*>(cache);
   g.layer_bytes = layer_bytes(desc);
+  g.tile_bytes = static_cast<int64_t>(desc->head_dim) * desc->block_size * elt_bytes(desc->kv_dtype);
   g.num_layers = desc->num_layers;
   g.num_kv_heads = desc->num_kv_heads;
   g.head_dim = desc->head_dim;
@@ -216,18 +222,16 @@ size_t pa_bytes_per_token(const pa_pool_desc* desc) {
          elt_bytes(desc->kv_dtype);
 }
 
-pa_status pa_create_pool(const pa_pool_desc* desc, void* d_k_cache, void* d_v_cache,
-                         pa_pool** out) {
+pa_status pa_create_pool(const pa_pool_desc* desc, void* d_cache, pa_pool** out) {
   return guarded("create_pool", [&]() -> pa_status {
     if (out == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool: null output");
     *out = nullptr;
     const std::string why = check_desc(desc);
     if (!why.empty()) return fail(PA_ERR_INVALID_ARG, "create_pool: " + why);
-    if (d_k_cache == nullptr || d_v_cache == nullptr)
-      return fail(PA_ERR_INVALID_ARG, "create_pool: null cache pointer");
-    if ((reinterpret_cast<uintptr_t>(d_k_cache) | reinterpret_cast<uintptr_t>(d_v_cache)) & 15)
-      return fail(PA_ERR_INVALID_ARG, "create_pool: caches must be 16-byte aligned");
-    pa_pool* p = new (std::nothrow) pa_pool(*desc, make_geom(desc, d_k_cache, d_v_cache));
+    if (d_cache == nullptr) return fail(PA_ERR_INVALID_ARG, "create_pool: null cache pointer");
+    if (reinterpret_cast<uintptr_t>(d_cache) & 15)
+      return fail(PA_ERR_INVALID_ARG, "create_pool: the cache must be 16-byte aligned");
+    pa_pool* p = new (std::nothrow) pa_pool(*desc, make_geom(desc, d_cache));
     if (p == nullptr) return fail(PA_ERR_NO_MEMORY, "create_pool: out of host memory");
     *out = p;
     return PA_OK;
@@ -253,7 +257,7 @@ pa_status pa_create_pool_vmm(const pa_pool_desc* desc, size_t physical_bytes, pa
     const std::string err =
         pa::VirtualCache::create(desc->num_layers, desc->max_seqs, region, physical_bytes, device, &vc);
     if (!err.empty()) return fail(PA_ERR_UNSUPPORTED, "create_pool_vmm: " + err);
-    pa_pool* p = new (std::nothrow) pa_pool(*desc, make_geom(desc, vc->k_base(), vc->v_base()));
+    pa_pool* p = new (std::nothrow) pa_pool(*desc, make_geom(desc, vc->base()));
     if (p == nullptr) {
       delete vc;
       return fail(PA_ERR_NO_MEMORY, "create_pool_vmm: out of host memory");
@@ -349,8 +353,7 @@ pa_status pa_reserve(pa_pool* pool, const int32_t* req_ids, int32_t n, const int
       if (total > slots_cap || (total > 0 && slots_out == nullptr))
         return fail(PA_ERR_INVALID_ARG, "reserve: slots_out holds " + std::to_string(slots_cap) +
                                             " slots, " + std::to_string(total) + " needed");
-      const int64_t unit = static_cast<int64_t>(pool->desc.num_kv_heads) * pool->desc.head_dim *
-                           pool->desc.block_size * elt_bytes(pool->desc.kv_dtype);
+      const int64_t unit = block_bytes(&pool->desc);
       std::vector<int64_t> bytes(n);
       int64_t more = 0;
       for (int32_t i = 0; i < n; ++i) {
@@ -776,8 +779,7 @@ pa_status pa_check_decode_args(const pa_pool* pool, const int32_t* h_block_table
         if (rid < 0 || rid >= d.max_seqs)
           return fail(PA_ERR_INVALID_ARG, at + ": request id " + std::to_string(rid) + " outside [0, max_seqs)");
         if (pool->vmm != nullptr) {
-          const int64_t unit = static_cast<int64_t>(d.num_kv_heads) * d.head_dim * bs * elt_bytes(d.kv_dtype);
-          if (nblk * unit > pool->vmm->region_mapped(rid))
+          if (nblk * block_bytes(&d) > pool->vmm->region_mapped(rid))
             return fail(PA_ERR_INVALID_ARG, at + ": length " + std::to_string(L) + " reaches past the pages mapped for request " +
                                                 std::to_string(rid));
         }
@@ -817,10 +819,9 @@ pa_status pa_check_slots(const pa_pool* pool, const int32_t* h_slots, int32_t n)
         return fail(PA_ERR_INVALID_ARG, w + ": slot " + std::to_string(slot) + " (token " + std::to_string(i) +
                                             ") is not a row of the pool");
       if (pool->vmm != nullptr) {
-        const int64_t unit = static_cast<int64_t>(d.num_kv_heads) * d.head_dim * d.block_size * elt_bytes(d.kv_dtype);
         const int32_t rid = slot / d.max_seq_len;
         const int64_t pos = slot % d.max_seq_len;
-        if ((pos / d.block_size + 1) * unit > pool->vmm->region_mapped(rid))
+        if ((pos / d.block_size + 1) * block_bytes(&d) > pool->vmm->region_mapped(rid))
           return fail(PA_ERR_INVALID_ARG, w + ": slot " + std::to_string(slot) + " lies in an unmapped page");
       }
       taken.push_back(slot);

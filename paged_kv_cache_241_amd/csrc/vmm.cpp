@@ -1,4 +1,4 @@
-// Demand-paged contiguous K and V caches (see vmm.hpp).
+// Demand-paged contiguous KV cache (see vmm.hpp).
 #include "vmm.hpp"
 
 namespace pa {
@@ -50,20 +50,13 @@ std::string VirtualCache::create(int32_t num_layers, int32_t max_seqs, int64_t r
   vc->reserved_ = static_cast<size_t>(num_layers) * max_seqs * region_bytes;
   vc->pages_.assign(max_seqs, 0);
   vc->maps_.resize(max_seqs);
-  void* k = nullptr;
-  void* v = nullptr;
-  e = hipMemAddressReserve(&k, vc->reserved_, gran, nullptr, 0);
+  void* base = nullptr;
+  e = hipMemAddressReserve(&base, vc->reserved_, gran, nullptr, 0);
   if (e != hipSuccess) {
     delete vc;
     return hip_err("hipMemAddressReserve", e);
   }
-  vc->k_base_ = static_cast<char*>(k);
-  e = hipMemAddressReserve(&v, vc->reserved_, gran, nullptr, 0);
-  if (e != hipSuccess) {
-    delete vc;
-    return hip_err("hipMemAddressReserve", e);
-  }
-  vc->v_base_ = static_cast<char*>(v);
+  vc->base_ = static_cast<char*>(base);
   *out = vc;
   return "";
 }
@@ -71,15 +64,14 @@ std::string VirtualCache::create(int32_t num_layers, int32_t max_seqs, int64_t r
 VirtualCache::~VirtualCache() {
   for (auto& list : maps_)
     for (const Mapping& m : list) unmap(m);
-  if (k_base_) (void)hipMemAddressFree(k_base_, reserved_);
-  if (v_base_) (void)hipMemAddressFree(v_base_, reserved_);
+  if (base_) (void)hipMemAddressFree(base_, reserved_);
   (void)hipGetLastError();
 }
 
 int64_t VirtualCache::bytes_short(int32_t rid, int64_t bytes) const {
   const int64_t want = (bytes + page_ - 1) / page_;
   const int64_t more = want > pages_[rid] ? want - pages_[rid] : 0;
-  return more * page_ * 2 * num_layers_;
+  return more * page_ * num_layers_;
 }
 
 std::string VirtualCache::map_range(char* addr, size_t size, Mapping* m) const {
@@ -121,30 +113,28 @@ std::string VirtualCache::grow(int32_t rid, int64_t bytes) {
   std::vector<Mapping>& list = maps_[rid];
   const size_t before = list.size();
   for (int32_t l = 0; l < num_layers_; ++l) {
-    for (char* base : {k_base_, v_base_}) {
-      char* region = base + (static_cast<int64_t>(l) * max_seqs_ + rid) * region_;
-      for (int64_t pg = have; pg < want; ++pg) {
-        Mapping m{};
-        const std::string err = map_range(region + pg * page_, static_cast<size_t>(page_), &m);
-        if (!err.empty()) {
-          while (list.size() > before) {
-            unmap(list.back());
-            list.pop_back();
-          }
-          return err;
+    char* region = base_ + (static_cast<int64_t>(l) * max_seqs_ + rid) * region_;
+    for (int64_t pg = have; pg < want; ++pg) {
+      Mapping m{};
+      const std::string err = map_range(region + pg * page_, static_cast<size_t>(page_), &m);
+      if (!err.empty()) {
+        while (list.size() > before) {
+          unmap(list.back());
+          list.pop_back();
         }
-        list.push_back(m);
+        return err;
       }
+      list.push_back(m);
     }
   }
   pages_[rid] = static_cast<int32_t>(want);
-  mapped_ += (want - have) * page_ * 2 * num_layers_;
+  mapped_ += (want - have) * page_ * num_layers_;
   return "";
 }
 
 std::string VirtualCache::trim(int32_t rid) {
   for (const Mapping& m : maps_[rid]) unmap(m);
-  mapped_ -= static_cast<int64_t>(pages_[rid]) * page_ * 2 * num_layers_;
+  mapped_ -= static_cast<int64_t>(pages_[rid]) * page_ * num_layers_;
   maps_[rid].clear();
   pages_[rid] = 0;
   return "";

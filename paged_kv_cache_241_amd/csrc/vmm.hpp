@@ -1,7 +1,7 @@
-// Demand-paged contiguous K and V caches ("Leveraging Low-Level CUDA APIs for
-// vAttention's Dynamic Memory", 5.2.1-5.2.3): per layer a virtual tensor for
-// the maximum batch in which request reqId owns the sub-range at
-// reqId x region_bytes; virtual memory is reserved once, and physical pages
+// Demand-paged contiguous KV cache ("Leveraging Low-Level CUDA APIs for
+// vAttention's Dynamic Memory", 5.2.1-5.2.3): per layer a virtual tensor (K
+// and V tile pairs) for the maximum batch in which request reqId owns the
+// sub-range at reqId x region_bytes; virtual memory is reserved once, and physical pages
 // are mapped into a request's sub-range as it grows (sub-ranges are backed
 // independently, one physical allocation per page: 2 MiB where the sub-ranges
 // allow, else the allocation granularity).  Built on
@@ -19,30 +19,29 @@ namespace pa {
 
 class VirtualCache {
  public:
-  // Reserves num_layers * max_seqs * region_bytes of virtual memory for K and
-  // the same for V on `device`, with no physical memory.  physical_bytes caps
-  // the memory mapped over all layers, K and V.  Returns "" on success, else
-  // the reason (and *out stays null).
+  // Reserves num_layers * max_seqs * region_bytes of virtual memory on
+  // `device`, with no physical memory.  physical_bytes caps the memory mapped
+  // over all layers.  Returns "" on success, else the reason (and *out stays
+  // null).
   static std::string create(int32_t num_layers, int32_t max_seqs, int64_t region_bytes,
                             size_t physical_bytes, int device, VirtualCache** out);
   ~VirtualCache();
   VirtualCache(const VirtualCache&) = delete;
   VirtualCache& operator=(const VirtualCache&) = delete;
 
-  char* k_base() const { return k_base_; }
-  char* v_base() const { return v_base_; }
+  char* base() const { return base_; }
   int64_t page_bytes() const { return page_; }
   int64_t region_bytes() const { return region_; }
 
   // Physical bytes request rid's growth to hold its first `bytes` bytes (in
-  // every layer, K and V) would add.
+  // every layer) would add.
   int64_t bytes_short(int32_t rid, int64_t bytes) const;
   int64_t bytes_free() const { return budget_ - mapped_; }
   int64_t bytes_mapped() const { return mapped_; }
   int64_t bytes_budget() const { return budget_; }
   int64_t region_mapped(int32_t rid) const { return static_cast<int64_t>(pages_[rid]) * page_; }
 
-  // Back the first `bytes` bytes of rid's sub-range in every layer, K and V.
+  // Back the first `bytes` bytes of rid's sub-range in every layer.
   // The caller has checked bytes_short against bytes_free.  On a HIP error,
   // whatever this call mapped is taken back and the reason returned.
   std::string grow(int32_t rid, int64_t bytes);
@@ -63,9 +62,8 @@ class VirtualCache {
   int device_ = 0;
   int32_t num_layers_ = 0, max_seqs_ = 0;
   int64_t region_ = 0, page_ = 0, budget_ = 0, mapped_ = 0;
-  size_t reserved_ = 0;  // bytes of each of the two virtual ranges
-  char* k_base_ = nullptr;
-  char* v_base_ = nullptr;
+  size_t reserved_ = 0;  // bytes of the virtual range
+  char* base_ = nullptr;
   std::vector<int32_t> pages_;              // pages backed per sub-range, per request id
   std::vector<std::vector<Mapping>> maps_;  // per request id
 };

@@ -1,6 +1,6 @@
 """A paged KV cache over torch device memory, driven through libpa.so.
 
-PyTorch supplies the device memory (the two cache arrays, q, out, tables,
+PyTorch supplies the device memory (the cache array, q, out, tables,
 workspace) and the stream; every allocator step and every kernel is the C
 library's.  Method names follow the C ABI (``pa_seq_add`` -> ``add``, ...).
 """
@@ -31,9 +31,12 @@ def _stream_handle(stream):
 
 
 class Pool:
-    """K and V caches for ``num_layers`` layers plus the host block allocator.
+    """The KV cache of ``num_layers`` layers plus the host block allocator.
 
-    Cache tensors hold one tile per (block, KV head), as include/pa.h lays out:
+    ``kv_cache`` is the one array include/pa.h lays out, a tile pair per
+    (block, KV head): ``[num_layers][units][num_kv_heads][2][head_dim * block_size]``
+    (K tile, then V tile).  ``k_cache`` and ``v_cache`` are views of its K and V
+    tiles:
       ``k_cache``: ``[num_layers][units][num_kv_heads][head_dim/VE][block_size][VE]``
       ``v_cache``: ``[num_layers][units][num_kv_heads][head_dim][block_size]``
     with ``VE = 16 / element bytes`` and ``units = num_blocks`` (paged) or
@@ -50,9 +53,9 @@ class Pool:
         those calls); device calls then fail.
 
         ``vmm_bytes``: a demand-paged contiguous pool (pa_create_pool_vmm) whose
-        caches the library backs with up to that many bytes of physical pages
-        as requests grow; ``k_cache`` / ``v_cache`` are then None (the library
-        owns the memory and unbacked ranges must not be read)."""
+        cache the library backs with up to that many bytes of physical pages
+        as requests grow; ``kv_cache`` / ``k_cache`` / ``v_cache`` are then None
+        (the library owns the memory and unbacked ranges must not be read)."""
         import torch
 
         self.lib = capi.load()
@@ -67,13 +70,14 @@ class Pool:
         tdt = torch.bfloat16 if kv_dtype == "bf16" else torch.float32
         units = num_blocks if layout == "paged" else max_seqs * (max_seq_len // block_size)
         ve = 16 // (2 if kv_dtype == "bf16" else 4)
+        kv_shape = (num_layers, units, num_kv_heads, 2, head_dim * block_size)
         k_shape = (num_layers, units, num_kv_heads, head_dim // ve, block_size, ve)
         v_shape = (num_layers, units, num_kv_heads, head_dim, block_size)
         self.vmm = vmm_bytes is not None
         if self.vmm:
             if layout != "contiguous":
                 raise ValueError("demand paging backs the contiguous layout")
-            self.k_cache = self.v_cache = None
+            self.kv_cache = self.k_cache = self.v_cache = None
             h = ctypes.c_void_p()
             capi.check(self.lib.pa_create_pool_vmm(ctypes.byref(self.desc), int(vmm_bytes),
                                                    ctypes.byref(h)), "pa_create_pool_vmm")
@@ -81,22 +85,25 @@ class Pool:
                          max_seq_len, tdt)
             return
         if host_only:
-            self.k_cache = self.v_cache = None
+            self.kv_cache = self.k_cache = self.v_cache = None
             self._fake = torch.empty(16, dtype=torch.uint8)
-        elif fill is None:
-            self.k_cache = torch.empty(k_shape, dtype=tdt, device=device)
-            self.v_cache = torch.empty(v_shape, dtype=tdt, device=device)
         else:
-            self.k_cache = torch.full(k_shape, fill, dtype=tdt, device=device)
-            self.v_cache = torch.full(v_shape, fill, dtype=tdt, device=device)
+            if fill is None:
+                self.kv_cache = torch.empty(kv_shape, dtype=tdt, device=device)
+            else:
+                self.kv_cache = torch.full(kv_shape, fill, dtype=tdt, device=device)
+            # views of the K tiles and the V tiles (the last axis of a tile
+            # pair's half is contiguous, so it splits into the tile's axes)
+            self.k_cache = self.kv_cache[:, :, :, 0].view(k_shape)
+            self.v_cache = self.kv_cache[:, :, :, 1].view(v_shape)
         if host_only:
             # any 16-byte aligned address: allocator calls never dereference it
-            kp = vp = (self._fake.data_ptr() + 15) // 16 * 16
+            ptr = (self._fake.data_ptr() + 15) // 16 * 16
         else:
-            assert self.k_cache.numel() * self.k_cache.element_size() == nbytes
-            kp, vp = self.k_cache.data_ptr(), self.v_cache.data_ptr()
+            assert self.kv_cache.numel() * self.kv_cache.element_size() == nbytes
+            ptr = self.kv_cache.data_ptr()
         h = ctypes.c_void_p()
-        capi.check(self.lib.pa_create_pool(ctypes.byref(self.desc), kp, vp, ctypes.byref(h)),
+        capi.check(self.lib.pa_create_pool(ctypes.byref(self.desc), ptr, ctypes.byref(h)),
                    "pa_create_pool")
         self._finish(h, num_layers, num_blocks, block_size, num_kv_heads, head_dim, max_seqs,
                      max_seq_len, tdt)
@@ -108,7 +115,7 @@ class Pool:
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.max_seqs, self.max_seq_len = max_seqs, max_seq_len
         self.torch_dtype = tdt
-        self._device = self.vmm or self.k_cache is not None
+        self._device = self.vmm or self.kv_cache is not None
 
     def vmm_stats(self) -> dict:
         st = capi.pa_vmm_stats()

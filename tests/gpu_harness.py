@@ -25,6 +25,21 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return A.f32_to_f64(t.numpy())
 
 
+def raw_bits(t: torch.Tensor) -> np.ndarray:
+    """The raw element bits of a bf16 (uint16) or fp32 (uint32) tensor."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.view(torch.int32).numpy().view(np.uint32).copy()
+
+
+def bits_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 values of raw bf16 (uint16) or fp32 (uint32) bits."""
+    if bits.dtype == np.uint16:
+        return A.bf16_bits_to_f64(bits)
+    return A.f32_to_f64(bits.view(np.float32))
+
+
 class _Tracked:
     """Pool allocator calls plus each request's length (to know positions)."""
 
@@ -196,22 +211,21 @@ class Case:
         n = int(self.pl.lengths[s])
         bs = self.cfg.block_size
         nblk = -(-n // bs)
+        kv = self.pool.kv_cache[layer]                # the raw tile pairs of the layer
         if self.layout == "paged":
             t = self.tables_np[s][:nblk]
-            tt = torch.from_numpy(np.ascontiguousarray(t)).long().to(self.pool.k_cache.device)
-            kt = self.pool.k_cache[layer].index_select(0, tt)
-            vt = self.pool.v_cache[layer].index_select(0, tt)
+            tt = torch.from_numpy(np.ascontiguousarray(t)).long().to(kv.device)
+            sel = raw_bits(kv.index_select(0, tt))
         else:
             r = self.batch_rids[s]
             per = self.cfg.max_seq_len // bs
-            kt = self.pool.k_cache[layer][r * per:r * per + nblk]
-            vt = self.pool.v_cache[layer][r * per:r * per + nblk]
+            sel = raw_bits(kv[r * per:r * per + nblk])
+        kt, vt = A.pair_tiles(sel, self.cfg.head_dim, bs)
         tail = n - (nblk - 1) * bs if nblk else bs   # rows written in the last block
-        kt, vt = kt.clone(), vt.clone()
         if nblk and tail < bs:
             kt[nblk - 1, :, :, tail:, :] = 0          # K tile [d/VE][BS][VE]
             vt[nblk - 1, :, :, tail:] = 0             # V tile [d][BS]
-        kb, vb = A.k_rows(to_f64(kt)), A.v_rows(to_f64(vt))
+        kb, vb = A.k_rows(bits_f64(kt)), A.v_rows(bits_f64(vt))
         if self.layout == "paged":
             local = list(range(nblk))
             return A.gather_paged(kb, local, n, bs), A.gather_paged(vb, local, n, bs)

@@ -60,12 +60,11 @@ def test_cpu_baseline_spreads_the_oracle_over_host_cores():
     rids = [pool.add() for _ in range(6)]
     pool.reserve(rids, [17, 40, 1, 33, 64, 5])
     g = torch.Generator().manual_seed(3)
-    k = torch.randn((64, 2, 8, 16, 8), generator=g).to(torch.bfloat16)
-    v = torch.randn((64, 2, 64, 16), generator=g).to(torch.bfloat16)
+    kv = torch.randn((1, 64, 2, 2, 64 * 16), generator=g).to(torch.bfloat16)
     fake = SimpleNamespace(
         cfg=SimpleNamespace(block_size=16, max_seq_len=256, kv_dtype="bf16", num_kv_heads=2,
                             head_dim=64),
-        pool=SimpleNamespace(k_cache=k[None], v_cache=v[None], block_tables=pool.block_tables),
+        pool=SimpleNamespace(kv_cache=kv, block_tables=pool.block_tables),
         q=[torch.randn((6, 4, 64), generator=g).to(torch.bfloat16)], layout="paged",
         rids_np=np.array(rids, np.int32), batch=rids, scale=0.125)
     res = bench.cpu_baseline(fake, 0.3)

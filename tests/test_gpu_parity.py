@@ -66,9 +66,8 @@ def test_append_and_copy_bit_exact_whole_cache(cid, over):
 
     def init(pool):
         # initial cache content comes from the seeded generator, before any call
-        for name, t, off in (("k", pool.k_cache, 11), ("v", pool.v_cache, 12)):
-            saved[name] = W.normal(tuple(t.shape), cfg.seed + off, cfg.kv_dtype, "cuda")
-            t.copy_(saved[name])
+        saved["kv"] = W.normal(tuple(pool.kv_cache.shape), cfg.seed + 11, cfg.kv_dtype, "cuda")
+        pool.kv_cache.copy_(saved["kv"])
 
     case = Case(cfg, layers=(0, 1), init=init)
     if cid == 5:
@@ -77,7 +76,9 @@ def test_append_and_copy_bit_exact_whole_cache(cid, over):
     # oracle: replay the plan on the oracle allocator over the same initial
     # bytes, in token-row form
     _, _, log = case.replay_on_oracle()
-    exp = {"k": A.k_rows(_bits(saved["k"])), "v": np.ascontiguousarray(A.v_rows(_bits(saved["v"])))}
+    d, bs = cfg.head_dim, cfg.block_size
+    kt, vt = A.pair_tiles(_bits(saved["kv"]), d, bs)
+    exp = {"k": A.k_rows(kt), "v": np.ascontiguousarray(A.v_rows(vt))}
     rows = {l: (_bits(case.vals[l][1]), _bits(case.vals[l][2])) for l in (0, 1)}
     for handles, counts, starts, slots, pairs in log:
         for key in ("k", "v"):
@@ -93,8 +94,9 @@ def test_append_and_copy_bit_exact_whole_cache(cid, over):
         for l in (0, 1):
             exp["k"][l] = A.append_scatter(exp["k"][l], sl, rows[l][0][idx])
             exp["v"][l] = A.append_scatter(exp["v"][l], sl, rows[l][1][idx])
-    assert np.array_equal(A.k_rows(_bits(case.pool.k_cache)), exp["k"])
-    assert np.array_equal(A.v_rows(_bits(case.pool.v_cache)), exp["v"])
+    kt, vt = A.pair_tiles(_bits(case.pool.kv_cache), d, bs)
+    assert np.array_equal(A.k_rows(kt), exp["k"])
+    assert np.array_equal(A.v_rows(vt), exp["v"])
 
 
 def test_bulk_append_scattered_and_straddling_slots_bit_exact():
@@ -109,11 +111,10 @@ def test_bulk_append_scattered_and_straddling_slots_bit_exact():
     nb = 300 + -(-700 // bs) + 4
     pool = Pool(1, nb, bs, hkv, d, "bf16", "paged", max_seqs=400, max_seq_len=1024)
     pool.set_free_order(W.free_order(nb, 2417))
-    saved = {}
-    for name, t, off in (("k", pool.k_cache, 21), ("v", pool.v_cache, 22)):
-        saved[name] = W.normal(tuple(t.shape), 2417 + off, "bf16", "cuda")
-        t.copy_(saved[name])
-    exp = {"k": A.k_rows(_bits(saved["k"]))[0], "v": np.ascontiguousarray(A.v_rows(_bits(saved["v"])))[0]}
+    saved = W.normal(tuple(pool.kv_cache.shape), 2417 + 21, "bf16", "cuda")
+    pool.kv_cache.copy_(saved)
+    kt, vt = A.pair_tiles(_bits(saved), d, bs)
+    exp = {"k": A.k_rows(kt)[0], "v": np.ascontiguousarray(A.v_rows(vt))[0]}
     rids = [pool.add() for _ in range(301)]
     gen = torch.Generator(device="cpu").manual_seed(2417)
     for rids_now, counts in ((rids[:300], [1] * 300), (rids[:300], [1] * 300),
@@ -127,8 +128,9 @@ def test_bulk_append_scattered_and_straddling_slots_bit_exact():
         exp["k"] = A.append_scatter(exp["k"], slots, _bits(kr))
         exp["v"] = A.append_scatter(exp["v"], slots, _bits(vr))
     torch.cuda.synchronize()
-    assert np.array_equal(A.k_rows(_bits(pool.k_cache))[0], exp["k"])
-    assert np.array_equal(A.v_rows(_bits(pool.v_cache))[0], exp["v"])
+    kt, vt = A.pair_tiles(_bits(pool.kv_cache), d, bs)
+    assert np.array_equal(A.k_rows(kt)[0], exp["k"])
+    assert np.array_equal(A.v_rows(vt)[0], exp["v"])
     pool.close()
 
 

@@ -23,7 +23,7 @@ from oracle import attention as A
 from paged_kv_cache_241_amd import capi
 from paged_kv_cache_241_amd.pool import Pool
 
-from gpu_harness import Case, to_f64
+from gpu_harness import Case, bits_f64, raw_bits, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -42,18 +42,12 @@ def _image(nbytes: int, where: str) -> torch.Tensor:
     return torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
 
-def _block_bytes(cache: torch.Tensor, blocks) -> torch.Tensor:
-    """[layers][len(blocks)][bytes of one block's tiles] of a K or V cache."""
-    idx = torch.tensor(list(blocks), dtype=torch.int64, device=cache.device)
-    sel = cache.index_select(1, idx).contiguous()
-    return sel.view(torch.uint8).reshape(cache.shape[0], len(blocks), -1).cpu()
-
-
 def _expected_image(pool: Pool, blocks) -> torch.Tensor:
-    """image[layer][j][K|V][...] as include/pa.h lays it out."""
-    k = _block_bytes(pool.k_cache, blocks)
-    v = _block_bytes(pool.v_cache, blocks)
-    return torch.stack([k, v], dim=2).reshape(-1)
+    """image[layer][j][num_kv_heads][K|V][tile] as include/pa.h lays it out:
+    each listed block's tile pairs, layer by layer."""
+    idx = torch.tensor(list(blocks), dtype=torch.int64, device=pool.kv_cache.device)
+    sel = pool.kv_cache.index_select(1, idx).contiguous()
+    return sel.view(torch.uint8).reshape(-1).cpu()
 
 
 def _refresh_tables(case: Case) -> None:
@@ -163,8 +157,8 @@ def test_exhaustion_swap_out_makes_room_and_the_request_resumes():
     assert torch.equal(out1, out0)
     # and the oracle agrees with what the request attends to
     tables, lens = pool.block_tables([b], 8)
-    kb = A.k_rows(to_f64(pool.k_cache[0]))
-    vb = A.v_rows(to_f64(pool.v_cache[0]))
+    kt, vt = A.pair_tiles(raw_bits(pool.kv_cache[0]), pool.head_dim, pool.block_size)
+    kb, vb = A.k_rows(bits_f64(kt)), A.v_rows(bits_f64(vt))
     t = tables[0][: -(-int(lens[0]) // 16)]
     k = A.gather_paged(kb, t, int(lens[0]), 16)
     v = A.gather_paged(vb, t, int(lens[0]), 16)

@@ -227,6 +227,26 @@ def test_tile_readers_worked_example():
     assert A.v_rows(v)[0, 0].tolist() == [[0, 3, 6, 9], [1, 4, 7, 10], [2, 5, 8, 11]]
 
 
+def test_pair_tiles_worked_example():
+    # fp32 (VE = 4), d = 8, BS = 2: one tile pair of 32 elements labelled by
+    # position.  K tile = elements 0..15 as [2][2][4]: token 0 holds chunk 0
+    # of row 0 (0..3) and chunk 1 of row 0 (8..11); V tile = elements 16..31
+    # as [8][2]: token o of dim e is 16 + 2e + o.
+    pair = np.arange(32, dtype=np.float32).reshape(1, 1, 32)
+    kt, vt = A.pair_tiles(pair, 8, 2)
+    assert kt.shape == (1, 1, 2, 2, 4) and vt.shape == (1, 1, 8, 2)
+    assert A.k_rows(kt)[0, 0].tolist() == [[0, 1, 2, 3, 8, 9, 10, 11], [4, 5, 6, 7, 12, 13, 14, 15]]
+    assert A.v_rows(vt)[0, 0].tolist() == [[16, 18, 20, 22, 24, 26, 28, 30],
+                                           [17, 19, 21, 23, 25, 27, 29, 31]]
+    # bf16 bits (VE = 8), d = 8, BS = 1, two heads given as [..., 2, d*BS]:
+    # head 1's K row is elements 16..23, its V row 24..31
+    bits = np.arange(32, dtype=np.uint16).reshape(1, 2, 2, 8)
+    kt, vt = A.pair_tiles(bits, 8, 1)
+    assert kt.shape == (1, 2, 1, 1, 8) and vt.shape == (1, 2, 8, 1)
+    assert A.k_rows(kt)[0, 1, 0].tolist() == list(range(16, 24))
+    assert A.v_rows(vt)[0, 1, 0].tolist() == list(range(24, 32))
+
+
 def test_contiguous_rows_follow_reqid_times_s():
     # 2 requests, S = 4, BS = 2: request r's blocks are 2r and 2r+1
     rows = np.arange(4 * 1 * 2 * 1).reshape(4, 1, 2, 1)
