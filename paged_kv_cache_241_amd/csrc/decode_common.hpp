@@ -14,6 +14,7 @@ namespace pa {
 namespace {
 
 constexpr int kWave = 64;
+constexpr int kComputeUnits = 256;  // MI355X: 8 XCDs x 32 CUs
 constexpr int kChunk = 16;        // tokens per MFMA tile
 constexpr float kLog2e = 1.4426950408889634f;
 

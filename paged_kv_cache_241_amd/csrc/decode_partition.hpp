@@ -78,6 +78,14 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   // partitions (the last ones) come first and the shared ones, which exit at
   // once, after them.
   const int tid = threadIdx.x;
+  // A balanced-start grid is at most two workgroups per CU, all resident
+  // from the start; the second one on a CU (ids from kComputeUnits on, as the
+  // dispatcher deals them) loses the SIMDs' issue arbitration to the older
+  // first one and finished about 1.3 us later on the Llama-3-8B batch-64
+  // layer (per-wave clocks).  Its waves issue at a higher priority instead.
+  if constexpr (BAL) {
+    if (bid >= kComputeUnits) __builtin_amdgcn_s_setprio(1);
+  }
   int s, kvh, part, L;
   if (a.plan != nullptr) {
     const int2 it = a.plan[bid / hkv];
