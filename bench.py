@@ -242,8 +242,9 @@ class Bench:
     def prepare(self, max_steps: int, separate_append: bool = False, shared_tokens: int = 0):
         """Fixed device buffers, double-buffered pinned staging, ctypes arguments.
 
-        shared_tokens > 0: decode with pa_decode_shared in partitions of that
-        many tokens (its append is a separate pa_append_kv)."""
+        shared_tokens > 0: decode with pa_append_decode_shared (or, with
+        separate_append, pa_append_kv + pa_decode_shared) in partitions of
+        that many tokens."""
         import ctypes
 
         import torch
@@ -285,7 +286,6 @@ class Bench:
         self.sh = ctypes.c_void_p(self.stream.cuda_stream)
         self.shared_T = shared_tokens
         if shared_tokens:
-            separate_append = True
             self.pt = shared_tokens
             need = self.pool.workspace_bytes(b, self.cfg.num_q_heads,
                                              max(self.cfg.max_seq_len, shared_tokens + 1), shared_tokens)
@@ -368,12 +368,17 @@ class Bench:
                     self.stride, req, self.lens_d.data_ptr(), b, max_context, self.pt,
                     self.out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, self.sh)
             if self.shared_T:
-                self.check(lib.pa_decode_shared(
-                    pool.handle, layer, self.q[layer].data_ptr(), self.dtype_code, cfg.num_q_heads,
-                    self.scale, tables, self.stride, self.lens_d.data_ptr(), b, max_context,
-                    self.shared_T, self.sh_seq.data_ptr(), self.sh_groups.data_ptr(), self.sh_ng,
-                    self.sh_mm, self.sh_ms, self.out.data_ptr(), self.ws.data_ptr(), self.ws_bytes,
-                    self.sh), "pa_decode_shared")
+                shared_tail = (self.q[layer].data_ptr(), self.dtype_code, cfg.num_q_heads,
+                               self.scale, tables, self.stride, self.lens_d.data_ptr(), b, max_context,
+                               self.shared_T, self.sh_seq.data_ptr(), self.sh_groups.data_ptr(),
+                               self.sh_ng, self.sh_mm, self.sh_ms, self.out.data_ptr(),
+                               self.ws.data_ptr(), self.ws_bytes, self.sh)
+                if self.separate_append:
+                    self.check(lib.pa_decode_shared(pool.handle, layer, *shared_tail), "pa_decode_shared")
+                else:
+                    self.check(lib.pa_append_decode_shared(
+                        pool.handle, layer, self.k_new[layer].data_ptr(), self.v_new[layer].data_ptr(),
+                        self.slots_d.data_ptr(), *shared_tail), "pa_append_decode_shared")
             elif self.separate_append:
                 self.check(lib.pa_decode(pool.handle, layer, *tail), "pa_decode")
             else:
@@ -652,8 +657,6 @@ def main():
             cfg = W.get(args.config, **over)
     nl = args.layers or cfg.num_layers
     bench = Bench(cfg, args.layout, nl, args.warmup + args.steps + 1, args.partition_tokens)
-    if args.shared_prefix:
-        args.separate_append = True
     bench.prepare(args.warmup + args.steps, args.separate_append, args.shared_prefix)
     for _ in range(args.warmup):
         bench.step()
@@ -710,7 +713,9 @@ def main():
             "head_dim": cfg.head_dim, "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
             "mean_context_timed": round(float(np.mean(lens_seen)), 2),
             "layers_rotated": nl, "partition_tokens": part, "layout": args.layout,
-            "decode": "shared prefixes read once (pa_decode_shared)" if args.shared_prefix else
+            "decode": ("shared prefixes read once (" +
+                       ("pa_append_kv + pa_decode_shared" if args.separate_append else "pa_append_decode_shared") +
+                       ")") if args.shared_prefix else
                       ("pa_append_kv + pa_decode" if args.separate_append else "pa_append_decode"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -721,7 +726,8 @@ def main():
         "pool_utilisation": round(stats["utilisation"], 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("pa_decode_shared (decode_shared_kernel: shared pass and private partitions; "
+            "kernel": (("pa_decode_shared" if args.separate_append else "pa_append_decode_shared") +
+                       " (decode_shared_kernel: shared pass and private partitions; "
                        "decode_merge_kernel)" if args.shared_prefix else
                        ("pa_decode" if args.separate_append else "pa_append_decode") +
                        " (decode_partition_kernel; decode_plan_kernel and decode_merge_kernel "

@@ -271,6 +271,26 @@ pa_status pa_decode_shared(pa_pool* pool, int32_t layer, const void* d_q, pa_dty
                            int32_t max_shared, float* d_out, void* d_workspace,
                            size_t workspace_bytes, void* stream);
 
+/* One decode step of a layer for such a batch in one launch (plus the
+ * merge): pa_append_kv of each sequence's new token, then pa_decode_shared
+ * over contexts that end with it.  d_k, d_v, d_slots as for
+ * pa_append_decode; the other arguments as for pa_decode_shared.  The new
+ * token of every sequence that appends (slot >= 0) must lie past its shared
+ * prefix (seq_shared[s] <= L_s - 1): pa_shared_groups called after the
+ * step's pa_reserve gives that, since the reserve makes each writer's last
+ * block its own ([PAS] Summary: a shared block is copied before a sharer
+ * writes into it); pa_check_shared_args checks it on host copies.  The cache
+ * afterwards equals pa_append_kv's, the output pa_decode_shared's after that
+ * append, bit for bit. */
+pa_status pa_append_decode_shared(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                                  const int32_t* d_slots, const void* d_q, pa_dtype q_dtype,
+                                  int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                                  int32_t table_stride, const int32_t* d_context_lens, int32_t num_seqs,
+                                  int32_t max_context, int32_t partition_tokens, const int32_t* d_seq_shared,
+                                  const int32_t* d_groups, int32_t num_groups, int32_t max_members,
+                                  int32_t max_shared, float* d_out, void* d_workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* ---- pre-emption by swapping ([ROC] "Fragmentation is lost users" and the
  * Pre-emption term: when paging runs out, a request's cache is evicted and
  * swapped back in later; [PAS] Summary: the scheduler pre-empts requests) ----
@@ -456,6 +476,14 @@ pa_status pa_check_slots(const pa_pool* pool, const int32_t* h_slots, int32_t n)
  * destination is also a source ([PAS] Summary: a shared block is copied
  * before a sharer writes into it).  Paged only. */
 pa_status pa_check_block_pairs(const pa_pool* pool, const int32_t* h_pairs, int32_t n);
+
+/* The shared prefixes of a pa_decode_shared / pa_append_decode_shared call
+ * (host int32 [num_seqs], with the lengths and, for the fused call, the
+ * slots): each a multiple of partition_tokens within its context, and no
+ * appending sequence's new token inside its shared prefix. */
+pa_status pa_check_shared_args(const pa_pool* pool, const int32_t* h_seq_shared,
+                               const int32_t* h_context_lens, const int32_t* h_slots, int32_t num_seqs,
+                               int32_t partition_tokens);
 
 /* Message of the calling thread's last error ("" if none). */
 const char* pa_last_error(void);

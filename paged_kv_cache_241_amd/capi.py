@@ -45,7 +45,8 @@ EXPORTS = (
     "pa_decode_partition_tokens", "pa_decode_workspace_bytes", "pa_decode", "pa_append_decode",
     "pa_swap_bytes", "pa_swap_out", "pa_swap_in", "pa_create_pool_vmm", "pa_vmm_info",
     "pa_vmm_trim", "pa_shared_groups", "pa_decode_shared", "pa_check_decode_args",
-    "pa_check_slots", "pa_check_block_pairs", "pa_append_decode_noalloc", "pa_last_error",
+    "pa_check_slots", "pa_check_block_pairs", "pa_append_decode_noalloc", "pa_append_decode_shared",
+    "pa_check_shared_args", "pa_last_error",
 )
 
 # bytes of the device scratch pa_append_decode_noalloc holds on each GPU
@@ -128,6 +129,10 @@ def load() -> ctypes.CDLL:
         "pa_decode_shared": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _i32, ctypes.c_float, _vp,
                                             _i32, _vp, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _i32,
                                             _vp, _vp, ctypes.c_size_t, _vp]),
+        "pa_append_decode_shared": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
+                                                   ctypes.c_float, _vp, _i32, _vp, _i32, _i32, _i32, _vp,
+                                                   _vp, _i32, _i32, _i32, _vp, _vp, ctypes.c_size_t, _vp]),
+        "pa_check_shared_args": (ctypes.c_int, [_vp, _p32, _p32, _p32, _i32, _i32]),
         "pa_append_kv": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i32, _vp]),
         "pa_decode_partition_tokens": (ctypes.c_int32, [_vp, _i32, _i32, _i32]),
         "pa_decode_workspace_bytes": (ctypes.c_size_t, [_vp, _i32, _i32, _i32, _i32]),

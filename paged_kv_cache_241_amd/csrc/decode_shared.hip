@@ -400,7 +400,11 @@ hipError_t launch_shared_d(const CacheGeom& g, const DecodeArgs& a, const Shared
                         static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
   if (nwork == 0) return hipSuccess;
   const int G = a.num_q_heads / g.num_kv_heads;
-  const size_t lds = static_cast<size_t>(std::max(shared_lds_bytes<KIND, D>(), merge_lds_bytes(kSharedWaves, G, D)));
+  // the shared pass's stage buffers, or the private partitions' merge (and,
+  // with a fused append, its staged tail chunk), whichever is larger
+  const int private_lds = merge_lds_bytes(kSharedWaves, G, D) +
+                          (a.new_k != nullptr && g.block_size >= kChunk ? append_stage_bytes(D, g.elt) : 0);
+  const size_t lds = static_cast<size_t>(std::max(shared_lds_bytes<KIND, D>(), private_lds));
   const dim3 grid(static_cast<uint32_t>(nwork)), block(kSharedWaves * kWave);
   switch (g.block_size) {
     case 8: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 8>), grid, block, lds, st, g, a, sh); break;

@@ -718,6 +718,53 @@ pa_status pa_shared_groups(const pa_pool* pool, const int32_t* req_ids, int32_t 
   });
 }
 
+pa_status pa_append_decode_shared(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                                  const int32_t* d_slots, const void* d_q, pa_dtype q_dtype,
+                                  int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                                  int32_t table_stride, const int32_t* d_context_lens, int32_t num_seqs,
+                                  int32_t max_context, int32_t partition_tokens, const int32_t* d_seq_shared,
+                                  const int32_t* d_groups, int32_t num_groups, int32_t max_members,
+                                  int32_t max_shared, float* d_out, void* d_workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return guarded("append_decode_shared", [&]() -> pa_status {
+    if (d_seq_shared == nullptr) return fail(PA_ERR_INVALID_ARG, "append_decode_shared: null seq_shared");
+    if (d_k == nullptr || d_v == nullptr || d_slots == nullptr)
+      return fail(PA_ERR_INVALID_ARG, "append_decode_shared: null k, v or slots");
+    if ((reinterpret_cast<uintptr_t>(d_k) | reinterpret_cast<uintptr_t>(d_v)) & 15)
+      return fail(PA_ERR_INVALID_ARG, "append_decode_shared: k and v must be 16-byte aligned");
+    return decode_impl("append_decode_shared", pool, layer, d_k, d_v, d_slots, d_q, q_dtype, num_q_heads,
+                       scale, d_block_tables, table_stride, nullptr, d_context_lens, num_seqs, max_context,
+                       partition_tokens, d_out, d_workspace, workspace_bytes, stream, d_seq_shared, d_groups,
+                       num_groups, max_members, max_shared);
+  });
+}
+
+pa_status pa_check_shared_args(const pa_pool* pool, const int32_t* h_seq_shared,
+                               const int32_t* h_context_lens, const int32_t* h_slots, int32_t num_seqs,
+                               int32_t partition_tokens) {
+  return guarded("check_shared_args", [&]() -> pa_status {
+    const std::string w = "check_shared_args";
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null pool");
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, w + ": negative num_seqs");
+    if (partition_tokens <= 0 || bad_partition(pool, partition_tokens))
+      return fail(PA_ERR_INVALID_ARG, w + ": partition_tokens must be a positive multiple of 16 and of block_size");
+    if (num_seqs == 0) return PA_OK;
+    if (h_seq_shared == nullptr || h_context_lens == nullptr)
+      return fail(PA_ERR_INVALID_ARG, w + ": null seq_shared or lengths");
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      const std::string at = w + ": sequence " + std::to_string(s);
+      const int32_t sh = h_seq_shared[s], L = h_context_lens[s];
+      if (sh < 0 || sh % partition_tokens != 0 || sh > L)
+        return fail(PA_ERR_INVALID_ARG, at + ": shared prefix " + std::to_string(sh) +
+                                            " is not a multiple of partition_tokens within the context");
+      if (h_slots != nullptr && h_slots[s] >= 0 && sh > L - 1)
+        return fail(PA_ERR_INVALID_ARG, at + ": its new token (position " + std::to_string(L - 1) +
+                                            ") lies in its shared prefix: find the groups after pa_reserve");
+    }
+    return PA_OK;
+  });
+}
+
 pa_status pa_decode_shared(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
                            int32_t num_q_heads, float scale, const int32_t* d_block_tables,
                            int32_t table_stride, const int32_t* d_context_lens, int32_t num_seqs,

@@ -216,8 +216,12 @@ class Pool:
 
     def decode_shared(self, layer: int, q, scale: float, block_tables, context_lens, max_context: int,
                       partition_tokens: int, seq_shared, groups, max_members: int, max_shared: int,
-                      out=None, workspace=None, stream=None):
-        """pa_decode_shared: seq_shared int32 [B] and groups int32 [g][2] on the device."""
+                      out=None, workspace=None, stream=None, append=None):
+        """pa_decode_shared: seq_shared int32 [B] and groups int32 [g][2] on the device.
+
+        ``append=(k, v, slots)`` stores each sequence's new token first, in the
+        same launch (pa_append_decode_shared); k, v are [B][Hkv][D], slots int32 [B].
+        """
         import torch
 
         assert self._device, "host-only pool"
@@ -233,14 +237,33 @@ class Pool:
             need = self.workspace_bytes(b, hq, max(int(max_context), int(partition_tokens) + 1),
                                         partition_tokens)
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        capi.check(self.lib.pa_decode_shared(
-            self.handle, layer, q.data_ptr(), _DTYPES[self.kv_dtype], hq, float(scale),
-            block_tables.data_ptr(), int(block_tables.shape[1]), context_lens.data_ptr(), b,
-            int(max_context), int(partition_tokens), seq_shared.data_ptr(),
-            groups.data_ptr() if groups.numel() else None, int(groups.shape[0]), int(max_members),
-            int(max_shared), out.data_ptr(), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), _stream_handle(stream)), "pa_decode_shared")
+        tail = (q.data_ptr(), _DTYPES[self.kv_dtype], hq, float(scale),
+                block_tables.data_ptr(), int(block_tables.shape[1]), context_lens.data_ptr(), b,
+                int(max_context), int(partition_tokens), seq_shared.data_ptr(),
+                groups.data_ptr() if groups.numel() else None, int(groups.shape[0]), int(max_members),
+                int(max_shared), out.data_ptr(), workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), _stream_handle(stream))
+        if append is None:
+            capi.check(self.lib.pa_decode_shared(self.handle, layer, *tail), "pa_decode_shared")
+        else:
+            k, v, slots = append
+            for t in (k, v):
+                assert t.is_cuda and t.is_contiguous() and t.dtype == self.torch_dtype
+                assert tuple(t.shape) == (b, self.num_kv_heads, self.head_dim)
+            assert slots.is_cuda and slots.dtype == torch.int32 and tuple(slots.shape) == (b,)
+            capi.check(self.lib.pa_append_decode_shared(self.handle, layer, k.data_ptr(), v.data_ptr(),
+                                                        slots.data_ptr(), *tail), "pa_append_decode_shared")
         return out
+
+    def check_shared_args(self, seq_shared, context_lens, partition_tokens: int, slots=None) -> None:
+        """pa_check_shared_args on host int32 arrays."""
+        sh = np.ascontiguousarray(seq_shared, dtype=np.int32)
+        ln = np.ascontiguousarray(context_lens, dtype=np.int32)
+        sl = None if slots is None else np.ascontiguousarray(slots, dtype=np.int32)
+        n = len(sh)
+        capi.check(self.lib.pa_check_shared_args(
+            self.handle, _ptr32(sh) if n else None, _ptr32(ln) if n else None,
+            _ptr32(sl) if sl is not None else None, n, int(partition_tokens)), "pa_check_shared_args")
 
     # -- pre-emption by swapping ---------------------------------------------
     def swap_bytes(self, rid: int) -> int:

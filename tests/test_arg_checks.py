@@ -152,3 +152,27 @@ def test_noalloc_decode_refuses_more_than_its_scratch_before_any_launch():
                                       256, addr, None)
     assert st == capi.PA_ERR_WORKSPACE, lib.pa_last_error()
     assert str(capi.PA_NOALLOC_SCRATCH_BYTES).encode() in lib.pa_last_error()
+
+
+def test_shared_args():
+    # samples of one prompt: 3 forks of a 40-token prompt, then the step's
+    # token each (the shared 16-token blocks stay shared, the partly filled
+    # last one is copied by every writer but the last)
+    p = Pool(host_only=True, num_layers=1, num_blocks=32, block_size=16, num_kv_heads=1,
+             head_dim=64, kv_dtype="bf16", layout="paged", max_seqs=8, max_seq_len=256)
+    a = p.add()
+    p.reserve([a], [40])
+    rids = [a] + [p.fork(a) for _ in range(3)]
+    slots, pairs = p.reserve(rids)
+    assert len(pairs) == 3
+    seq_shared, groups, mm, ms = p.shared_groups(rids, 16)
+    _, lens = p.block_tables(rids)
+    assert seq_shared.tolist() == [32] * 4 and lens.tolist() == [41] * 4
+    p.check_shared_args(seq_shared, lens, 16, slots=slots)
+    p.check_shared_args(seq_shared, lens, 16)
+    # groups found before the step's reserve would cover the new token
+    _refused(p.check_shared_args, np.full(4, 48, np.int32), np.full(4, 48, np.int32), 16,
+             slots=slots)
+    _refused(p.check_shared_args, np.array([24, 32, 32, 32], np.int32), lens, 16)   # not a multiple
+    _refused(p.check_shared_args, np.array([64, 32, 32, 32], np.int32), lens, 16)   # past the context
+    _refused(p.check_shared_args, seq_shared, lens, 24)                             # bad partition

@@ -36,18 +36,27 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _run_shared(case: Case, T: int, order):
-    """pa_decode_shared over the batch in `order` (indices into the batch)."""
+def _run_shared(case: Case, T: int, order, append=None):
+    """pa_decode_shared over the batch in `order` (indices into the batch);
+    append=(k, v, slots) in batch order: pa_append_decode_shared."""
     rids = [case.batch_rids[i] for i in order]
     seq_shared, groups, mm, ms = case.pool.shared_groups(rids, T)
     idx = torch.tensor(order, dtype=torch.int64, device="cuda")
     q = case.vals[0][0].index_select(0, idx).contiguous()
     tables = case.tables.index_select(0, idx).contiguous()
     lens = case.lens.index_select(0, idx).contiguous()
+    if append is not None:
+        append = tuple(t.index_select(0, idx).contiguous() for t in append)
+    # the device arrays, checked on host copies before the launch
+    lens_np = lens.cpu().numpy()
+    case.pool.check_decode_args(tables.cpu().numpy(), lens_np, case.max_context,
+                                slots=append[2].cpu().numpy() if append is not None else None)
+    case.pool.check_shared_args(seq_shared, lens_np, T,
+                                slots=append[2].cpu().numpy() if append is not None else None)
     out = case.pool.decode_shared(0, q, case.scale, tables, lens, case.max_context, T,
                                   torch.from_numpy(seq_shared).cuda(),
                                   torch.from_numpy(np.ascontiguousarray(groups)).cuda().view(-1, 2),
-                                  mm, ms)
+                                  mm, ms, append=append)
     torch.cuda.synchronize()
     back = torch.empty_like(out)
     back[idx] = out
@@ -151,3 +160,44 @@ def test_random_shared_batches(seed):
     plain = case.decode(partition_tokens=T)
     for s in range(batch):
         assert row_rel_err(to_f64(got[s]), to_f64(plain[s])) <= 1e-5, s
+
+
+@pytest.mark.parametrize("over,T,shuffle", [
+    ({"batch": 24, "prompt_len": 200, "private_len": 40, "num_blocks": 200}, 32, False),
+    ({"batch": 24, "prompt_len": 200, "private_len": 1, "num_blocks": 200, "block_size": 32}, 64, True),
+    ({"batch": 16, "prompt_len": 160, "private_len": 40, "num_blocks": 200, "kv_dtype": "f32"}, 64, False),
+    ({"batch": 24, "prompt_len": 200, "private_len": 40, "num_blocks": 400, "block_size": 8}, 16, True),
+    # the benchmark's shared-prefix step at full size: literal 2048-token
+    # prompts, and the 2056-token variant whose step copies each prompt's
+    # half-full last block for 7 of its 8 samples
+    ({}, 1024, False),
+    ({"prompt_len": 2056}, 1024, False),
+])
+def test_fused_shared_step_equals_append_then_shared_decode(over, T, shuffle):
+    # pa_append_decode_shared against pa_append_kv + pa_decode_shared: the
+    # same output bits and the same cache bytes, and the oracle's tolerances
+    cfg = W.get(5, **over)
+    sep = Case(cfg, step_append=False, fill=0.0)
+    fus = Case(cfg, step_append=False, fill=0.0)
+    assert torch.equal(sep.step_slots, fus.step_slots)
+    k, v = sep.step_kv()
+    order = list(range(cfg.batch))
+    if shuffle:
+        np.random.default_rng(cfg.batch).shuffle(order)
+    sep.pool.check_slots(sep.step_slots.cpu().numpy())
+    sep.pool.append_kv(0, k, v, sep.step_slots)
+    a, _, groups = _run_shared(sep, T, order)
+    b, _, _ = _run_shared(fus, T, order, append=(k, v, fus.step_slots))
+    assert len(groups) > 0
+    assert torch.equal(a, b)
+    assert torch.equal(sep.pool.kv_cache, fus.pool.kv_cache)
+    if cfg.batch <= 64:
+        _check_oracle(fus, b)
+    else:
+        rng = np.random.default_rng(6)
+        sample = sorted(set([0, 7, 8, cfg.batch - 1] + [int(x) for x in rng.choice(cfg.batch, 4, replace=False)]))
+        g = to_f64(b)
+        ref = fus.reference(sample)
+        for s in sample:
+            err = row_rel_err(g[s], ref[s])
+            assert err <= BF16_STATED and err <= BF16_INTERNAL, (s, err)
