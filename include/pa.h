@@ -17,19 +17,20 @@
  * Cache layout (device memory owned by the caller)
  * ---------------------------------------------------------------------------
  * One device array, element type kv_dtype, holds the K and V caches of all
- * layers.  Each layer is an array of tile pairs, one pair per (block, KV
- * head): the K tile of that block and head, then its V tile.  VE = 16 /
- * sizeof(element) (8 for bf16, 4 for fp32):
+ * layers.  Each layer is an array of (block, KV head) regions; a region holds
+ * block_size / sub tile pairs of sub = min(block_size, 16) token rows each:
+ * the K tile of those rows, then their V tile.  VE = 16 / sizeof(element)
+ * (8 for bf16, 4 for fp32):
  *
- *   cache: [num_layers][units][num_kv_heads][2][tile]     (2: K, then V)
- *   K tile [head_dim/VE][block_size][VE]
- *   V tile [head_dim][block_size]
+ *   cache: [num_layers][units][num_kv_heads][block_size/sub][2][tile]  (2: K, then V)
+ *   K tile [head_dim/VE][sub][VE]
+ *   V tile [head_dim][sub]
  *
  * The K tile keeps each token row in 16-byte chunks (chunk-major); the V tile
  * is dimension-major.  Both make the decode kernel's matrix-core operand
- * loads contiguous wave accesses, and a (block, head)'s K and V together are
- * one contiguous run for the decode to read (8 KiB for bf16, 16 tokens,
- * head_dim 128).
+ * loads contiguous wave accesses, and the K and V of 16 consecutive tokens of
+ * a head are one contiguous run for the decode to read (8 KiB for bf16,
+ * head_dim 128), with blocks of 32 tokens as with blocks of 16.
  *
  * PA_PAGED: units = num_blocks.  Block b holds, for every KV head,
  * block_size consecutive tokens; a sequence's blocks need not be adjacent and
@@ -44,10 +45,11 @@
  *
  * A "slot" names one token row: slot = u*block_size + o, u the block, o the
  * row in it (contiguous: slot = reqId*max_seq_len + position).  Element
- * (slot, head h, dim e) of layer l is, with pair = ((l*units + u)*num_kv_heads
- * + h) * 2 * head_dim * block_size (in elements from the array's start):
- *   K: pair + ((e / VE) * block_size + o) * VE + e % VE
- *   V: pair + head_dim * block_size + e * block_size + o
+ * (slot, head h, dim e) of layer l is, with r = o % sub and pair =
+ * ((l*units + u)*num_kv_heads + h) * 2 * head_dim * block_size
+ * + (o / sub) * 2 * head_dim * sub (in elements from the array's start):
+ *   K: pair + ((e / VE) * sub + r) * VE + e % VE
+ *   V: pair + head_dim * sub + e * sub + r
  *
  * ---------------------------------------------------------------------------
  * Conventions
@@ -299,10 +301,9 @@ pa_status pa_append_decode_shared(pa_pool* pool, int32_t layer, const void* d_k,
  * grow (pa_reserve), fork, or have its table read (PA_ERR_INVALID_ARG) until
  * it is swapped in; pa_seq_free drops it.  Its image, in memory the caller
  * owns, holds every layer's copy of its blocks:
- *     image[layer][j][num_kv_heads][0 = K, 1 = V][tile]
- * for j < ceil(L / block_size) in logical order, each block's tile pairs as
- * the pool lays them out (K [head_dim/VE][block_size][VE], then V
- * [head_dim][block_size]), i.e.
+ *     image[layer][j][num_kv_heads][region]
+ * for j < ceil(L / block_size) in logical order, each (block, head) region as
+ * the pool lays it out (its tile pairs), i.e.
  * num_layers * ceil(L/BS) * 2 * num_kv_heads * head_dim * BS * elt bytes.
  * Whole blocks are copied, rows past L included.  Sharing is not kept: blocks
  * the request shared are copied out in full and come back as its own.

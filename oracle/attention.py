@@ -6,13 +6,15 @@ nothing is blocked, fused or reordered beyond the definitions below.
 Cache layout.  The pages fix none; the C library documents this one, and the
 functions here read it as written there:
 
-* One array holds a layer's K and V: an array of tile pairs, one per (block,
-  KV head), shape ``[units][Hkv][pair]`` with ``pair`` = the K tile's
-  ``d*BS`` elements followed by the V tile's ``d*BS``.  ``pair_tiles`` splits
-  it.  The K tile is ``[d/VE][BS][VE]`` (the row of a token cut into 16-byte
-  chunks of ``VE`` elements, chunk-major), the V tile is ``[d][BS]``
-  (dimension-major).  ``k_rows`` / ``v_rows`` turn tiles into plain token rows
-  ``[units][Hkv][BS][d]``, which is what the gathers read.
+* One array holds a layer's K and V: one region of ``2*d*BS`` elements per
+  (block, KV head), shape ``[units][Hkv][region]``.  A region holds
+  ``BS/sub`` tile pairs of ``sub = min(BS, 16)`` token rows: the K tile of
+  those rows (``d*sub`` elements), then their V tile (``d*sub``).  The K tile
+  is ``[d/VE][sub][VE]`` (the row of a token cut into 16-byte chunks of
+  ``VE`` elements, chunk-major), the V tile is ``[d][sub]`` (dimension-major).
+  ``pair_tiles`` turns a region into the block's K tile ``[d/VE][BS][VE]``
+  and V tile ``[d][BS]``; ``k_rows`` / ``v_rows`` turn those into plain token
+  rows ``[units][Hkv][BS][d]``, which is what the gathers read.
 * paged: ``units`` are the physical blocks; block ``b`` holds BS consecutive
   token rows of every KV head.
 * contiguous: request ``r`` owns the ``S/BS`` consecutive blocks starting at
@@ -59,24 +61,26 @@ def f32_to_f64(x: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def pair_tiles(cache: np.ndarray, head_dim: int, block_size: int):
-    """K tiles and V tiles of a cache held as tile pairs.
+    """K tiles and V tiles of a cache held as (block, head) regions.
 
     ``cache`` holds raw elements (any dtype; VE = 16 bytes / element size),
-    shape ``[..., 2*d*BS]`` or ``[..., 2, d*BS]``: per (block, KV head) the K
-    tile's ``d*BS`` elements, then the V tile's.  Returns views
-    ``(k_tiles [..., d/VE, BS, VE], v_tiles [..., d, BS])``.
+    shape ``[..., 2*d*BS]``: per (block, KV head) ``BS/sub`` tile pairs of
+    ``sub = min(BS, 16)`` rows, each the K tile ``[d/VE][sub][VE]`` of those
+    rows, then their V tile ``[d][sub]``.  Returns the block's tiles
+    ``(k_tiles [..., d/VE, BS, VE], v_tiles [..., d, BS])``: row ``o`` of the
+    block is row ``o % sub`` of pair ``o // sub``.
     """
     cache = np.asarray(cache)
-    n = head_dim * block_size
-    if cache.shape[-2:] == (2, n):
-        lead = cache.shape[:-2]
-    else:
-        assert cache.shape[-1] == 2 * n, "last axis must be one tile pair"
-        lead = cache.shape[:-1]
-    flat = cache.reshape(*lead, 2 * n)
-    ve = 16 // flat.itemsize
-    k = flat[..., :n].reshape(*lead, head_dim // ve, block_size, ve)
-    v = flat[..., n:].reshape(*lead, head_dim, block_size)
+    assert cache.shape[-1] == 2 * head_dim * block_size, "last axis must be one region"
+    lead = cache.shape[:-1]
+    sub = min(block_size, 16)
+    ve = 16 // cache.itemsize
+    pairs = cache.reshape(*lead, block_size // sub, 2, head_dim * sub)
+    k = pairs[..., 0, :].reshape(*lead, block_size // sub, head_dim // ve, sub, ve)
+    v = pairs[..., 1, :].reshape(*lead, block_size // sub, head_dim, sub)
+    # pair p's rows are the block's rows p*sub .. p*sub + sub - 1
+    k = np.moveaxis(k, -4, -3).reshape(*lead, head_dim // ve, block_size, ve)
+    v = np.moveaxis(v, -3, -2).reshape(*lead, head_dim, block_size)
     return k, v
 
 

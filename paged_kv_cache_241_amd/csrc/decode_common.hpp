@@ -1,7 +1,7 @@
 // Device helpers shared by the decode kernels (kernels.hip, decode_shared.hip):
 // wave constants, vector types, cache-read flavours, bf16 packing, and the
-// per-shape constants of the tile layout (K [D/VE][BS][VE], then V [D][BS],
-// per (block, head)).
+// per-shape constants of the tile layout (per (block, head), tile pairs of
+// up to 16 token rows: K [D/VE][rows][VE], then V [D][rows]).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -90,8 +90,13 @@ struct Geo {
   static constexpr int VE = 16 / ELT;          // elements per 16-byte K chunk
   static constexpr int NX = D / (4 * VE);      // 16-byte K loads per lane per chunk
   static constexpr int NN = D / 16;            // 16-column output tiles
-  static constexpr int TILE = D * BS * ELT;    // bytes of one K (or V) tile of a (block, head)
-  static constexpr int PAIR = 2 * TILE;        // a (block, head)'s K tile, then its V tile
+  // A (block, head) holds BS / SUB tile pairs of SUB = min(BS, 16) token
+  // rows each: the K tile [D/VE][SUB][VE], then the V tile [D][SUB].  With
+  // blocks of 16 or 32 every 16-token chunk is one pair, one contiguous run.
+  static constexpr int SUB = BS < kChunk ? BS : kChunk;
+  static constexpr int CH = D * SUB * ELT;     // bytes of one K (or V) tile of a pair
+  static constexpr int SUBPAIR = 2 * CH;       // one pair: K tile, then V tile
+  static constexpr int PAIR = D * BS * ELT * 2;  // all pairs of a (block, head)
 };
 
 }  // namespace

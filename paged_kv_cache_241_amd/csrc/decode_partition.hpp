@@ -58,7 +58,7 @@ template <int KIND, int D, int BS, int W, bool NT, bool PIPE = false, bool BAL =
 __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, const DecodeArgs& a, int bid,
                                                       int nblocks, float* lds) {
   using GG = Geo<KIND, D, BS>;
-  constexpr int NX = GG::NX, NN = GG::NN, TILE = GG::TILE, PAIR = GG::PAIR, ELT = GG::ELT;
+  constexpr int NX = GG::NX, NN = GG::NN, CH = GG::CH, SUBPAIR = GG::SUBPAIR, PAIR = GG::PAIR, ELT = GG::ELT;
   constexpr int kWaves = W;
   constexpr int kThreads = W * kWave;
   // V operand per lane per output tile: 4 consecutive tokens of one dim
@@ -186,7 +186,7 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
 
   // K tiles of the layer; each V tile follows its K tile
   const char* kl = geo.base + static_cast<int64_t>(a.layer) * geo.layer_bytes;
-  const char* vl = kl + TILE;
+  const char* vl = kl + CH;
   const int32_t* table = nullptr;
   int64_t first_block = 0;
   if (geo.paged) {
@@ -195,8 +195,9 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
     const int rid = a.req_ids ? a.req_ids[s] : s;
     first_block = static_cast<int64_t>(rid) * geo.blocks_per_seq;
   }
-  // byte offset of the tile pair (block of token t, kvh); t is clamped into
-  // the context so that every address stays inside a block the sequence owns
+  // byte offset of the tile pair (block of token t, kvh) for blocks shorter
+  // than a chunk (one pair per block); t is clamped into the context so that
+  // every address stays inside a block the sequence owns
   auto tile_of = [&](int t) -> int64_t {
     t = min(t, L - 1);
     const int64_t u = geo.paged ? static_cast<int64_t>(table[t / BS]) : first_block + t / BS;
@@ -221,25 +222,24 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   // u: the chunk's block when BS >= kChunk (from block_of_chunk)
   auto load = [&](int c, int64_t u, uint4 (&kk)[NX], VOp (&vv)[NN]) {
     if constexpr (BS >= kChunk) {
-      // the chunk lies in one block: a wave-uniform tile base plus a 32-bit
-      // lane offset (rows past the context stay inside the tile)
-      const int64_t tile = (u * hkv + kvh) * PAIR;
+      // the chunk is one tile pair of its block: a wave-uniform pair base
+      // plus a 32-bit lane offset (rows past the context stay inside it)
+      const int64_t tile = (u * hkv + kvh) * PAIR + ((c * kChunk) % BS / kChunk) * SUBPAIR;
       const char* kt = kl + tile;
       const char* vt = vl + tile;
-      const int row0 = (c * kChunk) % BS;
       // the empty asm keeps each lane offset a 32-bit value inside the loop,
       // so that the loads use a scalar base plus a 32-bit vector offset
       // instead of a 64-bit vector address per lane
-      uint32_t ko = static_cast<uint32_t>((j4 * BS + row0 + n) * 16);
+      uint32_t ko = static_cast<uint32_t>((j4 * kChunk + n) * 16);
       asm volatile("" : "+v"(ko));
 #pragma unroll
-      for (int x = 0; x < NX; ++x) kk[x] = kv16<NT>(kt + ko + x * 4 * BS * 16);
-      uint32_t vo = static_cast<uint32_t>((n * BS + row0 + 4 * j4) * ELT);
+      for (int x = 0; x < NX; ++x) kk[x] = kv16<NT>(kt + ko + x * 4 * kChunk * 16);
+      uint32_t vo = static_cast<uint32_t>((n * kChunk + 4 * j4) * ELT);
       asm volatile("" : "+v"(vo));
 #pragma unroll
       for (int nb = 0; nb < NN; ++nb) {
-        if constexpr (KIND == kBF16) vv[nb] = kv8<NT>(vt + vo + nb * 16 * BS * ELT);
-        else vv[nb] = kv16<NT>(vt + vo + nb * 16 * BS * ELT);
+        if constexpr (KIND == kBF16) vv[nb] = kv8<NT>(vt + vo + nb * 16 * kChunk * ELT);
+        else vv[nb] = kv16<NT>(vt + vo + nb * 16 * kChunk * ELT);
       }
     } else {
       // blocks shorter than a chunk: each lane finds its own block
@@ -541,19 +541,16 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
       if (slot >= 0) {
         const int64_t u = slot / BS;
         const int o = slot % BS;                 // row in the block
-        const int row0 = o - o % kChunk;          // the chunk's first row
-        char* kt = geo.base + static_cast<int64_t>(a.layer) * geo.layer_bytes + (u * hkv + kvh) * PAIR;
-        char* vt = kt + TILE;
+        const int oc = o % kChunk;                // row in the chunk (its tile pair)
+        char* kt = geo.base + static_cast<int64_t>(a.layer) * geo.layer_bytes + (u * hkv + kvh) * PAIR +
+                   (o / kChunk) * SUBPAIR;
+        char* vt = kt + CH;
         constexpr int kVUnits = D * kChunk * ELT / 16;   // 16-byte units of the chunk's V
-        constexpr int kPerRow = kChunk * ELT / 16;        // units per dim row
-        for (int t = tid; t < kVUnits; t += kThreads) {
-          const int e = t / kPerRow, q = t % kPerRow;
-          *reinterpret_cast<uint4*>(vt + (e * BS + row0) * ELT + q * 16) =
-              *reinterpret_cast<const uint4*>(stage_v + t * 16);
-        }
+        for (int t = tid; t < kVUnits; t += kThreads)
+          *reinterpret_cast<uint4*>(vt + t * 16) = *reinterpret_cast<const uint4*>(stage_v + t * 16);
         for (int t = tid; t < 2 * kRowVec; t += kThreads) {
-          const int r = t / kRowVec, q = t % kRowVec;   // row (o & ~1) + r, piece q
-          *reinterpret_cast<uint4*>(kt + (q * BS + (o & ~1) + r) * 16) =
+          const int r = t / kRowVec, q = t % kRowVec;   // row (oc & ~1) + r, piece q
+          *reinterpret_cast<uint4*>(kt + (q * kChunk + (oc & ~1) + r) * 16) =
               *reinterpret_cast<const uint4*>(stage_k + r * D * ELT + q * 16);
         }
       }
@@ -570,7 +567,7 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
     char* kt = geo.base + static_cast<int64_t>(a.layer) * geo.layer_bytes + (u * hkv + kvh) * PAIR;
     *reinterpret_cast<uint4*>(kt + (q * BS + o) * 16) = sm_new[q];
     const uint4 vw = sm_new[kRowVec + q];
-    char* vt = kt + TILE;
+    char* vt = kt + CH;
     const uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
     if constexpr (KIND == kBF16) {
 #pragma unroll

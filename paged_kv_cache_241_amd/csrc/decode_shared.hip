@@ -68,7 +68,7 @@ template <int KIND, int D, int BS>
 __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeArgs& a, const SharedArgs& g,
                                             int w, char* lds) {
   using GG = Geo<KIND, D, BS>;
-  constexpr int NX = GG::NX, NN = GG::NN, TILE = GG::TILE, PAIR = GG::PAIR, ELT = GG::ELT;
+  constexpr int NX = GG::NX, NN = GG::NN, CH = GG::CH, SUBPAIR = GG::SUBPAIR, PAIR = GG::PAIR, ELT = GG::ELT;
   constexpr int kThreads = kSharedWaves * kWave;
   constexpr int kUnits = D * ELT;  // 16-byte units of one chunk's K, and of its V
   // Stages of STEP consecutive chunks move through LDS (double buffered).
@@ -131,7 +131,7 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
 
   // K tiles of the layer; each V tile follows its K tile
   const char* kl = geo.base + static_cast<int64_t>(a.layer) * geo.layer_bytes;
-  const char* vl = kl + TILE;
+  const char* vl = kl + CH;
   // the group's blocks are its first member's (all members hold the same ones)
   const const_i32_ptr table = reinterpret_cast<const_i32_ptr>(
       reinterpret_cast<uintptr_t>(a.tables + static_cast<int64_t>(first) * a.table_stride));
@@ -152,14 +152,14 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
     if constexpr (kUnits % kThreads == 0) return (k * kThreads) / kUnits;
     else return __builtin_amdgcn_readfirstlane((wave * kWave + k * kThreads) / kUnits);
   };
-  // the lane's offsets of its units inside a (block, head) tile, for blocks
-  // of at least a chunk (the chunk's first row adds a wave-uniform part)
+  // the lane's offsets of its units inside a chunk's tile pair, for blocks
+  // of at least a chunk (the pair's place in its block is wave-uniform)
   uint32_t ko[kPerS], vo[kPerS];
 #pragma unroll
   for (int k = 0; k < kPerS; ++k) {
     const int uu = tid + k * kThreads - chunk_of(k) * kUnits;
-    ko[k] = static_cast<uint32_t>(((uu / 16) * BS + uu % 16) * 16);
-    vo[k] = static_cast<uint32_t>(((uu / ELT) * BS + (uu % ELT) * (16 / ELT)) * ELT);
+    ko[k] = static_cast<uint32_t>(uu * 16);
+    vo[k] = static_cast<uint32_t>(((uu / ELT) * kChunk + (uu % ELT) * (16 / ELT)) * ELT);
   }
   uint4 sk[kPerS], sv[kPerS];
   // stage st of the partition: chunks cb + st*STEP + j, clamped into the
@@ -172,9 +172,9 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
       for (int j = 0; j < STEP; ++j) {
         const int c = min(cb + st * STEP + j, ce - 1);
         const int64_t blk = table[__builtin_amdgcn_readfirstlane((c * kChunk) / BS)];
-        const int64_t tile = (blk * hkv + kvh) * PAIR;
-        kb[j] = kl + tile + ((c * kChunk) % BS) * 16;
-        vb[j] = vl + tile + ((c * kChunk) % BS) * ELT;
+        const int64_t tile = (blk * hkv + kvh) * PAIR + ((c * kChunk) % BS / kChunk) * SUBPAIR;
+        kb[j] = kl + tile;
+        vb[j] = vl + tile;
       }
 #pragma unroll
       for (int k = 0; k < kPerS; ++k) {

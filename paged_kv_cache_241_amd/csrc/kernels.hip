@@ -292,26 +292,28 @@ __device__ __forceinline__ void append_item(const CacheGeom& g, int32_t layer, c
   const int slot = slots[i];
   if (slot < 0) return;
   const int64_t u = slot / g.block_size;
-  const int o = slot % g.block_size;
-  char* kt = g.base + static_cast<int64_t>(layer) * g.layer_bytes + (u * g.num_kv_heads + h) * 2 * g.tile_bytes;
-  *reinterpret_cast<uint4*>(kt + (static_cast<int64_t>(q) * g.block_size + o) * 16) = k[idx];
+  // the row's tile pair in its (block, head): pairs of up to 16 rows
+  const int sub = g.block_size < 16 ? g.block_size : 16;
+  const int o = slot % g.block_size % sub;
+  const int64_t sub_bytes = static_cast<int64_t>(g.head_dim) * sub * g.elt;
+  char* kt = g.base + static_cast<int64_t>(layer) * g.layer_bytes + (u * g.num_kv_heads + h) * 2 * g.tile_bytes +
+             (slot % g.block_size / sub) * 2 * sub_bytes;
+  *reinterpret_cast<uint4*>(kt + (static_cast<int64_t>(q) * sub + o) * 16) = k[idx];
   const uint4 w = v[idx];
-  char* vt = kt + g.tile_bytes;
+  char* vt = kt + sub_bytes;
   const int d0 = q * ve;
   if (g.elt == 2) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      *reinterpret_cast<uint16_t*>(vt + ((d0 + 2 * e) * g.block_size + o) * 2) =
-          static_cast<uint16_t>(ws[e] & 0xFFFFu);
-      *reinterpret_cast<uint16_t*>(vt + ((d0 + 2 * e + 1) * g.block_size + o) * 2) =
-          static_cast<uint16_t>(ws[e] >> 16);
+      *reinterpret_cast<uint16_t*>(vt + ((d0 + 2 * e) * sub + o) * 2) = static_cast<uint16_t>(ws[e] & 0xFFFFu);
+      *reinterpret_cast<uint16_t*>(vt + ((d0 + 2 * e + 1) * sub + o) * 2) = static_cast<uint16_t>(ws[e] >> 16);
     }
   } else {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      *reinterpret_cast<uint32_t*>(vt + ((d0 + e) * g.block_size + o) * 4) = ws[e];
+      *reinterpret_cast<uint32_t*>(vt + ((d0 + e) * sub + o) * 4) = ws[e];
   }
 }
 

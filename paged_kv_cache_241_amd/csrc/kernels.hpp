@@ -14,19 +14,21 @@ enum Kind : int { kF32 = 0, kBF16 = 1 };
 constexpr int kDecodeWaves = 4;
 
 // Cache geometry.  One array holds K and V of every layer.  Per layer it is
-// an array of tile pairs, one pair per (block, KV head): the K tile, then the
-// V tile of the same block and head, so that the two form one contiguous run
-// (2 x 4 KiB for bf16, 16 tokens, head_dim 128):
-//   K tile [head_dim/VE][block_size][VE]  (16-byte chunks, VE = 16/elt)
-//   V tile [head_dim][block_size]
-// Pair (u, h) of layer l starts at l*layer_bytes + (u*num_kv_heads + h) *
-// 2*tile_bytes from the base; its V tile tile_bytes further on.  Paged: u is
-// the physical block.  Contiguous: request r owns blocks r*blocks_per_seq ..
-// r*blocks_per_seq + blocks_per_seq - 1.  A slot is u*block_size + row.
+// an array of (block, KV head) regions of 2*tile_bytes each.  A region holds
+// block_size / sub tile pairs, sub = min(block_size, 16) token rows each: the
+// K tile, then the V tile of the same rows, so that a 16-token chunk is one
+// contiguous run (2 x 4 KiB for bf16, head_dim 128):
+//   K tile [head_dim/VE][sub][VE]  (16-byte chunks, VE = 16/elt)
+//   V tile [head_dim][sub]
+// Region (u, h) of layer l starts at l*layer_bytes + (u*num_kv_heads + h) *
+// 2*tile_bytes from the base; row o's pair o / sub pairs further on.  Paged:
+// u is the physical block.  Contiguous: request r owns blocks
+// r*blocks_per_seq .. r*blocks_per_seq + blocks_per_seq - 1.  A slot is
+// u*block_size + row.
 struct CacheGeom {
   char* base = nullptr;        // layer 0, block 0, head 0, K tile
   int64_t layer_bytes = 0;     // bytes of one layer (K and V)
-  int64_t tile_bytes = 0;      // bytes of one K (or V) tile: head_dim * block_size * elt
+  int64_t tile_bytes = 0;      // K (or V) bytes of one (block, head): head_dim * block_size * elt
   int32_t num_layers = 0;
   int32_t num_kv_heads = 0;
   int32_t head_dim = 0;

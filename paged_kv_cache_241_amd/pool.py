@@ -33,12 +33,10 @@ def _stream_handle(stream):
 class Pool:
     """The KV cache of ``num_layers`` layers plus the host block allocator.
 
-    ``kv_cache`` is the one array include/pa.h lays out, a tile pair per
-    (block, KV head): ``[num_layers][units][num_kv_heads][2][head_dim * block_size]``
-    (K tile, then V tile).  ``k_cache`` and ``v_cache`` are views of its K and V
-    tiles:
-      ``k_cache``: ``[num_layers][units][num_kv_heads][head_dim/VE][block_size][VE]``
-      ``v_cache``: ``[num_layers][units][num_kv_heads][head_dim][block_size]``
+    ``kv_cache`` is the one array include/pa.h lays out, one region per
+    (block, KV head): ``[num_layers][units][num_kv_heads][2 * head_dim * block_size]``,
+    each region ``block_size / sub`` tile pairs of ``sub = min(block_size, 16)``
+    token rows (K tile ``[head_dim/VE][sub][VE]``, then V tile ``[head_dim][sub]``),
     with ``VE = 16 / element bytes`` and ``units = num_blocks`` (paged) or
     ``max_seqs * max_seq_len / block_size`` (contiguous: request r owns the
     ``max_seq_len / block_size`` consecutive blocks from ``r * max_seq_len / block_size``).
@@ -54,8 +52,8 @@ class Pool:
 
         ``vmm_bytes``: a demand-paged contiguous pool (pa_create_pool_vmm) whose
         cache the library backs with up to that many bytes of physical pages
-        as requests grow; ``kv_cache`` / ``k_cache`` / ``v_cache`` are then None
-        (the library owns the memory and unbacked ranges must not be read)."""
+        as requests grow; ``kv_cache`` is then None (the library owns the
+        memory and unbacked ranges must not be read)."""
         import torch
 
         self.lib = capi.load()
@@ -69,15 +67,12 @@ class Pool:
             raise capi.PaError(capi.PA_ERR_INVALID_ARG, "Pool", "invalid pool description")
         tdt = torch.bfloat16 if kv_dtype == "bf16" else torch.float32
         units = num_blocks if layout == "paged" else max_seqs * (max_seq_len // block_size)
-        ve = 16 // (2 if kv_dtype == "bf16" else 4)
-        kv_shape = (num_layers, units, num_kv_heads, 2, head_dim * block_size)
-        k_shape = (num_layers, units, num_kv_heads, head_dim // ve, block_size, ve)
-        v_shape = (num_layers, units, num_kv_heads, head_dim, block_size)
+        kv_shape = (num_layers, units, num_kv_heads, 2 * head_dim * block_size)
         self.vmm = vmm_bytes is not None
         if self.vmm:
             if layout != "contiguous":
                 raise ValueError("demand paging backs the contiguous layout")
-            self.kv_cache = self.k_cache = self.v_cache = None
+            self.kv_cache = None
             h = ctypes.c_void_p()
             capi.check(self.lib.pa_create_pool_vmm(ctypes.byref(self.desc), int(vmm_bytes),
                                                    ctypes.byref(h)), "pa_create_pool_vmm")
@@ -85,17 +80,12 @@ class Pool:
                          max_seq_len, tdt)
             return
         if host_only:
-            self.kv_cache = self.k_cache = self.v_cache = None
+            self.kv_cache = None
             self._fake = torch.empty(16, dtype=torch.uint8)
+        elif fill is None:
+            self.kv_cache = torch.empty(kv_shape, dtype=tdt, device=device)
         else:
-            if fill is None:
-                self.kv_cache = torch.empty(kv_shape, dtype=tdt, device=device)
-            else:
-                self.kv_cache = torch.full(kv_shape, fill, dtype=tdt, device=device)
-            # views of the K tiles and the V tiles (the last axis of a tile
-            # pair's half is contiguous, so it splits into the tile's axes)
-            self.k_cache = self.kv_cache[:, :, :, 0].view(k_shape)
-            self.v_cache = self.kv_cache[:, :, :, 1].view(v_shape)
+            self.kv_cache = torch.full(kv_shape, fill, dtype=tdt, device=device)
         if host_only:
             # any 16-byte aligned address: allocator calls never dereference it
             ptr = (self._fake.data_ptr() + 15) // 16 * 16

@@ -60,7 +60,7 @@ def test_cpu_baseline_spreads_the_oracle_over_host_cores():
     rids = [pool.add() for _ in range(6)]
     pool.reserve(rids, [17, 40, 1, 33, 64, 5])
     g = torch.Generator().manual_seed(3)
-    kv = torch.randn((1, 64, 2, 2, 64 * 16), generator=g).to(torch.bfloat16)
+    kv = torch.randn((1, 64, 2, 2 * 64 * 16), generator=g).to(torch.bfloat16)
     fake = SimpleNamespace(
         cfg=SimpleNamespace(block_size=16, max_seq_len=256, kv_dtype="bf16", num_kv_heads=2,
                             head_dim=64),

@@ -423,8 +423,7 @@ def test_fused_append_decode_equals_separate_calls(cid, over, layout, pt):
     a = sep.decode(partition_tokens=pt)
     b = fus.decode(partition_tokens=pt, append=(k, v, fus.step_slots))
     assert torch.equal(a, b)
-    assert torch.equal(sep.pool.k_cache, fus.pool.k_cache)
-    assert torch.equal(sep.pool.v_cache, fus.pool.v_cache)
+    assert torch.equal(sep.pool.kv_cache, fus.pool.kv_cache)
     _check(fus, b, range(cfg.batch))
     if cid == 5:
         # the step's first private write copied each prompt's shared last block
@@ -449,5 +448,4 @@ def test_fused_append_skips_negative_slots(batch):
     # the caches hold every new row exactly once and nothing else changed:
     # the same bytes as separate appends of all rows
     ref.pool.append_kv(0, k, v, ref.step_slots)
-    assert torch.equal(case.pool.k_cache, ref.pool.k_cache)
-    assert torch.equal(case.pool.v_cache, ref.pool.v_cache)
+    assert torch.equal(case.pool.kv_cache, ref.pool.kv_cache)

@@ -238,13 +238,23 @@ def test_pair_tiles_worked_example():
     assert A.k_rows(kt)[0, 0].tolist() == [[0, 1, 2, 3, 8, 9, 10, 11], [4, 5, 6, 7, 12, 13, 14, 15]]
     assert A.v_rows(vt)[0, 0].tolist() == [[16, 18, 20, 22, 24, 26, 28, 30],
                                            [17, 19, 21, 23, 25, 27, 29, 31]]
-    # bf16 bits (VE = 8), d = 8, BS = 1, two heads given as [..., 2, d*BS]:
-    # head 1's K row is elements 16..23, its V row 24..31
-    bits = np.arange(32, dtype=np.uint16).reshape(1, 2, 2, 8)
+    # bf16 bits (VE = 8), d = 8, BS = 1, two heads: head 1's K row is
+    # elements 16..23, its V row 24..31
+    bits = np.arange(32, dtype=np.uint16).reshape(1, 2, 16)
     kt, vt = A.pair_tiles(bits, 8, 1)
     assert kt.shape == (1, 2, 1, 1, 8) and vt.shape == (1, 2, 8, 1)
     assert A.k_rows(kt)[0, 1, 0].tolist() == list(range(16, 24))
     assert A.v_rows(vt)[0, 1, 0].tolist() == list(range(24, 32))
+    # 32-token blocks, fp32 (VE = 4), d = 4: two pairs of 16 rows.  Pair 0:
+    # K elements 0..63 (row r: 4r .. 4r+3), V 64..127 (dim e, row r: 64 +
+    # 16e + r); pair 1 the same from 128.  Block row 17 is row 1 of pair 1.
+    region = np.arange(256, dtype=np.float32).reshape(1, 256)
+    kt, vt = A.pair_tiles(region, 4, 32)
+    assert kt.shape == (1, 1, 32, 4) and vt.shape == (1, 4, 32)
+    kr, vr = A.k_rows(kt)[0], A.v_rows(vt)[0]
+    assert kr[0].tolist() == [0, 1, 2, 3] and kr[15].tolist() == [60, 61, 62, 63]
+    assert kr[16].tolist() == [128, 129, 130, 131] and kr[17].tolist() == [132, 133, 134, 135]
+    assert vr[0].tolist() == [64, 80, 96, 112] and vr[17].tolist() == [193, 209, 225, 241]
 
 
 def test_contiguous_rows_follow_reqid_times_s():

@@ -47,8 +47,7 @@ def _one(cfg, pt):
                                        partition_tokens=pt)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
-    assert torch.equal(ref.pool.k_cache, new.pool.k_cache)
-    assert torch.equal(ref.pool.v_cache, new.pool.v_cache)
+    assert torch.equal(ref.pool.kv_cache, new.pool.kv_cache)
     check_rows(new, b, range(cfg.batch))
     return need
 
