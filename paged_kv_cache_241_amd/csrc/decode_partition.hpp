@@ -195,14 +195,6 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
     const int rid = a.req_ids ? a.req_ids[s] : s;
     first_block = static_cast<int64_t>(rid) * geo.blocks_per_seq;
   }
-  // byte offset of the tile pair (block of token t, kvh) for blocks shorter
-  // than a chunk (one pair per block); t is clamped into the context so that
-  // every address stays inside a block the sequence owns
-  auto tile_of = [&](int t) -> int64_t {
-    t = min(t, L - 1);
-    const int64_t u = geo.paged ? static_cast<int64_t>(table[t / BS]) : first_block + t / BS;
-    return (u * hkv + kvh) * PAIR;
-  };
 
   float m = -INFINITY;  // running max of head n (log2 units)
   float lsum = 0.0f;    // this lane's share of head n's weight sum
@@ -242,14 +234,26 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
         else vv[nb] = kv16<NT>(vt + vo + nb * 16 * kChunk * ELT);
       }
     } else {
-      // blocks shorter than a chunk: each lane finds its own block
+      // blocks shorter than a chunk: the chunk spans blocks j0 and j0 + 1
+      // (the second clamped into the context); both table entries are
+      // wave-uniform scalar loads and each lane takes its token's (a table
+      // entry per lane would be a dependent vector load)
+      const int j0 = (c * kChunk) / BS;
+      const int j1 = min(j0 + 1, (L - 1) / BS);
+      auto entry = [&](int j) -> int64_t {
+        return geo.paged ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(
+                               reinterpret_cast<const_i32_ptr>(reinterpret_cast<uintptr_t>(table))[j]))
+                         : first_block + j;
+      };
+      const int64_t p0 = (entry(j0) * hkv + kvh) * PAIR, p1 = (entry(j1) * hkv + kvh) * PAIR;
+      auto pair_of = [&](int t) -> int64_t { return min(t, L - 1) / BS == j0 ? p0 : p1; };
       const int tk = c * kChunk + n;
-      const char* kt = kl + tile_of(tk) + (tk % BS) * 16;
+      const char* kt = kl + pair_of(tk) + (tk % BS) * 16;
 #pragma unroll
       for (int x = 0; x < NX; ++x) kk[x] = kv16<NT>(kt + (x * 4 + j4) * BS * 16);
       int tv = c * kChunk + 4 * j4;
       tv = min(tv, ((L - 1) / 4) * 4);
-      const char* vt = vl + tile_of(tv) + (tv % BS) * ELT;
+      const char* vt = vl + pair_of(tv) + (tv % BS) * ELT;
 #pragma unroll
       for (int nb = 0; nb < NN; ++nb) {
         if constexpr (KIND == kBF16) vv[nb] = kv8<NT>(vt + (nb * 16 + n) * BS * ELT);
