@@ -418,39 +418,47 @@ def swap_probe(bench, n: int) -> dict:
             "image": "pinned host memory"}
 
 
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "pa_decode_llama3-8b_b64_ctx1024_hbm_counters.md")
+COUNTERS_GLOB = os.path.join(ROOT, "profiles", "*_hbm_counters.md")
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed counter summary, or None.
+def measured_traffic(workload: str, steps: int, warmup: int):
+    """HBM bytes per decode step of one layer from the committed counter summaries, or None.
 
-    The rocprofv3 FETCH_SIZE / WRITE_SIZE runs of that summary were taken for
-    one workload and one kernel source; the figure is used only while both
-    still match (the kernel source's SHA-256 is compared).
+    Each summary's machine lines give, per workload, the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE bytes of one layer's launches and the device sources' digest
+    they were taken with; a line that names `steps` and `warmup` holds only
+    for a run with those counts (the contexts it decodes depend on them).  A
+    figure is used only while the sources still hash the same.
     """
-    try:
-        text = open(COUNTERS_FILE).read()
-    except OSError:
-        return None
+    import glob
+
     fields = {}
-    for line in text.splitlines():
-        if "traffic_bytes_per_launch=" in line:
-            kv = dict(item.split("=", 1) for item in line.split())
-            if kv.get("workload") == workload:
-                fields = kv
+    for path in sorted(glob.glob(COUNTERS_GLOB)):
+        try:
+            text = open(path).read()
+        except OSError:
+            continue
+        for line in text.splitlines():
+            if "traffic_bytes_per_launch=" in line:
+                kv = dict(item.split("=", 1) for item in line.split() if "=" in item)
+                if kv.get("workload") == workload:
+                    fields = kv
     if not fields:
+        return None
+    if "steps" in fields and (int(fields["steps"]) != steps or int(fields.get("warmup", -1)) != warmup):
         return None
     if kernel_source_digest() != fields.get("kernel_src_sha256_16"):
         return None
     return int(fields["traffic_bytes_per_launch"])
 
 
-# the sources the decode partition kernel is compiled from
-KERNEL_SOURCES = ("kernels.hip", "decode_partition.hpp", "decode_common.hpp", "kernels.hpp")
+# the sources every decode kernel (partition, plan, merge, shared) is compiled from
+KERNEL_SOURCES = ("kernels.hip", "decode_partition.hpp", "decode_common.hpp", "kernels.hpp",
+                  "decode_shared.hip")
 
 
 def kernel_source_digest() -> str:
-    """First 16 hex digits of SHA-256 over the partition kernel's sources, in order."""
+    """First 16 hex digits of SHA-256 over the decode kernels' sources, in order."""
     import hashlib
 
     h = hashlib.sha256()
@@ -718,7 +726,10 @@ def main():
                        ")") if args.shared_prefix else
                       ("pa_append_kv + pa_decode" if args.separate_append else "pa_append_decode"),
         },
-        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        # logical K/V bytes count a shared block once per sharer; the share of
+        # HBM's peak is taken on the distinct bytes
+        "pct_of_hbm_peak": round(100 * value * kv_frac / HBM_PEAK_GBS, 2),
+        "value_distinct_gbs": round(value * kv_frac, 2),
         "decode_us_per_layer": round(per_launch_s * 1e6, 3),
         "decode_kv_gbs": round(timed_kv / n_launches / per_launch_s / 1e9, 2),
         "decode_launches_timed": n_launches,
@@ -737,16 +748,28 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "kv_unique_fraction": round(kv_frac, 4),
+            "basis": "algorithmic bytes per launch" + (" (distinct blocks once)" if kv_frac < 1.0 else ""),
             "traffic": None,
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
         },
     }
-    # the counters were taken on workload 2 as it stands: no other batch,
-    # context, block size, layer count or partition size
-    as_counted = not (args.batch or args.context or args.block_size or args.layers or args.partition_tokens)
-    if args.config == 2 and args.layout == "paged" and as_counted:
-        res["roofline"]["traffic"] = measured_traffic(
-            "cfg2-paged" + ("" if args.separate_append else "-fused"))
+    # the counters were taken on each workload as it stands: no other batch,
+    # context, prompt, block size, layer count or partition size
+    as_counted = not (args.batch or args.context or args.block_size or args.layers or
+                      args.partition_tokens or args.prompt_len)
+    if args.layout == "paged" and as_counted:
+        key = (f"cfg{args.config}-paged" + (f"-shared{args.shared_prefix}" if args.shared_prefix else "") +
+               ("" if args.separate_append else "-fused"))
+        traffic = measured_traffic(key, args.steps, args.warmup)
+        roof = res["roofline"]
+        roof["traffic"] = traffic
+        if traffic is not None and kv_frac < 1.0:
+            # shared blocks may be served by the caches, so where blocks are
+            # shared the fraction is taken on the bytes HBM actually moved
+            roof["achieved_algorithmic"] = roof["achieved"]
+            roof["achieved"] = round(traffic / per_launch_s / 1e9, 2)
+            roof["frac"] = round(traffic / per_launch_s / 1e9 / HBM_PEAK_GBS, 4)
+            roof["basis"] = "measured HBM bytes (traffic) per launch"
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(bench, args.cpu_seconds)
         if cpu is not None:
@@ -769,9 +792,10 @@ def main():
             res["roofline"]["frac_of_probe_best"] = round(achieved / max(probe.values()), 4)
             if "decode_pattern" in probe:
                 res["roofline"]["frac_of_decode_pattern"] = round(achieved / probe["decode_pattern"], 4)
-            if "decode_mapped" in probe and args.config == 2 and as_counted:
-                # the same tiles in the decode's own order, no arithmetic
-                res["roofline"]["frac_of_decode_mapped"] = round(achieved / probe["decode_mapped"], 4)
+            if "decode_mapped_kv8k" in probe and args.config == 2 and as_counted:
+                # the same tiles in the decode's own order and the library's
+                # layout (K and V of a block side by side), no arithmetic
+                res["roofline"]["frac_of_decode_mapped"] = round(achieved / probe["decode_mapped_kv8k"], 4)
     print(json.dumps(res), flush=True)
 
 

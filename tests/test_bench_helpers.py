@@ -73,3 +73,30 @@ def test_cpu_baseline_spreads_the_oracle_over_host_cores():
     assert res["single_core"]["value"] > 0
     if cores > 1:
         assert res["value"] > res["single_core"]["value"]
+
+
+def test_measured_traffic_is_gated_by_workload_steps_and_source_digest(tmp_path, monkeypatch):
+    digest = bench.kernel_source_digest()
+    (tmp_path / "a_hbm_counters.md").write_text(
+        "text\n"
+        f"    traffic_bytes_per_launch=1000 kernel_src_sha256_16={digest} workload=cfg2-paged-fused\n"
+        f"    traffic_bytes_per_launch=2000 kernel_src_sha256_16={digest} workload=cfg3-paged-fused "
+        "steps=100 warmup=5\n"
+        "    traffic_bytes_per_launch=3000 kernel_src_sha256_16=0000000000000000 workload=cfg4-paged\n")
+    monkeypatch.setattr(bench, "COUNTERS_GLOB", str(tmp_path / "*_hbm_counters.md"))
+    assert bench.measured_traffic("cfg2-paged-fused", 7, 1) == 1000      # holds at any step count
+    assert bench.measured_traffic("cfg3-paged-fused", 100, 5) == 2000
+    assert bench.measured_traffic("cfg3-paged-fused", 20, 5) is None      # other contexts decoded
+    assert bench.measured_traffic("cfg4-paged", 100, 5) is None           # sources changed since
+    assert bench.measured_traffic("cfg1-paged", 100, 5) is None
+
+
+def test_committed_counter_lines_parse():
+    import glob
+    lines = [ln for p in glob.glob(bench.COUNTERS_GLOB) for ln in open(p).read().splitlines()
+             if "traffic_bytes_per_launch=" in ln]
+    assert len(lines) >= 5
+    for ln in lines:
+        kv = dict(item.split("=", 1) for item in ln.split())
+        assert int(kv["traffic_bytes_per_launch"]) > 0
+        assert len(kv["kernel_src_sha256_16"]) == 16 and kv["workload"].startswith("cfg")
