@@ -158,6 +158,7 @@ class Bench:
                          vmm_bytes=full if self.vmm else None)
         self.full_bytes = full
         self.reserve_s = 0.0   # host time inside pa_reserve during the prefill
+        self.step_reserve_s = 0.0   # host time inside the steps' pa_reserve calls
         if layout == "paged":
             order = np.concatenate([W.free_order(pl.num_blocks, cfg.seed),
                                     np.arange(pl.num_blocks, nb, dtype=np.int32)])
@@ -198,6 +199,7 @@ class Bench:
 
         W.run_ops(pl.ops, Tracked(), self.rids, on_reserve=self._prefill)
         torch.cuda.synchronize()
+        self.prefill_mapped = self.pool.vmm_stats()["mapped_bytes"] if self.vmm else 0
         for layer in range(num_layers):   # values no longer needed
             self.rows[layer] = None
         self.batch = [self.rids[h] for h in pl.batch_handles]
@@ -322,8 +324,10 @@ class Bench:
         if st["event"] is not None:
             st["event"].synchronize()        # its previous uploads have run
         b = len(self.batch)
+        t0 = time.perf_counter()
         self.check(lib.pa_reserve(pool.handle, self.rids_c, b, None, self.p32(st["slots"]), b,
                                   self.p32(st["pairs"]), b, ctypes.byref(self.ncow)), "pa_reserve")
+        self.step_reserve_s += time.perf_counter() - t0
         slots = st["slots"].numpy()
         if self.layout == "paged" and (self.ncow.value or bool((slots % cfg.block_size == 0).any())):
             self.tables_dirty = True
@@ -679,6 +683,7 @@ def main():
     lens_seen = []
     lens_all = []
     torch.cuda.synchronize()
+    bench.step_reserve_s = 0.0
     t0 = time.perf_counter()
     for i in range(args.steps):
         lens = bench.step(evs.get(i))
@@ -782,8 +787,13 @@ def main():
             "page_bytes": v["page_bytes"], "mapped_bytes": v["mapped_bytes"],
             "contiguous_reservation_bytes": bench.full_bytes,
             "mapped_share": round(v["mapped_bytes"] / bench.full_bytes, 4),
+            "prefill_mapped_bytes": bench.prefill_mapped,
             "prefill_reserve_s": round(bench.reserve_s, 4),
-            "map_rate_gbs": round(v["mapped_bytes"] / bench.reserve_s / 1e9, 2) if bench.reserve_s else None,
+            "prefill_map_rate_gbs": round(bench.prefill_mapped / bench.reserve_s / 1e9, 2) if bench.reserve_s else None,
+            # pages mapped by the warm-up and timed steps' pa_reserve calls
+            # (inside the timed region where contexts cross a page)
+            "steps_mapped_bytes": v["mapped_bytes"] - bench.prefill_mapped,
+            "timed_reserve_s": round(bench.step_reserve_s, 4),
         }
     if not args.no_hbm_probe:
         probe = hbm_probe()
