@@ -65,7 +65,8 @@
  * Validation: host-visible arguments are checked on the host.  Device arrays
  *   (tables, lengths, slots, pairs) are trusted: their entries must be in
  *   range; out-of-range entries give undefined results.  pa_check_decode_args,
- *   pa_check_slots and pa_check_block_pairs check host copies of them.
+ *   pa_check_slots, pa_check_block_pairs and pa_check_shared_args check host
+ *   copies of them.
  * Threads and streams: a pool is not thread-safe.  Device calls only enqueue
  *   work on the given stream (hipStream_t passed as void*, NULL = the default
  *   stream) and never synchronise; the caller orders them.

@@ -56,6 +56,24 @@ def test_workshop_readouts():
     assert 0.5 * w["median_ttft_paged_s"] < p["median_ttft_s"] < 2 * w["median_ttft_paged_s"]
 
 
+def test_contiguous_queue_never_drains_so_its_ttft_depends_on_the_run_length():
+    """At 18 requests/s the 52 contiguous slots serve fewer requests than
+    arrive: the median time to first token grows with the number simulated,
+    while paging's stays flat.  The page gives no run length; 1000 requests
+    brings out its 6.01 s."""
+    w = _golden()
+    c_ttft, p_ttft = [], []
+    for n in (300, 600, 1000):
+        out = AD.workshop(rate=w["rate_per_s"], requests=n)
+        c_ttft.append(out["contiguous"]["median_ttft_s"])
+        p_ttft.append(out["paged"]["median_ttft_s"])
+    assert c_ttft[0] < c_ttft[1] < c_ttft[2]
+    assert c_ttft[2] > 2 * c_ttft[1] > 4 * c_ttft[0]
+    assert abs(c_ttft[2] - w["median_ttft_contiguous_s"]) < 0.15 * w["median_ttft_contiguous_s"]
+    for t in p_ttft:
+        assert 0.5 * w["median_ttft_paged_s"] < t < 2 * w["median_ttft_paged_s"]
+
+
 class _OracleAllocator:
     """The oracle allocator under the simulation's admission rules."""
 
