@@ -41,11 +41,13 @@ constexpr bool decode_pipe_ok() { return KIND == kBF16 && BS >= kChunk; }
 __host__ __device__ constexpr int merge_lds_bytes(int waves, int G, int D) {
   return waves * G * (D + 2) * 4;
 }
-// LDS bytes after the merge area that a fused append stages its tail chunk in
-// (blocks of at least a chunk): the chunk's V tile rows (D x 16 tokens), the
-// two K rows that share the new row's 32-byte sectors, and the slot.
-__host__ __device__ constexpr int append_stage_bytes(int D, int elt) {
-  return D * 16 * elt + 2 * D * elt + 16;
+// LDS bytes after the merge area that a fused append uses: with blocks of
+// at least a chunk it stages its tail chunk there (the chunk's V tile rows,
+// D x 16 tokens, the two K rows that share the new row's 32-byte sectors, and
+// the slot); with shorter blocks it keeps the new row (K pieces, V pieces)
+// for the store after the loop.
+__host__ __device__ constexpr int append_lds_bytes(int D, int elt, int bs) {
+  return bs >= 16 ? D * 16 * elt + 2 * D * elt + 16 : 2 * D * elt;
 }
 
 // The body of decode_partition_kernel for workgroup `bid` of `nblocks`, with
@@ -54,7 +56,7 @@ __host__ __device__ constexpr int append_stage_bytes(int D, int elt) {
 // private partitions.  PIPE: each wave keeps the loads of its next chunk in
 // flight while it computes the current one.  BAL: the waves that hold one
 // chunk more than the others load their first two chunks together.
-template <int KIND, int D, int BS, int W, bool NT, bool PIPE = false, bool BAL = false>
+template <int KIND, int D, int BS, int W, bool NT, bool PIPE = false, bool BAL = false, bool PAIRED = false>
 __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, const DecodeArgs& a, int bid,
                                                       int nblocks, float* lds) {
   using GG = Geo<KIND, D, BS>;
@@ -77,7 +79,13 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   // last; after a shared-prefix pass it runs upwards, so that the private
   // partitions (the last ones) come first and the shared ones, which exit at
   // once, after them.
-  const int tid = threadIdx.x;
+  // PAIRED: the workgroup runs two work items, one per W waves, each with
+  // its own LDS; every wave then passes exactly one barrier, the merge's or
+  // (leaving early) the one in leave()
+  const int tid = PAIRED ? static_cast<int>(threadIdx.x) % kThreads : static_cast<int>(threadIdx.x);
+  auto leave = [] {
+    if constexpr (PAIRED) __syncthreads();
+  };
   // A balanced-start grid is at most two workgroups per CU, all resident
   // from the start; the second one on a CU (ids from kComputeUnits on, as the
   // dispatcher deals them) loses the SIMDs' issue arbitration to the older
@@ -89,7 +97,7 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   int s, kvh, part, L;
   if (a.plan != nullptr) {
     const int2 it = a.plan[bid / hkv];
-    if (it.x < 0) return;
+    if (it.x < 0) return leave();
     s = it.x / P;
     part = it.x % P;
     kvh = bid % hkv;
@@ -109,14 +117,14 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
         float* o = a.out + (static_cast<int64_t>(s) * a.num_q_heads + kvh * G) * D;
         for (int e = tid; e < G * D; e += kThreads) o[e] = 0.0f;
       }
-      return;
+      return leave();
     }
   }
   const int h0 = kvh * G;
   const int nch = (L + kChunk - 1) / kChunk;
   const int cb = part * a.partition_chunks;
   const int ce = min(nch, cb + a.partition_chunks);
-  if (a.seq_shared != nullptr && cb * kChunk < a.seq_shared[s]) return;  // the shared pass's
+  if (a.seq_shared != nullptr && cb * kChunk < a.seq_shared[s]) return leave();  // the shared pass's
 
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -136,7 +144,6 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   // waits for the slot (a slot < 0 appends nothing and the cache is read as
   // it is), so no load of the workgroup's start waits on another.
   constexpr int kRowVec = D * ELT / 16;  // 16-byte pieces of one row
-  __shared__ uint4 sm_new[2 * kRowVec];  // K pieces, then V pieces
   const bool last_new = a.new_k != nullptr && wave == 0 && ce == nch;
   int slot_new = -1;
   uint4 nk[NX];      // lane (n, j4): K pieces x*4+j4 of the new row
@@ -168,6 +175,8 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   char* stage_v = stage;                                    // [D][16] elements
   char* stage_k = stage + D * kChunk * ELT;                 // [2][D] elements
   int* stage_slot = reinterpret_cast<int*>(stage_k + 2 * D * ELT);
+  // blocks shorter than a chunk: the new row's K pieces, then its V pieces
+  uint4* sm_new = reinterpret_cast<uint4*>(stage);
 
   // q operand: head n of the group, zero beyond G (the row address is
   // clamped to a head of this group so that it always exists)

@@ -5,23 +5,26 @@
 // same K and V.  This pass reads each shared chunk once per (group, KV head)
 // and attends every member's query heads to it.
 //
-// One workgroup of 4 waves per (group, KV head, block of 64 query columns,
+// One workgroup of 8 waves per (group, KV head, block of 64 query columns,
 // partition of the shared prefix).  A query column is one (member, query
-// head) pair; wave w owns columns 16w .. 16w + 15 of the block, the same
-// 16-column MFMA tile the partition kernel uses for one sequence's heads.
-// Per stage of two 16-token chunks the workgroup copies K and V once into LDS
-// (double buffered, one barrier per stage); every wave reads its operands
-// from LDS and runs the score tiles, one online-softmax step and the P V
-// products over all stages of the partition.  Each wave writes its columns'
-// partials (running max, weight sum, unnormalised output) into the split-K
-// workspace at the members' own partition slots; the partition kernel does
-// the private partitions and the merge kernel combines them all in partition
-// order.
+// head) pair.  The waves form two sets of 4; in each set wave w owns columns
+// 16w .. 16w + 15 of the block, the same 16-column MFMA tile the partition
+// kernel uses for one sequence's heads.  Per stage of four 16-token chunks
+// (two for fp32) the workgroup copies K and V once into LDS (double
+// buffered, one barrier per stage); set s reads the stage's chunks 2s and
+// 2s + 1 from LDS and runs the score tiles, one online-softmax step and the
+// P V products.  At the end the second set's state merges into the first's,
+// which writes its columns' partials (running max, weight sum, unnormalised
+// output) into the split-K workspace at the members' own partition slots.
+// The rest of the launch runs the partition kernel's body for the private
+// partitions, two work items per workgroup (one per set of 4 waves), and the
+// merge kernel combines all partitions in partition order.
 //
-// What bounds it (measured on MI355X with per-workgroup clocks): the
-// workgroups' compute per stage (score tiles, softmax, P V on the VALU and
-// MFMA of a SIMD shared by 2-3 waves) more than the wait for the next stage's
-// loads, plus the launch ramp of ~640 workgroups.
+// What bounds it (measured on MI355X): the shared pass's per-stage chain
+// (load -> LDS -> score tiles, softmax, P V) more than HBM; two sets per
+// workgroup keep twice the loads in flight and halve the stages, which
+// shortened the Yi-6B shared-prefix step from 84.4 to 83.6 us per layer
+// (one set per 4-wave workgroup and 4-wave partition workgroups before).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -36,9 +39,14 @@
 namespace pa {
 namespace {
 
-constexpr int kSharedWaves = 4;
+// Two sets of 4 waves: the 4 waves of a set own the block's 64 query
+// columns, 16 each, and the two sets attend to different chunks of every
+// stage; their online-softmax states are merged at the end.
+constexpr int kSets = 2;
+constexpr int kSetWaves = 4;
+constexpr int kSharedWaves = kSets * kSetWaves;
 constexpr int kColsPerWave = 16;
-constexpr int kColsPerBlock = kSharedWaves * kColsPerWave;
+constexpr int kColsPerBlock = kSetWaves * kColsPerWave;
 
 // max over lanes l, l ^ 16 and l ^ 32 with the cross-lane swaps of the VALU
 // (v_permlane16_swap: rows 1 and 3 of the first operand trade places with
@@ -52,15 +60,16 @@ __device__ __forceinline__ float max_rows(float x) {
   return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
 }
 
-// Chunks per stage of the shared pass: two for bf16 (one 32-token P V step),
-// one for fp32 (which keeps the two stage buffers within 64 KiB).
+// Chunks per set and stage of the shared pass: two for bf16 (one 32-token
+// P V step), one for fp32 (which keeps the two stage buffers within 68 KiB).
 template <int KIND>
 constexpr int shared_step() { return KIND == kBF16 ? 2 : 1; }
-// LDS bytes of the shared pass: two stage buffers (see below)
+// LDS bytes of the shared pass: two stage buffers, each one part per set
+// (see below)
 template <int KIND, int D>
 constexpr int shared_lds_bytes() {
   constexpr int ELT = KIND == kBF16 ? 2 : 4, STEP = shared_step<KIND>();
-  return 2 * (STEP * D * ELT * 16 + 4 * (D * 4 * ELT * STEP + 128));
+  return 2 * kSets * (STEP * D * ELT * 16 + 4 * (D * 4 * ELT * STEP + 128));
 }
 
 // The shared pass of workgroup w, with `lds` shared_lds_bytes() of LDS.
@@ -71,22 +80,26 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
   constexpr int NX = GG::NX, NN = GG::NN, CH = GG::CH, SUBPAIR = GG::SUBPAIR, PAIR = GG::PAIR, ELT = GG::ELT;
   constexpr int kThreads = kSharedWaves * kWave;
   constexpr int kUnits = D * ELT;  // 16-byte units of one chunk's K, and of its V
-  // Stages of STEP consecutive chunks move through LDS (double buffered).
-  // K keeps the tile layout, [D/VE pieces][16 rows][16 B] per chunk: the
-  // score operands of a wave are 1 KiB contiguous reads.  V is regrouped:
-  // record (token group j4, dim e) holds tokens 4*j4 .. 4*j4+3 of dim e of
-  // each of the stage's chunks, chunk after chunk, so that a lane's P V
-  // operand is one 16-byte read and the 16 lanes of a token group read 256
-  // contiguous bytes (no bank conflicts); the four token groups are padded
-  // apart by 128 bytes.  For bf16 the two chunks of a stage form one 32-token
-  // P V step of v_mfma_f32_16x16x32_bf16, token (chunk j, 4*j4+i) being k
-  // index 8*j4 + 4*j + i of both operands.
+  // Stages of SCH consecutive chunks move through LDS (double buffered):
+  // set s attends to chunks s*STEP .. s*STEP + STEP-1 of each stage, held in
+  // its own part of the stage buffer.  K keeps the tile layout, [D/VE
+  // pieces][16 rows][16 B] per chunk: the score operands of a wave are 1 KiB
+  // contiguous reads.  V is regrouped: record (token group j4, dim e) holds
+  // tokens 4*j4 .. 4*j4+3 of dim e of each of the set's chunks, chunk after
+  // chunk, so that a lane's P V operand is one 16-byte read and the 16 lanes
+  // of a token group read 256 contiguous bytes (no bank conflicts); the four
+  // token groups are padded apart by 128 bytes.  For bf16 the two chunks of a
+  // set form one 32-token P V step of v_mfma_f32_16x16x32_bf16, token (chunk
+  // j, 4*j4+i) being k index 8*j4 + 4*j + i of both operands.
   constexpr int STEP = shared_step<KIND>();
-  constexpr int kStage = STEP * kUnits;  // 16-byte units of a stage's K (and of its V)
+  constexpr int SCH = kSets * STEP;       // chunks of a stage
+  constexpr int kSetUnits = STEP * kUnits;  // 16-byte units of a set's K (and of its V) per stage
+  constexpr int kStage = SCH * kUnits;      // 16-byte units of a stage's K (and of its V)
   constexpr int kVRec = 4 * ELT * STEP;
   constexpr int kVSeg = D * kVRec + 128;
-  constexpr int kKBytes = kStage * 16;
-  constexpr int kStageBuf = kKBytes + 4 * kVSeg;
+  constexpr int kKBytes = kSetUnits * 16;
+  constexpr int kSetBuf = kKBytes + 4 * kVSeg;
+  constexpr int kStageBuf = kSets * kSetBuf;
   static_assert(KIND != kBF16 || kVRec == 16, "a bf16 record is one 32-token operand");
   static_assert(2 * kStageBuf == shared_lds_bytes<KIND, D>(), "LDS stage buffers");
 
@@ -109,9 +122,11 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int set = wave / kSetWaves;   // which chunks of a stage
+  const int cw = wave % kSetWaves;    // which 16 columns
   const int n = lane & 15;
   const int j4 = lane >> 4;
-  const int col0 = cblk * kColsPerBlock + wave * kColsPerWave;
+  const int col0 = cblk * kColsPerBlock + cw * kColsPerWave;
 
   // q operand: column col0 + n = (member, head); columns past the group are
   // zero (their address is clamped to the group's last column)
@@ -162,15 +177,15 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
     vo[k] = static_cast<uint32_t>(((uu / ELT) * kChunk + (uu % ELT) * (16 / ELT)) * ELT);
   }
   uint4 sk[kPerS], sv[kPerS];
-  // stage st of the partition: chunks cb + st*STEP + j, clamped into the
+  // stage st of the partition: chunks cb + st*SCH + j, clamped into the
   // partition (the clamped copies are masked out below)
   auto load_stage = [&](int st, uint4 (&sk)[kPerS], uint4 (&sv)[kPerS]) {
     if constexpr (BS >= kChunk) {
-      const char* kb[STEP];
-      const char* vb[STEP];
+      const char* kb[SCH];
+      const char* vb[SCH];
 #pragma unroll
-      for (int j = 0; j < STEP; ++j) {
-        const int c = min(cb + st * STEP + j, ce - 1);
+      for (int j = 0; j < SCH; ++j) {
+        const int c = min(cb + st * SCH + j, ce - 1);
         const int64_t blk = table[__builtin_amdgcn_readfirstlane((c * kChunk) / BS)];
         const int64_t tile = (blk * hkv + kvh) * PAIR + ((c * kChunk) % BS / kChunk) * SUBPAIR;
         kb[j] = kl + tile;
@@ -183,7 +198,7 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
           const char* kbj = kb[0];
           const char* vbj = vb[0];
 #pragma unroll
-          for (int jj = 1; jj < STEP; ++jj) {
+          for (int jj = 1; jj < SCH; ++jj) {
             kbj = j == jj ? kb[jj] : kbj;
             vbj = j == jj ? vb[jj] : vbj;
           }
@@ -203,7 +218,7 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
         if (kPerS * kThreads == kStage || u < kStage) {
           const int j = chunk_of(k);
           const int uu = u - j * kUnits;
-          const int c = min(cb + st * STEP + j, ce - 1);
+          const int c = min(cb + st * SCH + j, ce - 1);
           const int t = c * kChunk + uu % 16;
           const int tv = c * kChunk + (uu % ELT) * (16 / ELT);
           const int32_t* trow = a.tables + static_cast<int64_t>(first) * a.table_stride;
@@ -215,15 +230,16 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
     }
   };
   auto store_stage = [&](int buf, const uint4 (&sk)[kPerS], const uint4 (&sv)[kPerS]) {
-    char* kd = lds + buf * kStageBuf;
-    char* vd = kd + kKBytes;
 #pragma unroll
     for (int k = 0; k < kPerS; ++k) {
       const int u = tid + k * kThreads;
       if (kPerS * kThreads == kStage || u < kStage) {
-        *reinterpret_cast<uint4*>(kd + u * 16) = sk[k];
-        const int j = chunk_of(k);
-        const int uu = u - j * kUnits;
+        const int jc = chunk_of(k);      // chunk of the stage
+        const int s = jc / STEP, j = jc % STEP;  // its set, and its place there
+        char* kd = lds + buf * kStageBuf + s * kSetBuf;
+        char* vd = kd + kKBytes;
+        *reinterpret_cast<uint4*>(kd + (u - s * kSetUnits) * 16) = sk[k];
+        const int uu = u - jc * kUnits;
         const int e = uu / ELT, q = uu % ELT;
         if constexpr (KIND == kBF16) {
           // tokens 8q .. 8q+7: token groups 2q and 2q+1
@@ -249,10 +265,11 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
   // stage st + 1 is loaded into registers; it goes to the other buffer after
   // the compute.  (A third stage in flight, in a second register set, was
   // measured slower: it costs occupancy and the wait is not the bound.)
-  const int stages = (ce - cb + STEP - 1) / STEP;
-  // one online-softmax step and the P V products of the stage in LDS buffer buf
+  const int stages = (ce - cb + SCH - 1) / SCH;
+  // one online-softmax step and the P V products of the set's chunks of the
+  // stage in LDS buffer buf
   auto compute = [&](int buf, int st) {
-    const char* kd = lds + buf * kStageBuf;
+    const char* kd = lds + buf * kStageBuf + set * kSetBuf;
     const char* vd = kd + kKBytes;
     // S[j][token 4*j4+i][column n]: the score tiles of the stage's chunks
     floatx4_t S[STEP];
@@ -274,13 +291,13 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
         }
       }
     }
-    // one online-softmax step for column n over the stage's chunks; chunks
+    // one online-softmax step for column n over the set's chunks; chunks
     // past the partition (clamped copies) weigh nothing
     float sc[STEP][4];
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < STEP; ++j) {
-      const bool live = cb + st * STEP + j < ce;
+      const bool live = cb + st * SCH + set * STEP + j < ce;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sc[j][i] = live ? S[j][i] * c2 : -INFINITY;
@@ -289,7 +306,10 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
     }
     mx = max_rows(mx);
     const float mn = fmaxf(m, mx);
-    const float alpha = fexp2(m - mn);
+    // a set whose chunks have all been past the partition so far keeps
+    // m = -inf and weighs nothing (mr avoids -inf - -inf)
+    const float mr = mn == -INFINITY ? 0.0f : mn;
+    const float alpha = fexp2(m - mr);
     m = mn;
     if (__any(alpha != 1.0f)) {
 #pragma unroll
@@ -301,7 +321,7 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
 #pragma unroll
     for (int j = 0; j < STEP; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[j][i] = fexp2(sc[j][i] - mn);
+      for (int i = 0; i < 4; ++i) p[j][i] = fexp2(sc[j][i] - mr);
     float part_sum = 0.0f;
     if constexpr (KIND == kBF16) {
       // weight = high + low, both bf16; the sum is what the MFMA multiplies
@@ -356,6 +376,35 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
     __syncthreads();
   }
 
+  // the second set's state of the same columns, into the first set's
+  // (the stage buffers are free after the loop's last barrier); per lane the
+  // two states cover disjoint chunks, so they merge as two partitions do
+  {
+    constexpr int R = 2 + 4 * NN;
+    static_assert(kSetWaves * R * kWave * 4 <= 2 * kStageBuf, "set merge fits the stage buffers");
+    float* xf = reinterpret_cast<float*>(lds) + cw * R * kWave + lane;
+    if (set == 1) {
+      xf[0] = m;
+      xf[kWave] = lsum;
+#pragma unroll
+      for (int nb = 0; nb < NN; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xf[(2 + 4 * nb + i) * kWave] = acc[nb][i];
+    }
+    __syncthreads();
+    if (set == 1) return;
+    // the first set's first chunk lies in the partition: m is finite
+    const float m1 = xf[0];
+    const float mn = fmaxf(m, m1);
+    const float a0 = fexp2(m - mn), a1 = fexp2(m1 - mn);
+    m = mn;
+    lsum = lsum * a0 + xf[kWave] * a1;
+#pragma unroll
+    for (int nb = 0; nb < NN; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[nb][i] = acc[nb][i] * a0 + xf[(2 + 4 * nb + i) * kWave] * a1;
+  }
+
   // partials of this wave's columns at the members' partition slot `part`
   lsum += xor16(lsum);
   lsum += xor32(lsum);
@@ -387,29 +436,41 @@ void decode_shared_kernel(CacheGeom geo, DecodeArgs a, SharedArgs g) {
   if (bid < g.n_shared) {
     shared_pass<KIND, D, BS>(geo, a, g, bid, lds_dyn);
   } else {
-    decode_partition_body<KIND, D, BS, kSharedWaves, true>(geo, a, bid - g.n_shared,
-                                                             gridDim.x - g.n_shared,
-                                                             reinterpret_cast<float*>(lds_dyn));
+    // two partition work items per workgroup, one per set of 4 waves, each
+    // with its own LDS; every wave passes exactly one barrier (the body's
+    // merge, or the one an idle half passes here)
+    const int half = static_cast<int>(threadIdx.x) / (kSetWaves * kWave);
+    const int item = 2 * (bid - g.n_shared) + half;
+    if (item >= g.n_private) {
+      __syncthreads();
+      return;
+    }
+    decode_partition_body<KIND, D, BS, kSetWaves, true, false, false, true>(
+        geo, a, item, g.n_private, reinterpret_cast<float*>(lds_dyn + half * g.private_lds));
   }
 }
 
 template <int KIND, int D>
 hipError_t launch_shared_d(const CacheGeom& g, const DecodeArgs& a, const SharedArgs& sh,
                            bool* supported, hipStream_t st) {
-  const int64_t nwork = static_cast<int64_t>(sh.n_shared) +
-                        static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
+  const int64_t n_private = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
+  const int64_t nwork = static_cast<int64_t>(sh.n_shared) + (n_private + 1) / 2;
   if (nwork == 0) return hipSuccess;
   const int G = a.num_q_heads / g.num_kv_heads;
-  // the shared pass's stage buffers, or the private partitions' merge (and,
-  // with a fused append, its staged tail chunk), whichever is larger
-  const int private_lds = merge_lds_bytes(kSharedWaves, G, D) +
-                          (a.new_k != nullptr && g.block_size >= kChunk ? append_stage_bytes(D, g.elt) : 0);
-  const size_t lds = static_cast<size_t>(std::max(shared_lds_bytes<KIND, D>(), private_lds));
+  // the shared pass's stage buffers, or two partition items' merge areas
+  // (and, with a fused append, their staged tail chunks), whichever is larger
+  const int private_lds = (merge_lds_bytes(kSetWaves, G, D) +
+                           (a.new_k != nullptr ? append_lds_bytes(D, g.elt, g.block_size) : 0) + 15) /
+                          16 * 16;
+  const size_t lds = static_cast<size_t>(std::max(shared_lds_bytes<KIND, D>(), 2 * private_lds));
+  SharedArgs sh2 = sh;
+  sh2.n_private = static_cast<int32_t>(n_private);
+  sh2.private_lds = private_lds;
   const dim3 grid(static_cast<uint32_t>(nwork)), block(kSharedWaves * kWave);
   switch (g.block_size) {
-    case 8: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 8>), grid, block, lds, st, g, a, sh); break;
-    case 16: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 16>), grid, block, lds, st, g, a, sh); break;
-    case 32: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 32>), grid, block, lds, st, g, a, sh); break;
+    case 8: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 8>), grid, block, lds, st, g, a, sh2); break;
+    case 16: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 16>), grid, block, lds, st, g, a, sh2); break;
+    case 32: hipLaunchKernelGGL((decode_shared_kernel<KIND, D, 32>), grid, block, lds, st, g, a, sh2); break;
     default: *supported = false; return hipSuccess;
   }
   return hipGetLastError();

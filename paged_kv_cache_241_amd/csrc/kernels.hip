@@ -373,7 +373,7 @@ hipError_t launch_decode_p(const CacheGeom& g, const DecodeArgs& a, hipStream_t 
   const int64_t nwork = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
   const int G = a.num_q_heads / g.num_kv_heads;
   const size_t lds = static_cast<size_t>(merge_lds_bytes(W, G, D)) +
-                     (a.new_k != nullptr && BS >= kChunk ? append_stage_bytes(D, g.elt) : 0);
+                     (a.new_k != nullptr ? append_lds_bytes(D, g.elt, BS) : 0);
   if (a.streaming)
     hipLaunchKernelGGL((decode_partition_kernel<KIND, D, BS, W, true, PIPE, BAL>), dim3(static_cast<uint32_t>(nwork)),
                        dim3(W * kWave), lds, st, g, a);

@@ -89,6 +89,10 @@ struct SharedArgs {
   int32_t col_blocks = 1;            // workgroups per (group, KV head, partition): 64 query columns each
   int32_t shared_parts = 0;          // partitions of the longest shared prefix
   int32_t n_shared = 0;              // shared-pass workgroups: groups x KV heads x col_blocks x shared_parts
+  // set by the launch: partition work items (sequences x KV heads x
+  // partitions, two per workgroup) and the LDS bytes of each one
+  int32_t n_private = 0;
+  int32_t private_lds = 0;
 };
 
 // The partition kernel and, with several partitions, the merge.  *supported
