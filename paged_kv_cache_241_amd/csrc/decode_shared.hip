@@ -178,14 +178,18 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
   }
   uint4 sk[kPerS], sv[kPerS];
   // stage st of the partition: chunks cb + st*SCH + j, clamped into the
-  // partition (the clamped copies are masked out below)
-  auto load_stage = [&](int st, uint4 (&sk)[kPerS], uint4 (&sv)[kPerS]) {
+  // partition (the clamped copies are masked out below).  past: the stage
+  // after the last, loaded only so that the loop needs no branch around its
+  // loads (a branch makes the wait for them also wait for every newer load);
+  // all lanes then read the first 16 bytes of the partition's first chunk,
+  // one line per wave instead of a stage of chunks from HBM again.
+  auto load_stage = [&](int st, bool past, uint4 (&sk)[kPerS], uint4 (&sv)[kPerS]) {
     if constexpr (BS >= kChunk) {
       const char* kb[SCH];
       const char* vb[SCH];
 #pragma unroll
       for (int j = 0; j < SCH; ++j) {
-        const int c = min(cb + st * SCH + j, ce - 1);
+        const int c = past ? cb : min(cb + st * SCH + j, ce - 1);
         const int64_t blk = table[__builtin_amdgcn_readfirstlane((c * kChunk) / BS)];
         const int64_t tile = (blk * hkv + kvh) * PAIR + ((c * kChunk) % BS / kChunk) * SUBPAIR;
         kb[j] = kl + tile;
@@ -204,7 +208,7 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
           }
           // a wave-uniform base plus a 32-bit lane offset (kept a 32-bit
           // value by the empty asm): the loads take the scalar-base form
-          uint32_t ok = ko[k], ov = vo[k];
+          uint32_t ok = past ? 0u : ko[k], ov = past ? 0u : vo[k];
           asm volatile("" : "+v"(ok), "+v"(ov));
           sk[k] = kv16<true>(kbj + ok);
           sv[k] = kv16<true>(vbj + ov);
@@ -217,8 +221,8 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
         const int u = tid + k * kThreads;
         if (kPerS * kThreads == kStage || u < kStage) {
           const int j = chunk_of(k);
-          const int uu = u - j * kUnits;
-          const int c = min(cb + st * SCH + j, ce - 1);
+          const int uu = past ? 0 : u - j * kUnits;
+          const int c = past ? cb : min(cb + st * SCH + j, ce - 1);
           const int t = c * kChunk + uu % 16;
           const int tv = c * kChunk + (uu % ELT) * (16 / ELT);
           const int32_t* trow = a.tables + static_cast<int64_t>(first) * a.table_stride;
@@ -363,14 +367,11 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
     }
     lsum = lsum * alpha + part_sum;
   };
-  load_stage(0, sk, sv);
+  load_stage(0, false, sk, sv);
   store_stage(0, sk, sv);
   __syncthreads();
   for (int st = 0; st < stages; ++st) {
-    // loads past the last stage re-read the partition's last chunk (an L2
-    // hit) rather than branch: a branch around loads makes the wait for them
-    // also wait for every newer load
-    load_stage(min(st + 1, stages - 1), sk, sv);
+    load_stage(st + 1, st + 1 >= stages, sk, sv);
     compute(st & 1, st);
     store_stage((st & 1) ^ 1, sk, sv);
     __syncthreads();
