@@ -69,7 +69,7 @@ namespace pa {
 namespace {
 
 constexpr int kMergeWaves = 4;   // merge rows per workgroup, one a wave
-constexpr int kMergeUnroll = 8;  // rows of up to this many partitions load all at once
+constexpr int kMergeUnroll = 8;  // rows of up to this many partitions load all at once (at most)
 constexpr int kMaxGroup = 16;     // query heads per KV head the tile can hold
 
 template <int KIND, int D, int BS, int W, bool NT, bool PIPE, bool BAL = false>
@@ -173,12 +173,13 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a,
 
 // Merge context partitions in partition order: one wave per (seq, q head),
 // kMergeWaves rows per workgroup, D / 64 output dims a lane.  Rows of up to
-// kMergeUnroll partitions issue all their loads (maxima and sums as scalar
-// loads, partial outputs as vector loads) before any arithmetic; longer rows
-// find their maximum 64 partitions a round in the lanes, then load and sum
-// kMergeUnroll partitions at a time.  The sums run over p in order, as
-// fma(w_p, acc_p, .) and fma(w_p, l_p, .).
-template <int D>
+// U partitions (2, 4 or kMergeUnroll: the launch's partition count rounded
+// up) issue all their loads (maxima and sums as scalar loads, partial
+// outputs as vector loads) before any arithmetic; longer rows find their
+// maximum 64 partitions a round in the lanes, then load and sum U partitions
+// at a time.  The sums run over p in order, as fma(w_p, acc_p, .) and
+// fma(w_p, l_p, .), whatever U is.
+template <int D, int U>
 __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(DecodeArgs a) {
   constexpr int E = D / kWave;
   static_assert(E * kWave == D, "D is a multiple of the wave");
@@ -198,12 +199,12 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(Decod
   float A[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) A[e] = 0.0f;
-  if (ps > 0 && ps <= kMergeUnroll) {
+  if (ps > 0 && ps <= U) {
     // all of the row's loads at once (indices clamped into [0, ps), the
     // copies past ps weigh nothing), then the same sums as below
-    float mp[kMergeUnroll], lp[kMergeUnroll], ap[kMergeUnroll][E];
+    float mp[U], lp[U], ap[U][E];
 #pragma unroll
-    for (int k = 0; k < kMergeUnroll; ++k) {
+    for (int k = 0; k < U; ++k) {
       const int p = min(k, ps - 1);
       mp[k] = ml[2 * p];
       lp[k] = ml[2 * p + 1];
@@ -213,12 +214,12 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(Decod
     // (the clamped copies repeat partition ps - 1: the max is unchanged)
     float mx = mp[0];
 #pragma unroll
-    for (int k = 1; k < kMergeUnroll; ++k) mx = fmaxf(mx, mp[k]);
+    for (int k = 1; k < U; ++k) mx = fmaxf(mx, mp[k]);
     // selects rather than branches, so that every load is used and issued
     // up front
     float Lt = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kMergeUnroll; ++k) {
+    for (int k = 0; k < U; ++k) {
       const float wt = fexp2(mp[k] - mx);
       const bool live = k < ps;
 #pragma unroll
@@ -233,17 +234,17 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(Decod
     for (int e = 0; e < E; ++e) A[e] = A[e] / Lt;
   } else if (ps > 0) {
     // the maximum over all partitions (64 a round in the lanes), then the
-    // sums in groups of kMergeUnroll partitions whose loads issue together
+    // sums in groups of U partitions whose loads issue together
     float mx = -INFINITY;
     for (int p0 = 0; p0 < ps; p0 += kWave)
       if (p0 + lane < ps) mx = fmaxf(mx, ml[2 * (p0 + lane)]);
 #pragma unroll
     for (int x = kWave / 2; x >= 1; x /= 2) mx = fmaxf(mx, __shfl_xor(mx, x));
     float Lt = 0.0f;
-    for (int p0 = 0; p0 < ps; p0 += kMergeUnroll) {
-      float mp[kMergeUnroll], lp[kMergeUnroll], ap[kMergeUnroll][E];
+    for (int p0 = 0; p0 < ps; p0 += U) {
+      float mp[U], lp[U], ap[U][E];
 #pragma unroll
-      for (int k = 0; k < kMergeUnroll; ++k) {
+      for (int k = 0; k < U; ++k) {
         const int p = min(p0 + k, ps - 1);
         mp[k] = ml[2 * p];
         lp[k] = ml[2 * p + 1];
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void decode_merge_kernel(Decod
         for (int e = 0; e < E; ++e) ap[k][e] = accp[static_cast<int64_t>(p) * D + e];
       }
 #pragma unroll
-      for (int k = 0; k < kMergeUnroll; ++k) {
+      for (int k = 0; k < U; ++k) {
         const float wt = fexp2(mp[k] - mx);
         const bool live = p0 + k < ps;
 #pragma unroll
@@ -411,8 +412,12 @@ hipError_t launch_decode_t(const CacheGeom& g, const DecodeArgs& a, hipStream_t 
 template <int D>
 hipError_t launch_merge_d(const DecodeArgs& a, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_q_heads;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(static_cast<uint32_t>((rows + kMergeWaves - 1) / kMergeWaves)),
-                     dim3(kMergeWaves * kWave), 0, st, a);
+  // rows load all their partitions at once up to U: the fewest loads that
+  // still cover the launch's partition count (clamped copies weigh nothing)
+  const dim3 grid(static_cast<uint32_t>((rows + kMergeWaves - 1) / kMergeWaves)), block(kMergeWaves * kWave);
+  if (a.num_partitions <= 2) hipLaunchKernelGGL((decode_merge_kernel<D, 2>), grid, block, 0, st, a);
+  else if (a.num_partitions <= 4) hipLaunchKernelGGL((decode_merge_kernel<D, 4>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((decode_merge_kernel<D, kMergeUnroll>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
