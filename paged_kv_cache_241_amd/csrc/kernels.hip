@@ -417,6 +417,9 @@ hipError_t launch_merge_d(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<uint32_t>((rows + kMergeWaves - 1) / kMergeWaves)), block(kMergeWaves * kWave);
   if (a.num_partitions <= 2) hipLaunchKernelGGL((decode_merge_kernel<D, 2>), grid, block, 0, st, a);
   else if (a.num_partitions <= 4) hipLaunchKernelGGL((decode_merge_kernel<D, 4>), grid, block, 0, st, a);
+  else if (a.num_partitions <= 8) hipLaunchKernelGGL((decode_merge_kernel<D, 8>), grid, block, 0, st, a);
+  else if (a.num_partitions <= 16) hipLaunchKernelGGL((decode_merge_kernel<D, 16>), grid, block, 0, st, a);
+  else if (a.num_partitions <= 32) hipLaunchKernelGGL((decode_merge_kernel<D, 32>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((decode_merge_kernel<D, kMergeUnroll>), grid, block, 0, st, a);
   return hipGetLastError();
 }

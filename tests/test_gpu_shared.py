@@ -98,6 +98,25 @@ def test_shared_decode_matches_oracle_and_plain_decode(over, T):
         assert err <= 1e-5, (s, err)
 
 
+def test_odd_number_of_partition_items_leaves_one_half_idle():
+    # The launch runs the private partitions two work items per workgroup;
+    # with sequences x KV heads x partitions odd, the last workgroup's second
+    # half has no item and only passes its barrier.  3 prompts x 3 samples,
+    # one KV head, 3 partitions of 32 tokens: 27 items.
+    cfg = W.get(5, batch=9, samples=3, prompt_len=64, private_len=20, num_blocks=100,
+                num_kv_heads=1, num_q_heads=8, max_seq_len=96)
+    case = Case(cfg)
+    T = 32
+    parts = -(-case.max_context // T)
+    assert (cfg.batch * cfg.num_kv_heads * parts) % 2 == 1
+    got, seq_shared, groups = _run_shared(case, T, list(range(cfg.batch)))
+    assert len(groups) == 3 and int(seq_shared.min()) == 64
+    _check_oracle(case, got)
+    plain = case.decode(partition_tokens=T)
+    for s in range(cfg.batch):
+        assert row_rel_err(to_f64(got[s]), to_f64(plain[s])) <= 1e-5, s
+
+
 def test_mixed_groups_and_singletons():
     cfg = W.get(5, batch=24, prompt_len=200, private_len=40, num_blocks=200)
     case = Case(cfg)
