@@ -61,7 +61,7 @@ __device__ __forceinline__ float max_rows(float x) {
 }
 
 // Chunks per set and stage of the shared pass: two for bf16 (one 32-token
-// P V step), one for fp32 (which keeps the two stage buffers within 68 KiB).
+// P V step), one for fp32 (which keeps the two stage buffers at 66 KiB).
 template <int KIND>
 constexpr int shared_step() { return KIND == kBF16 ? 2 : 1; }
 // LDS bytes of the shared pass: two stage buffers, each one part per set
