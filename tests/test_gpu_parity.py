@@ -149,6 +149,26 @@ def test_tiny_fp32_all_rows():
         assert np.array_equal(k, kl) and np.array_equal(v, vl)
 
 
+def test_tiny_fp32_other_reading_appends_at_position_l():
+    # The tiny workload's lengths {1, 17, 40, 100} read as the contexts before
+    # the step: the step appends token L and attends over L + 1 (prefills of
+    # 1, 17, 40 and 100 tokens; the appended token lands on row 1, 1, 8 and 4
+    # of its 16-token block), fused and as separate calls.
+    cfg = W.get(1, contexts_before_append=True)
+    # zero-filled pools, so that rows nobody writes compare equal too
+    sep = Case(cfg, step_append=False, fill=0.0)
+    fus = Case(cfg, step_append=False, fill=0.0)
+    assert [int(x) for x in sep.lens_np] == [2, 18, 41, 101]
+    assert [int(x) % cfg.block_size for x in sep.step_slots.cpu()] == [1, 1, 8, 4]
+    k, v = sep.step_kv()
+    sep.pool.append_kv(0, k, v, sep.step_slots)
+    out = sep.decode()
+    _check(sep, out, range(cfg.batch))
+    got = fus.decode(append=(k, v, fus.step_slots))
+    assert torch.equal(got, out)
+    assert torch.equal(fus.pool.kv_cache, sep.pool.kv_cache)
+
+
 @pytest.mark.parametrize("cid,over", [
     (2, {"batch": 5, "num_blocks": 5 * 64 + 7}),
     (3, {"batch": 6}),

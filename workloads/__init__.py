@@ -25,7 +25,9 @@ The five workloads follow the pages' settings:
 
 Every context length is the length *after* the decode step's append: a
 sequence is prefilled with ``L - 1`` tokens and the step appends token ``L-1``
-and attends over all ``L``.
+and attends over all ``L``.  The tiny workload also runs in the other
+reading (``contexts_before_append=True``): its lengths are the contexts
+before the step, which appends token ``L`` and attends over ``L + 1``.
 
 Values: q, K and V rows are N(0, 1) float32 draws from a seeded
 ``torch.Generator``, cast to bfloat16 with round-to-nearest-even where the
@@ -59,6 +61,7 @@ class Config:
     samples: int = 0
     private_len: int = 0
     seed: int = BASE_SEED
+    contexts_before_append: bool = False   # tiny workload: the other reading of its lengths
 
     @property
     def group(self) -> int:
@@ -132,6 +135,8 @@ def plan(cfg: Config) -> Plan:
     b = cfg.batch
     if cfg.cid == 1:
         lengths = np.array(TINY_LENGTHS[:b], dtype=np.int64)
+        if cfg.contexts_before_append:
+            lengths = lengths + 1
         if b > len(TINY_LENGTHS):
             extra = rng.integers(1, 129, b - len(TINY_LENGTHS))
             lengths = np.concatenate([lengths, extra])
