@@ -215,7 +215,10 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
         }
       }
     } else {
-      // blocks shorter than a chunk: each unit finds its own block
+      // 8-token blocks: a chunk spans two blocks, whose table entries are
+      // wave-uniform scalar loads (the shared prefix is whole chunks, so both
+      // lie in it); each unit takes its token's
+      static_assert(2 * BS == kChunk, "blocks shorter than a chunk are half a chunk");
 #pragma unroll
       for (int k = 0; k < kPerS; ++k) {
         const int u = tid + k * kThreads;
@@ -223,12 +226,13 @@ __device__ __forceinline__ void shared_pass(const CacheGeom& geo, const DecodeAr
           const int j = chunk_of(k);
           const int uu = past ? 0 : u - j * kUnits;
           const int c = past ? cb : min(cb + st * SCH + j, ce - 1);
-          const int t = c * kChunk + uu % 16;
-          const int tv = c * kChunk + (uu % ELT) * (16 / ELT);
-          const int32_t* trow = a.tables + static_cast<int64_t>(first) * a.table_stride;
-          const int64_t bk = trow[t / BS], bv = trow[tv / BS];
-          sk[k] = kv16<true>(kl + (bk * hkv + kvh) * PAIR + ((uu / 16) * BS + t % BS) * 16);
-          sv[k] = kv16<true>(vl + (bv * hkv + kvh) * PAIR + ((uu / ELT) * BS + tv % BS) * ELT);
+          const int j0 = __builtin_amdgcn_readfirstlane(2 * c);
+          const int64_t b0 = table[j0], b1 = table[j0 + 1];
+          const int r = uu % 16;                     // K: the unit's token in the chunk
+          const int rv = (uu % ELT) * (16 / ELT);    // V: its first token
+          const int64_t bk = r < BS ? b0 : b1, bv = rv < BS ? b0 : b1;
+          sk[k] = kv16<true>(kl + (bk * hkv + kvh) * PAIR + ((uu / 16) * BS + r % BS) * 16);
+          sv[k] = kv16<true>(vl + (bv * hkv + kvh) * PAIR + ((uu / ELT) * BS + rv % BS) * ELT);
         }
       }
     }
