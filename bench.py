@@ -762,8 +762,8 @@ def main():
     # context, prompt, block size, layer count or partition size
     as_counted = not (args.batch or args.context or args.block_size or args.layers or
                       args.partition_tokens or args.prompt_len)
-    if args.layout == "paged" and as_counted:
-        key = (f"cfg{args.config}-paged" + (f"-shared{args.shared_prefix}" if args.shared_prefix else "") +
+    if args.layout in ("paged", "contiguous") and as_counted:
+        key = (f"cfg{args.config}-{args.layout}" + (f"-shared{args.shared_prefix}" if args.shared_prefix else "") +
                ("" if args.separate_append else "-fused"))
         traffic = measured_traffic(key, args.steps, args.warmup)
         roof = res["roofline"]
