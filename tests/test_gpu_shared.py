@@ -117,6 +117,21 @@ def test_odd_number_of_partition_items_leaves_one_half_idle():
         assert row_rel_err(to_f64(got[s]), to_f64(plain[s])) <= 1e-5, s
 
 
+def test_no_groups_falls_back_to_the_partition_kernel():
+    # samples of one prompt never adjacent in the batch: every request is a
+    # singleton, no shared pass runs, and the shared call must still equal the
+    # plain decode (its partitions and merge, with nothing skipped)
+    cfg = W.get(5, batch=24, prompt_len=200, private_len=40, num_blocks=200)
+    case = Case(cfg)
+    order = [p * 8 + k for k in range(8) for p in range(3)]   # 0, 8, 16, 1, 9, 17, ...
+    got, seq_shared, groups = _run_shared(case, 32, order)
+    assert len(groups) == 0 and int(seq_shared.max()) == 0
+    _check_oracle(case, got)
+    plain = case.decode(partition_tokens=32)
+    for s in range(cfg.batch):
+        assert row_rel_err(to_f64(got[s]), to_f64(plain[s])) <= 1e-5, s
+
+
 def test_mixed_groups_and_singletons():
     cfg = W.get(5, batch=24, prompt_len=200, private_len=40, num_blocks=200)
     case = Case(cfg)
