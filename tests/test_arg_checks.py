@@ -176,3 +176,29 @@ def test_shared_args():
     _refused(p.check_shared_args, np.array([24, 32, 32, 32], np.int32), lens, 16)   # not a multiple
     _refused(p.check_shared_args, np.array([64, 32, 32, 32], np.int32), lens, 16)   # past the context
     _refused(p.check_shared_args, seq_shared, lens, 24)                             # bad partition
+
+
+def test_shared_decode_host_checks_refuse_before_any_launch():
+    # every call below fails a host check before anything is launched (the
+    # device addresses are fake)
+    lib = capi.load()
+    keep, addr = _fake(1 << 12)
+
+    def call(pool, pt, groups, n_groups, max_members, max_shared):
+        return lib.pa_decode_shared(pool.handle, 0, addr, capi.PA_BF16, 2, ctypes.c_float(0.125), addr,
+                                    4, addr, 4, 64, pt, addr, groups, n_groups, max_members, max_shared,
+                                    addr, addr, 1 << 12, None)
+
+    contig = Pool(host_only=True, num_layers=1, num_blocks=0, block_size=16, num_kv_heads=1,
+                  head_dim=64, kv_dtype="bf16", layout="contiguous", max_seqs=8, max_seq_len=64)
+    assert call(contig, 32, addr, 1, 4, 32) == capi.PA_ERR_INVALID_ARG
+    assert b"paged layout" in lib.pa_last_error()
+    paged = Pool(host_only=True, num_layers=1, num_blocks=32, block_size=16, num_kv_heads=1,
+                 head_dim=64, kv_dtype="bf16", layout="paged", max_seqs=8, max_seq_len=64)
+    assert call(paged, 0, addr, 1, 4, 32) == capi.PA_ERR_INVALID_ARG           # no partition size
+    assert b"partition_tokens" in lib.pa_last_error()
+    assert call(paged, 32, addr, 1, 4, 48) == capi.PA_ERR_INVALID_ARG          # not whole partitions
+    assert b"max_shared" in lib.pa_last_error()
+    assert call(paged, 32, addr, 1, 4, 96) == capi.PA_ERR_INVALID_ARG          # past max_context
+    assert call(paged, 32, None, 1, 4, 32) == capi.PA_ERR_INVALID_ARG          # groups missing
+    assert b"null groups" in lib.pa_last_error()
