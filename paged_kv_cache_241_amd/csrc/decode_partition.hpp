@@ -563,11 +563,12 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
         // On balanced-start grids (one partition per context, all workgroups
         // resident) these stores and the output are the launch's last
         // traffic and go out non-temporal: Llama-3-8B batch-64 layer 45.49 ->
-        // 44.75 us, Yi-34B share 46.57 -> 45.73 us.  On the split ragged mix
-        // the same change cost 1.2 us (233.1 against 232.0 us), so the other
-        // grids keep ordinary stores.
+        // 44.75 us, Yi-34B share 46.57 -> 45.73 us.  The shared-prefix
+        // launch's private items (PAIRED) too: Yi-6B step 82.15 -> 80.74 us.
+        // On the split ragged mix the same change cost 1.2 us (233.1 against
+        // 232.0 us), so the other grids keep ordinary stores.
         auto st16 = [](char* dst, const char* src) {
-          if constexpr (BAL)
+          if constexpr (BAL || PAIRED)
             __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(src), reinterpret_cast<u32x4_t*>(dst));
           else
             *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
