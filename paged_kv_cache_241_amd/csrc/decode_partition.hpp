@@ -535,8 +535,7 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
       Lt = fmaf(wt, sm_l[w * G + g], Lt);
     }
     if (P == 1) {
-      if constexpr (BAL) __builtin_nontemporal_store(A / Lt, &a.out[(row0 + g) * D + e]);
-      else a.out[(row0 + g) * D + e] = A / Lt;
+      __builtin_nontemporal_store(A / Lt, &a.out[(row0 + g) * D + e]);
     } else {
       const int64_t prow = (row0 + g) * P + part;
       float* acc_ws = a.ws + static_cast<int64_t>(a.num_seqs) * a.num_q_heads * P * 2;
@@ -560,15 +559,18 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
                    (o / kChunk) * SUBPAIR;
         char* vt = kt + CH;
         constexpr int kVUnits = D * kChunk * ELT / 16;   // 16-byte units of the chunk's V
-        // On balanced-start grids (one partition per context, all workgroups
-        // resident) these stores and the output are the launch's last
-        // traffic and go out non-temporal: Llama-3-8B batch-64 layer 45.49 ->
-        // 44.75 us, Yi-34B share 46.57 -> 45.73 us.  The shared-prefix
-        // launch's private items (PAIRED) too: Yi-6B step 82.15 -> 80.74 us.
-        // On the split ragged mix the same change cost 1.2 us (233.1 against
-        // 232.0 us), so the other grids keep ordinary stores.
-        auto st16 = [](char* dst, const char* src) {
-          if constexpr (BAL || PAIRED)
+        // Where no split-K partial follows them (one partition per context)
+        // these stores and the output are the launch's last traffic and go
+        // out non-temporal: Llama-3-8B batch-64 layer 45.49 -> 44.75 us,
+        // Yi-34B share 46.57 -> 45.73 us, Yi-6B shared-prefix workload read
+        // per sample 133.9 -> 132.2 us, batch 256 x 512 tokens 100.7 -> 99.3
+        // us.  The shared-prefix launch's private items (PAIRED) too: Yi-6B
+        // step 82.15 -> 80.74 us.  On the split ragged mix the same change
+        // cost 1.2 us (233.1 against 232.0 us), so split launches keep
+        // ordinary stores.
+        const bool nt_end = BAL || PAIRED || P == 1;
+        auto st16 = [nt_end](char* dst, const char* src) {
+          if (nt_end)
             __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(src), reinterpret_cast<u32x4_t*>(dst));
           else
             *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
