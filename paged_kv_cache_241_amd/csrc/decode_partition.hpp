@@ -546,6 +546,10 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
       }
     }
   }
+  // Where no split-K partial follows them (one partition per context) the
+  // appended row's stores and the output are the launch's last traffic and
+  // go out non-temporal (measurements at st16 below)
+  const bool nt_end = BAL || PAIRED || P == 1;
   if constexpr (kWholeSectors) {
     // whole sectors from the staged chunk, by every thread: the chunk's D V
     // rows (16 tokens each) and K rows o & ~1, o | 1 of every 16-byte piece
@@ -559,16 +563,13 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
                    (o / kChunk) * SUBPAIR;
         char* vt = kt + CH;
         constexpr int kVUnits = D * kChunk * ELT / 16;   // 16-byte units of the chunk's V
-        // Where no split-K partial follows them (one partition per context)
-        // these stores and the output are the launch's last traffic and go
-        // out non-temporal: Llama-3-8B batch-64 layer 45.49 -> 44.75 us,
-        // Yi-34B share 46.57 -> 45.73 us, Yi-6B shared-prefix workload read
-        // per sample 133.9 -> 132.2 us, batch 256 x 512 tokens 100.7 -> 99.3
-        // us.  The shared-prefix launch's private items (PAIRED) too: Yi-6B
-        // step 82.15 -> 80.74 us.  On the split ragged mix the same change
-        // cost 1.2 us (233.1 against 232.0 us), so split launches keep
-        // ordinary stores.
-        const bool nt_end = BAL || PAIRED || P == 1;
+        // Non-temporal where no split-K partial follows: Llama-3-8B batch-64
+        // layer 45.49 -> 44.75 us, Yi-34B share 46.57 -> 45.73 us, Yi-6B
+        // shared-prefix workload read per sample 133.9 -> 132.2 us, batch
+        // 256 x 512 tokens 100.7 -> 99.3 us; the shared-prefix launch's
+        // private items (PAIRED) too: Yi-6B step 82.15 -> 80.74 us.  On the
+        // split ragged mix the same change cost 1.2 us (233.1 against 232.0
+        // us), so split launches keep ordinary stores.
         auto st16 = [nt_end](char* dst, const char* src) {
           if (nt_end)
             __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(src), reinterpret_cast<u32x4_t*>(dst));
@@ -592,15 +593,25 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
     const int64_t u = slot / BS;
     const int o = slot % BS;
     char* kt = geo.base + static_cast<int64_t>(a.layer) * geo.layer_bytes + (u * hkv + kvh) * PAIR;
-    *reinterpret_cast<uint4*>(kt + (q * BS + o) * 16) = sm_new[q];
+    // non-temporal on one-partition launches, as above (8-token blocks:
+    // Llama-3-8B batch-64 layer 46.32 -> 45.50 us, Yi-34B share 46.98 ->
+    // 46.47 us)
+    const uint4 kw = sm_new[q];
+    char* kd = kt + (q * BS + o) * 16;
+    if (nt_end) __builtin_nontemporal_store(u32x4_t{kw.x, kw.y, kw.z, kw.w}, reinterpret_cast<u32x4_t*>(kd));
+    else *reinterpret_cast<uint4*>(kd) = kw;
     const uint4 vw = sm_new[kRowVec + q];
     char* vt = kt + CH;
     const uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
     if constexpr (KIND == kBF16) {
+      auto st2 = [nt_end](char* dst, uint16_t x) {
+        if (nt_end) __builtin_nontemporal_store(x, reinterpret_cast<uint16_t*>(dst));
+        else *reinterpret_cast<uint16_t*>(dst) = x;
+      };
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint16_t*>(vt + ((q * VE + 2 * e) * BS + o) * 2) = static_cast<uint16_t>(w[e] & 0xFFFFu);
-        *reinterpret_cast<uint16_t*>(vt + ((q * VE + 2 * e + 1) * BS + o) * 2) = static_cast<uint16_t>(w[e] >> 16);
+        st2(vt + ((q * VE + 2 * e) * BS + o) * 2, static_cast<uint16_t>(w[e] & 0xFFFFu));
+        st2(vt + ((q * VE + 2 * e + 1) * BS + o) * 2, static_cast<uint16_t>(w[e] >> 16));
       }
     } else {
 #pragma unroll
