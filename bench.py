@@ -57,6 +57,9 @@ def parse():
                          "sharing a prompt read its blocks once)")
     ap.add_argument("--separate-append", action="store_true",
                     help="pa_append_kv then pa_decode per layer instead of one pa_append_decode")
+    ap.add_argument("--plan-per-layer", action="store_true",
+                    help="each layer's call makes its own work plan (pa_decode / pa_append_decode) "
+                         "instead of one pa_decode_plan per step and the planned calls")
     ap.add_argument("--layers", type=int, default=0, help="layer pools rotated (0: workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget")
     ap.add_argument("--swap-seqs", type=int, default=0, metavar="N",
@@ -241,12 +244,15 @@ class Bench:
             self.pool.append_kv(layer, kr.index_select(0, it).contiguous(),
                                 vr.index_select(0, it).contiguous(), st)
 
-    def prepare(self, max_steps: int, separate_append: bool = False, shared_tokens: int = 0):
+    def prepare(self, max_steps: int, separate_append: bool = False, shared_tokens: int = 0,
+                plan_per_layer: bool = False):
         """Fixed device buffers, double-buffered pinned staging, ctypes arguments.
 
         shared_tokens > 0: decode with pa_append_decode_shared (or, with
         separate_append, pa_append_kv + pa_decode_shared) in partitions of
-        that many tokens."""
+        that many tokens.  Otherwise a split launch's work plan is made once
+        per step (pa_decode_plan, then every layer's pa_append_decode_planned
+        or pa_decode_planned), or, with plan_per_layer, in each layer's call."""
         import ctypes
 
         import torch
@@ -302,6 +308,9 @@ class Bench:
         self.dtype_code = capi.PA_BF16 if self.cfg.kv_dtype == "bf16" else capi.PA_F32
         self.check = capi.check
         self.separate_append = separate_append
+        self.plan_once = not plan_per_layer and not shared_tokens
+        self.plans_made = 0     # steps whose launches ran from a plan made once
+        self.planned = ctypes.c_int32()
         self.nstep = 0
         # the tables only change when a block is handed out: upload on demand
         self.tables_dirty = True
@@ -367,6 +376,12 @@ class Bench:
             # separate one for the staging cost 1.3% of the step)
             ev[0].record(self.stream)
             st["event"] = ev[0]
+        if self.plan_once:
+            # one work plan for every layer: they all attend the same lengths
+            self.check(lib.pa_decode_plan(pool.handle, self.lens_d.data_ptr(), b, cfg.num_q_heads,
+                                          max_context, self.pt, self.ws.data_ptr(), self.ws_bytes,
+                                          ctypes.byref(self.planned), self.sh), "pa_decode_plan")
+            self.plans_made += self.planned.value
         for layer in range(self.nl):
             tail = (self.q[layer].data_ptr(), self.dtype_code, cfg.num_q_heads, self.scale, tables,
                     self.stride, req, self.lens_d.data_ptr(), b, max_context, self.pt,
@@ -384,11 +399,13 @@ class Bench:
                         pool.handle, layer, self.k_new[layer].data_ptr(), self.v_new[layer].data_ptr(),
                         self.slots_d.data_ptr(), *shared_tail), "pa_append_decode_shared")
             elif self.separate_append:
-                self.check(lib.pa_decode(pool.handle, layer, *tail), "pa_decode")
+                fn = lib.pa_decode_planned if self.plan_once else lib.pa_decode
+                self.check(fn(pool.handle, layer, *tail), "pa_decode")
             else:
-                self.check(lib.pa_append_decode(pool.handle, layer, self.k_new[layer].data_ptr(),
-                                                self.v_new[layer].data_ptr(), self.slots_d.data_ptr(),
-                                                *tail), "pa_append_decode")
+                fn = lib.pa_append_decode_planned if self.plan_once else lib.pa_append_decode
+                self.check(fn(pool.handle, layer, self.k_new[layer].data_ptr(),
+                              self.v_new[layer].data_ptr(), self.slots_d.data_ptr(), *tail),
+                           "pa_append_decode")
         if ev is not None:
             ev[1].record(self.stream)
         return lens
@@ -669,7 +686,8 @@ def main():
             cfg = W.get(args.config, **over)
     nl = args.layers or cfg.num_layers
     bench = Bench(cfg, args.layout, nl, args.warmup + args.steps + 1, args.partition_tokens)
-    bench.prepare(args.warmup + args.steps, args.separate_append, args.shared_prefix)
+    bench.prepare(args.warmup + args.steps, args.separate_append, args.shared_prefix,
+                  args.plan_per_layer)
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
@@ -729,7 +747,12 @@ def main():
             "decode": ("shared prefixes read once (" +
                        ("pa_append_kv + pa_decode_shared" if args.separate_append else "pa_append_decode_shared") +
                        ")") if args.shared_prefix else
-                      ("pa_append_kv + pa_decode" if args.separate_append else "pa_append_decode"),
+                      ("pa_append_kv + pa_decode" if args.separate_append else "pa_append_decode") +
+                      ("_planned" if bench.plan_once else ""),
+            "work_plan": ("none (shared-prefix launch)" if args.shared_prefix else
+                          "in each layer's call, where the launch uses one" if args.plan_per_layer else
+                          "once per step (pa_decode_plan), used by every layer" if bench.plans_made else
+                          "none (no launch of this size uses one)"),
         },
         # logical K/V bytes count a shared block once per sharer; the share of
         # HBM's peak is taken on the distinct bytes
@@ -746,8 +769,9 @@ def main():
                        " (decode_shared_kernel: shared pass and private partitions; "
                        "decode_merge_kernel)" if args.shared_prefix else
                        ("pa_decode" if args.separate_append else "pa_append_decode") +
-                       " (decode_partition_kernel; decode_plan_kernel and decode_merge_kernel "
-                       "when contexts are split)"),
+                       " (decode_partition_kernel; decode_merge_kernel when contexts are split, "
+                       "and decode_plan_kernel for large split launches, " +
+                       ("in each layer's call" if args.plan_per_layer else "once per step") + ")"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -759,9 +783,9 @@ def main():
         },
     }
     # the counters were taken on each workload as it stands: no other batch,
-    # context, prompt, block size, layer count or partition size
+    # context, prompt, block size, layer count, partition size or plan mode
     as_counted = not (args.batch or args.context or args.block_size or args.layers or
-                      args.partition_tokens or args.prompt_len)
+                      args.partition_tokens or args.prompt_len or args.plan_per_layer)
     if args.layout in ("paged", "contiguous") and as_counted:
         key = (f"cfg{args.config}-{args.layout}" + (f"-shared{args.shared_prefix}" if args.shared_prefix else "") +
                ("" if args.separate_append else "-fused"))

@@ -423,6 +423,47 @@ pa_status pa_append_decode(pa_pool* pool, int32_t layer, const void* d_k, const 
                            int32_t partition_tokens, float* d_out, void* d_workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Work plan of a split decode, made once for a decode iteration and used by
+ * every layer's pa_decode_planned / pa_append_decode_planned of that
+ * iteration ([KVP] Observation-1: an iteration advances each running request
+ * by one token, so all its layers attend the same context lengths; one block
+ * table serves every layer).  Arguments as pa_decode's, same meaning.  A
+ * launch with these sizes runs from a plan when its contexts are split into
+ * partitions and its grid holds at least 2048 workgroups; for such a launch
+ * the call enqueues the plan into its place in d_workspace (after the
+ * partials) and sets *planned_out (may be NULL) to 1, for any other launch it
+ * enqueues nothing and sets 0.  The plan depends only on the values of
+ * d_context_lens, num_seqs, num_q_heads, max_context and partition_tokens.
+ * Errors: as pa_decode (PA_ERR_WORKSPACE when d_workspace is too small for a
+ * launch that uses a plan). */
+pa_status pa_decode_plan(pa_pool* pool, const int32_t* d_context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t max_context, int32_t partition_tokens,
+                         void* d_workspace, size_t workspace_bytes, int32_t* planned_out, void* stream);
+
+/* pa_decode and pa_append_decode without their own plan: they read the plan
+ * that pa_decode_plan left in d_workspace, for the same context length values,
+ * num_seqs, num_q_heads, max_context and partition_tokens (so one plan serves
+ * all layers of an iteration; nothing else may write the workspace between
+ * the plan and its last use; pa_decode / pa_append_decode with those same
+ * arguments write an equivalent plan in its place).  Launches that use no plan run exactly as
+ * pa_decode / pa_append_decode.  Arguments, results (bit for bit) and errors
+ * are theirs.  A plan made for other values gives wrong results; its items
+ * are range-checked, so it reads and writes only what a correct call with
+ * these arguments may. */
+pa_status pa_decode_planned(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
+                            int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                            int32_t table_stride, const int32_t* d_req_ids,
+                            const int32_t* d_context_lens, int32_t num_seqs, int32_t max_context,
+                            int32_t partition_tokens, float* d_out, void* d_workspace,
+                            size_t workspace_bytes, void* stream);
+pa_status pa_append_decode_planned(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                                   const int32_t* d_slots, const void* d_q, pa_dtype q_dtype,
+                                   int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                                   int32_t table_stride, const int32_t* d_req_ids,
+                                   const int32_t* d_context_lens, int32_t num_seqs,
+                                   int32_t max_context, int32_t partition_tokens, float* d_out,
+                                   void* d_workspace, size_t workspace_bytes, void* stream);
+
 /* pa_append_decode for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same arguments without the workspace; the split-K partials

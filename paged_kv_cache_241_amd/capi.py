@@ -46,7 +46,8 @@ EXPORTS = (
     "pa_swap_bytes", "pa_swap_out", "pa_swap_in", "pa_create_pool_vmm", "pa_vmm_info",
     "pa_vmm_trim", "pa_shared_groups", "pa_decode_shared", "pa_check_decode_args",
     "pa_check_slots", "pa_check_block_pairs", "pa_append_decode_noalloc", "pa_append_decode_shared",
-    "pa_check_shared_args", "pa_last_error",
+    "pa_check_shared_args", "pa_decode_plan", "pa_decode_planned", "pa_append_decode_planned",
+    "pa_last_error",
 )
 
 # bytes of the device scratch pa_append_decode_noalloc holds on each GPU
@@ -141,6 +142,14 @@ def load() -> ctypes.CDLL:
         "pa_append_decode": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
                                             ctypes.c_float, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                                             _vp, _vp, ctypes.c_size_t, _vp]),
+        "pa_decode_plan": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, ctypes.c_size_t,
+                                          ctypes.POINTER(ctypes.c_int32), _vp]),
+        "pa_decode_planned": (ctypes.c_int, [_vp, _i32, _vp, ctypes.c_int, _i32, ctypes.c_float, _vp,
+                                             _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
+                                             ctypes.c_size_t, _vp]),
+        "pa_append_decode_planned": (ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
+                                                    ctypes.c_float, _vp, _i32, _vp, _vp, _i32, _i32,
+                                                    _i32, _vp, _vp, ctypes.c_size_t, _vp]),
         "pa_check_decode_args": (ctypes.c_int, [_vp, _p32, _i32, _p32, _p32, _p32, _i32, _i32]),
         "pa_check_slots": (ctypes.c_int, [_vp, _p32, _i32]),
         "pa_check_block_pairs": (ctypes.c_int, [_vp, _p32, _i32]),

@@ -97,11 +97,11 @@ __device__ __forceinline__ void decode_partition_body(const CacheGeom& geo, cons
   int s, kvh, part, L;
   if (a.plan != nullptr) {
     const int2 it = a.plan[bid / hkv];
-    if (it.x < 0) return leave();
+    if (it.x < 0 || it.x >= a.num_seqs * P) return leave();
     s = it.x / P;
     part = it.x % P;
     kvh = bid % hkv;
-    L = it.y;
+    L = min(max(it.y, 0), a.max_context);
   } else {
     const int work = work_item(bid, nblocks, !NT);
     const int pairs = a.num_seqs * hkv;

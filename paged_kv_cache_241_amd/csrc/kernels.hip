@@ -492,8 +492,32 @@ hipError_t launch_merge(const CacheGeom& g, const DecodeArgs& a, hipStream_t str
   return g.head_dim == 128 ? launch_merge_d<128>(a, stream) : launch_merge_d<64>(a, stream);
 }
 
+namespace {
+int2* plan_place(const CacheGeom& g, const DecodeArgs& a) {
+  // the plan follows the partials in the workspace
+  return reinterpret_cast<int2*>(a.ws + static_cast<int64_t>(a.num_seqs) * a.num_q_heads *
+                                            a.num_partitions * (g.head_dim + 2));
+}
+}  // namespace
+
+// Large split launches run from a plan (decode_plan_kernel).  Below
+// kPlanMinGrid workgroups the plan's launch (~3 us) costs more than it saves
+// (measured: batch 1-16 with contexts of 4-8 K tokens); after a shared-prefix
+// pass every context has one private partition left, and the plan does not
+// pay either.
+bool decode_uses_plan(const CacheGeom& g, const DecodeArgs& a) {
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
+  return a.num_seqs > 0 && a.num_partitions > 1 && a.seq_shared == nullptr && grid >= kPlanMinGrid;
+}
+
+hipError_t launch_decode_plan(const CacheGeom& g, const DecodeArgs& a, hipStream_t stream) {
+  if (!decode_uses_plan(g, a)) return hipSuccess;
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, plan_place(g, a));
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool* supported,
-                         hipStream_t stream) {
+                         hipStream_t stream, bool plan_made) {
   *supported = true;
   if (a.num_seqs <= 0) return hipSuccess;
   if (a.num_q_heads / g.num_kv_heads > kMaxGroup || (g.head_dim != 128 && g.head_dim != 64)) {
@@ -501,20 +525,12 @@ hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool
     return hipSuccess;
   }
   DecodeArgs ap = a;
-  // Large split launches run from a plan (decode_plan_kernel).  Below
-  // kPlanMinGrid workgroups the plan's launch (~3 us) costs more than it
-  // saves (measured: batch 1-16 with contexts of 4-8 K tokens); after a
-  // shared-prefix pass every context has one private partition left, and
-  // the plan does not pay either.
-  const int64_t grid = static_cast<int64_t>(a.num_seqs) * g.num_kv_heads * a.num_partitions;
-  if (a.num_partitions > 1 && a.seq_shared == nullptr && grid >= kPlanMinGrid) {
-    // the plan follows the partials in the workspace
-    int2* plan = reinterpret_cast<int2*>(a.ws + static_cast<int64_t>(a.num_seqs) * a.num_q_heads *
-                                                    a.num_partitions * (g.head_dim + 2));
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, plan);
-    hipError_t ep = hipGetLastError();
-    if (ep != hipSuccess) return ep;
-    ap.plan = plan;
+  if (decode_uses_plan(g, a)) {
+    if (!plan_made) {
+      const hipError_t ep = launch_decode_plan(g, a, stream);
+      if (ep != hipSuccess) return ep;
+    }
+    ap.plan = plan_place(g, a);
   }
   hipError_t e = hipSuccess;
   if (kind == kBF16 && g.head_dim == 128) e = launch_decode_bs<kBF16, 128>(g, ap, supported, stream);

@@ -63,6 +63,7 @@ struct DecodeArgs {
   int32_t table_stride = 0;
   int32_t partition_chunks = 0;      // 16-token chunks per partition
   int32_t num_partitions = 1;
+  int32_t max_context = 0;           // no context is longer (tables hold its blocks)
   // fused append (pa_append_decode): token L_s - 1 of sequence s is
   // new_k[s] / new_v[s] ([B][Hkv][D]), stored to slot new_slots[s] (< 0: none)
   const void* new_k = nullptr;
@@ -77,6 +78,9 @@ struct DecodeArgs {
   // work plan of a split launch (decode_plan_kernel's output in the
   // workspace): item i = {s * num_partitions + partition, L_s}, {-1, 0} past
   // the last.  Null: the grid enumerates every (partition, sequence, head).
+  // Items outside [0, num_seqs * num_partitions) are skipped and lengths
+  // clamped to [0, max_context], so a plan made for other lengths gives
+  // wrong results but no access outside the caller's arrays.
   const int2* plan = nullptr;
 };
 
@@ -95,11 +99,22 @@ struct SharedArgs {
   int32_t private_lds = 0;
 };
 
-// The partition kernel and, with several partitions, the merge.  *supported
-// is set to false (and nothing is launched) when no kernel exists for the
-// shape.
+// Whether a launch with these arguments runs from a work plan: split
+// launches of at least two rounds of resident workgroups, without shared
+// prefixes.
+bool decode_uses_plan(const CacheGeom& g, const DecodeArgs& a);
+
+// The work plan of such a launch, into its place in the workspace (after the
+// partials); nothing for other launches.
+hipError_t launch_decode_plan(const CacheGeom& g, const DecodeArgs& a, hipStream_t stream);
+
+// The partition kernel and, with several partitions, the merge; the plan
+// first where the launch uses one, unless plan_made (a launch_decode_plan for
+// the same lengths, sizes and workspace ran before it on the stream).
+// *supported is set to false (and nothing is launched) when no kernel exists
+// for the shape.
 hipError_t launch_decode(const CacheGeom& g, int kind, const DecodeArgs& a, bool* supported,
-                         hipStream_t stream);
+                         hipStream_t stream, bool plan_made = false);
 
 // The merge of a split launch's partials (nothing when unsplit).
 hipError_t launch_merge(const CacheGeom& g, const DecodeArgs& a, hipStream_t stream);

@@ -527,7 +527,7 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
                       void* d_workspace, size_t workspace_bytes, void* stream,
                       const int32_t* d_seq_shared = nullptr, const int32_t* d_groups = nullptr,
                       int32_t num_groups = 0, int32_t max_members = 0, int32_t max_shared = 0,
-                      bool static_workspace = false) {
+                      bool static_workspace = false, bool plan_made = false) {
   const std::string w(who);
   const bool shared = d_seq_shared != nullptr;
   if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null pool");
@@ -585,6 +585,7 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
   const int32_t pt = choose_partition_tokens(pool, num_seqs, max_context, partition_tokens);
   a.partition_chunks = pt / 16;
   a.num_partitions = num_partitions(max_context, pt);
+  a.max_context = max_context;
   if (shared) {
     // partials and the merge even where one partition would cover a context
     a.num_partitions = std::max(a.num_partitions, 2);
@@ -642,7 +643,8 @@ pa_status decode_impl(const char* who, pa_pool* pool, int32_t layer, const void*
     if (es != hipSuccess) return fail(PA_ERR_HIP, std::string(w + ": ") + hipGetErrorString(es));
     return PA_OK;
   }
-  hipError_t e = pa::launch_decode(pool->geom, kind, a, &supported, static_cast<hipStream_t>(stream));
+  hipError_t e = pa::launch_decode(pool->geom, kind, a, &supported, static_cast<hipStream_t>(stream),
+                                   plan_made);
   if (!supported) return fail(PA_ERR_UNSUPPORTED, w + ": no kernel for this shape");
   if (e != hipSuccess) return fail(PA_ERR_HIP, std::string(w + ": ") + hipGetErrorString(e));
   return PA_OK;
@@ -679,6 +681,82 @@ pa_status pa_append_decode(pa_pool* pool, int32_t layer, const void* d_k, const 
     return decode_impl("append_decode", pool, layer, d_k, d_v, d_slots, d_q, q_dtype, num_q_heads,
                        scale, d_block_tables, table_stride, d_req_ids, d_context_lens, num_seqs,
                        max_context, partition_tokens, d_out, d_workspace, workspace_bytes, stream);
+  });
+}
+
+pa_status pa_decode_plan(pa_pool* pool, const int32_t* d_context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t max_context, int32_t partition_tokens,
+                         void* d_workspace, size_t workspace_bytes, int32_t* planned_out, void* stream) {
+  return guarded("decode_plan", [&]() -> pa_status {
+    const std::string w = "decode_plan";
+    if (planned_out != nullptr) *planned_out = 0;
+    if (pool == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null pool");
+    const pa_pool_desc& d = pool->desc;
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, w + ": negative num_seqs");
+    if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
+      return fail(PA_ERR_INVALID_ARG, w + ": num_q_heads must be a positive multiple of num_kv_heads");
+    if (max_context < 0 || max_context > d.max_seq_len)
+      return fail(PA_ERR_INVALID_ARG, w + ": max_context must be in [0, max_seq_len]");
+    if (bad_partition(pool, partition_tokens))
+      return fail(PA_ERR_INVALID_ARG,
+                  w + ": partition_tokens must be 0 or a positive multiple of 16 and of block_size");
+    if (num_seqs == 0) return PA_OK;
+    if (d_context_lens == nullptr) return fail(PA_ERR_INVALID_ARG, w + ": null context lengths");
+    pa::DecodeArgs a;
+    a.lens = d_context_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    const int32_t pt = choose_partition_tokens(pool, num_seqs, max_context, partition_tokens);
+    a.partition_chunks = pt / 16;
+    a.num_partitions = num_partitions(max_context, pt);
+    a.max_context = max_context;
+    if (static_cast<int64_t>(num_seqs) * d.num_kv_heads * a.num_partitions > INT32_MAX)
+      return fail(PA_ERR_INVALID_ARG, w + ": launch too large");
+    if (!pa::decode_uses_plan(pool->geom, a)) return PA_OK;
+    const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, d.head_dim, a.num_partitions);
+    if (d_workspace == nullptr || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, w + ": workspace needs " + std::to_string(need) + " bytes, got " +
+                                        std::to_string(d_workspace ? workspace_bytes : 0));
+    if (reinterpret_cast<uintptr_t>(d_workspace) & 15)
+      return fail(PA_ERR_INVALID_ARG, w + ": workspace must be 16-byte aligned");
+    a.ws = static_cast<float*>(d_workspace);
+    const hipError_t e = pa::launch_decode_plan(pool->geom, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, w + ": " + hipGetErrorString(e));
+    if (planned_out != nullptr) *planned_out = 1;
+    return PA_OK;
+  });
+}
+
+pa_status pa_decode_planned(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
+                            int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                            int32_t table_stride, const int32_t* d_req_ids,
+                            const int32_t* d_context_lens, int32_t num_seqs, int32_t max_context,
+                            int32_t partition_tokens, float* d_out, void* d_workspace,
+                            size_t workspace_bytes, void* stream) {
+  return guarded("decode_planned", [&]() -> pa_status {
+    return decode_impl("decode_planned", pool, layer, nullptr, nullptr, nullptr, d_q, q_dtype,
+                       num_q_heads, scale, d_block_tables, table_stride, d_req_ids, d_context_lens,
+                       num_seqs, max_context, partition_tokens, d_out, d_workspace, workspace_bytes,
+                       stream, nullptr, nullptr, 0, 0, 0, false, /*plan_made=*/true);
+  });
+}
+
+pa_status pa_append_decode_planned(pa_pool* pool, int32_t layer, const void* d_k, const void* d_v,
+                                   const int32_t* d_slots, const void* d_q, pa_dtype q_dtype,
+                                   int32_t num_q_heads, float scale, const int32_t* d_block_tables,
+                                   int32_t table_stride, const int32_t* d_req_ids,
+                                   const int32_t* d_context_lens, int32_t num_seqs,
+                                   int32_t max_context, int32_t partition_tokens, float* d_out,
+                                   void* d_workspace, size_t workspace_bytes, void* stream) {
+  return guarded("append_decode_planned", [&]() -> pa_status {
+    if (d_k == nullptr || d_v == nullptr || d_slots == nullptr)
+      return fail(PA_ERR_INVALID_ARG, "append_decode_planned: null k, v or slots");
+    if ((reinterpret_cast<uintptr_t>(d_k) | reinterpret_cast<uintptr_t>(d_v)) & 15)
+      return fail(PA_ERR_INVALID_ARG, "append_decode_planned: k and v must be 16-byte aligned");
+    return decode_impl("append_decode_planned", pool, layer, d_k, d_v, d_slots, d_q, q_dtype,
+                       num_q_heads, scale, d_block_tables, table_stride, d_req_ids, d_context_lens,
+                       num_seqs, max_context, partition_tokens, d_out, d_workspace, workspace_bytes,
+                       stream, nullptr, nullptr, 0, 0, 0, false, /*plan_made=*/true);
   });
 }
 

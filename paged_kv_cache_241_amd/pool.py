@@ -349,13 +349,33 @@ class Pool:
         return int(self.lib.pa_decode_workspace_bytes(self.handle, num_seqs, num_q_heads,
                                                       max_context, partition_tokens))
 
+    def decode_plan(self, context_lens, num_q_heads: int, max_context: int, workspace,
+                    partition_tokens: int = 0, stream=None) -> bool:
+        """pa_decode_plan: the work plan of a split decode into ``workspace``,
+        for every layer's ``decode(..., planned=True)`` with these lengths and
+        sizes; False when such a launch uses no plan (nothing is enqueued)."""
+        import torch
+
+        assert self._device, "host-only pool"
+        assert context_lens.is_cuda and context_lens.dtype == torch.int32 and context_lens.is_contiguous()
+        b = int(context_lens.shape[0])
+        made = ctypes.c_int32(0)
+        capi.check(self.lib.pa_decode_plan(
+            self.handle, context_lens.data_ptr(), b, int(num_q_heads), int(max_context),
+            int(partition_tokens), workspace.data_ptr() if workspace is not None else None,
+            workspace.numel() * workspace.element_size() if workspace is not None else 0,
+            ctypes.byref(made), _stream_handle(stream)), "pa_decode_plan")
+        return bool(made.value)
+
     def decode(self, layer: int, q, scale: float, block_tables, context_lens, max_context: int,
                out=None, partition_tokens: int = 0, req_ids=None, workspace=None, stream=None,
-               append=None):
+               append=None, planned: bool = False):
         """Decode attention for q [B][Hq][D]; returns out fp32 [B][Hq][D].
 
         ``append=(k, v, slots)`` stores each sequence's new token first, in the
         same launch (pa_append_decode); k, v are [B][Hkv][D], slots int32 [B].
+        ``planned``: the plan ``decode_plan`` left in ``workspace`` is used
+        (pa_decode_planned / pa_append_decode_planned).
         """
         import torch
 
@@ -375,6 +395,7 @@ class Pool:
         assert out.is_contiguous() and out.dtype == torch.float32 and tuple(out.shape) == (b, hq, d)
         need = self.workspace_bytes(b, hq, max_context, partition_tokens)
         if need and workspace is None:
+            assert not planned, "a planned decode reads its plan from the caller's workspace"
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -384,15 +405,17 @@ class Pool:
                 int(max_context), int(partition_tokens), out.data_ptr(), ws_ptr, ws_bytes,
                 _stream_handle(stream))
         if append is None:
-            capi.check(self.lib.pa_decode(self.handle, layer, *args), "pa_decode")
+            name = "pa_decode_planned" if planned else "pa_decode"
+            capi.check(getattr(self.lib, name)(self.handle, layer, *args), name)
         else:
             k, v, slots = append
             for t in (k, v):
                 assert t.is_cuda and t.is_contiguous() and t.dtype == self.torch_dtype
                 assert tuple(t.shape) == (b, self.num_kv_heads, self.head_dim)
             assert slots.is_cuda and slots.dtype == torch.int32 and tuple(slots.shape) == (b,)
-            capi.check(self.lib.pa_append_decode(self.handle, layer, k.data_ptr(), v.data_ptr(),
-                                                 slots.data_ptr(), *args), "pa_append_decode")
+            name = "pa_append_decode_planned" if planned else "pa_append_decode"
+            capi.check(getattr(self.lib, name)(self.handle, layer, k.data_ptr(), v.data_ptr(),
+                                               slots.data_ptr(), *args), name)
         return out
 
     def append_decode_noalloc(self, layer: int, q, scale: float, block_tables, context_lens,

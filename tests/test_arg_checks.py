@@ -8,7 +8,9 @@ would make it read or write outside the caches.
   copies of the device arrays and refuse every planted bad entry (block ids
   outside the pool, lengths past max_context, short tables, request ids out
   of range, append slots that are not position L-1's or that repeat, copy
-  pairs that overlap), and accept what the allocator hands out.
+  pairs that overlap), and accept what the allocator hands out;
+* pa_decode_plan refuses a short or misaligned workspace and bad sizes
+  before any launch, and enqueues nothing for a launch that uses no plan.
 """
 
 import ctypes
@@ -202,3 +204,40 @@ def test_shared_decode_host_checks_refuse_before_any_launch():
     assert call(paged, 32, addr, 1, 4, 96) == capi.PA_ERR_INVALID_ARG          # past max_context
     assert call(paged, 32, None, 1, 4, 32) == capi.PA_ERR_INVALID_ARG          # groups missing
     assert b"null groups" in lib.pa_last_error()
+
+
+def test_decode_plan_host_checks_refuse_before_any_launch():
+    lib = capi.load()
+    p = Pool(host_only=True, num_layers=1, num_blocks=64, block_size=16, num_kv_heads=8,
+             head_dim=128, kv_dtype="bf16", layout="paged", max_seqs=512, max_seq_len=8192)
+    keep, addr = _fake(1 << 12)
+    made = ctypes.c_int32(7)
+    # 8 sequences of at most 1024 tokens: a few hundred workgroups, too few
+    # for a plan; nothing is enqueued and no workspace is looked at
+    st = lib.pa_decode_plan(p.handle, addr, 8, 32, 1024, 0, None, 0, ctypes.byref(made), None)
+    assert st == capi.PA_OK and made.value == 0, lib.pa_last_error()
+    # 256 sequences x 8 KV heads x 8 partitions of 1024 tokens run from a plan:
+    # a workspace short of the partials and the plan is refused
+    need = p.workspace_bytes(256, 32, 8192, 1024)
+    made.value = 7
+    st = lib.pa_decode_plan(p.handle, addr, 256, 32, 8192, 1024, addr, need - 16,
+                            ctypes.byref(made), None)
+    assert st == capi.PA_ERR_WORKSPACE and made.value == 0, lib.pa_last_error()
+    st = lib.pa_decode_plan(p.handle, addr, 256, 32, 8192, 1024, addr + 8, need,
+                            ctypes.byref(made), None)
+    assert st == capi.PA_ERR_INVALID_ARG and b"aligned" in lib.pa_last_error()
+    # arguments that no launch takes
+    for args in ((None, 256, 32, 8192, 1024),     # no lengths
+                 (addr, -1, 32, 8192, 1024),      # negative batch
+                 (addr, 256, 12, 8192, 1024),     # query heads not a multiple of the KV heads
+                 (addr, 256, 32, 8193, 1024),     # past max_seq_len
+                 (addr, 256, 32, 8192, 1000)):    # not a multiple of 16
+        st = lib.pa_decode_plan(p.handle, *args, addr, need, ctypes.byref(made), None)
+        assert st == capi.PA_ERR_INVALID_ARG, (args, lib.pa_last_error())
+    assert lib.pa_decode_plan(None, addr, 256, 32, 8192, 1024, addr, need, None,
+                              None) == capi.PA_ERR_INVALID_ARG
+    # the planned decode calls check what pa_decode checks
+    for fn, extra in ((lib.pa_decode_planned, ()), (lib.pa_append_decode_planned, (addr, addr, addr))):
+        st = fn(p.handle, 0, *extra, addr, capi.PA_BF16, 32, ctypes.c_float(0.088), addr, 512, None,
+                addr, 256, 8192, 1024, addr, addr, need - 16, None)
+        assert st == capi.PA_ERR_WORKSPACE, lib.pa_last_error()
