@@ -447,9 +447,10 @@ pa_status pa_decode_plan(pa_pool* pool, const int32_t* d_context_lens, int32_t n
  * the plan and its last use; pa_decode / pa_append_decode with those same
  * arguments write an equivalent plan in its place).  Launches that use no plan run exactly as
  * pa_decode / pa_append_decode.  Arguments, results (bit for bit) and errors
- * are theirs.  A plan made for other values gives wrong results; its items
- * are range-checked, so it reads and writes only what a correct call with
- * these arguments may. */
+ * are theirs.  A plan made for other values gives wrong outputs (and, with
+ * the append, wrong bytes in the rows the append rewrites); its items are
+ * range-checked, so the call still reads and writes only memory that a
+ * correct call with these arguments may. */
 pa_status pa_decode_planned(pa_pool* pool, int32_t layer, const void* d_q, pa_dtype q_dtype,
                             int32_t num_q_heads, float scale, const int32_t* d_block_tables,
                             int32_t table_stride, const int32_t* d_req_ids,
