@@ -8,7 +8,9 @@ in the decode launch.  K, V and q rows are N(0, 1), written through the
 library's allocator and append; the oracle attends over the same logical
 rows in fp64.  Tolerances are those of the other parity tests.  Two more
 cases run a batch of more than 1024 and of more than 4096 short sequences
-split into many partitions, so that every path of the work plan runs.
+split into many partitions, so that every path of the work plan runs.  Those
+and the large ragged batches also run the call from a plan made beforehand
+(pa_decode_plan with the planned calls), which must give the same bits.
 """
 
 from __future__ import annotations
@@ -37,7 +39,8 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _run(rng, hkv, G, d, bs, dtype, layout, lens, pt, fused, max_seq_len=1024, check_rows=None):
+def _run(rng, hkv, G, d, bs, dtype, layout, lens, pt, fused, max_seq_len=1024, check_rows=None,
+         planned=False):
     hq = hkv * G
     B = len(lens)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -69,12 +72,23 @@ def _run(rng, hkv, G, d, bs, dtype, layout, lens, pt, fused, max_seq_len=1024, c
     q = torch.randn((B, hq, d), generator=gen).to(tdt)
     scale = float(np.float32(1.0 / np.sqrt(d)))
     max_context = max(int(lens.max()), 1)
-    out = pool.decode(0, q.cuda(), scale, torch.from_numpy(tables).cuda(),
-                      torch.from_numpy(lens.astype(np.int32)).cuda(), max_context,
-                      partition_tokens=pt,
-                      req_ids=torch.tensor(rids, dtype=torch.int32, device="cuda") if layout != "paged" else None,
-                      append=append)
+    lens_d = torch.from_numpy(lens.astype(np.int32)).cuda()
+    tables_d = torch.from_numpy(tables).cuda()
+    req_d = torch.tensor(rids, dtype=torch.int32, device="cuda") if layout != "paged" else None
+    out = pool.decode(0, q.cuda(), scale, tables_d, lens_d, max_context, partition_tokens=pt,
+                      req_ids=req_d, append=append)
     torch.cuda.synchronize()
+    if planned:
+        # the same call from a plan made beforehand (pa_decode_plan, then
+        # pa_decode_planned / pa_append_decode_planned): the same bits; a
+        # repeated append stores the same rows again
+        ws = torch.empty(max(pool.workspace_bytes(B, hq, max_context, pt), 16), dtype=torch.uint8,
+                         device="cuda")
+        pool.decode_plan(lens_d, hq, max_context, ws, pt)
+        again = pool.decode(0, q.cuda(), scale, tables_d, lens_d, max_context, partition_tokens=pt,
+                            req_ids=req_d, append=append, workspace=ws, planned=True)
+        torch.cuda.synchronize()
+        assert torch.equal(again, out)
     got = to_f64(out)
     qf, kf, vf = to_f64(q), to_f64(rows_k), to_f64(rows_v)
     for s in (range(B) if check_rows is None else check_rows):
@@ -121,7 +135,8 @@ def test_many_short_sequences_split_into_many_partitions(B):
     if fused:
         lens = np.maximum(lens, 1)   # each sequence appends its last token in the launch
     sample = sorted(set([0, 1, 2, B - 1] + [int(x) for x in rng.choice(B, 40, replace=False)]))
-    _run(rng, 2, 4, 64, 16, "bf16", "paged", lens, 16, fused, max_seq_len=128, check_rows=sample)
+    _run(rng, 2, 4, 64, 16, "bf16", "paged", lens, 16, fused, max_seq_len=128, check_rows=sample,
+         planned=True)
 
 
 @pytest.mark.parametrize("seed", range(8))
@@ -144,7 +159,8 @@ def test_large_ragged_batch(seed):
     unit = max(16, bs)
     pt = int(rng.choice([0, 0, 256, 512, 1024])) // unit * unit
     rows = sorted(set([0, B - 1, int(np.argmax(lens))] + [int(x) for x in rng.choice(B, 8, replace=False)]))
-    _run(rng, hkv, G, 128, bs, dtype, layout, lens, pt, fused, max_seq_len=8192, check_rows=rows)
+    _run(rng, hkv, G, 128, bs, dtype, layout, lens, pt, fused, max_seq_len=8192, check_rows=rows,
+         planned=True)
 
 
 @pytest.mark.parametrize("fused", [True, False])
