@@ -61,6 +61,8 @@ def parse():
                     help="each layer's call makes its own work plan (pa_decode / pa_append_decode) "
                          "instead of one pa_decode_plan per step and the planned calls")
     ap.add_argument("--layers", type=int, default=0, help="layer pools rotated (0: workload's)")
+    ap.add_argument("--time-every", type=int, default=TIMING_EVERY, metavar="K",
+                    help="HIP events bracket the decode launches of every K-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget")
     ap.add_argument("--swap-seqs", type=int, default=0, metavar="N",
                     help="after the timed steps, swap N requests out to pinned host memory "
@@ -691,11 +693,14 @@ def main():
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
-    # HIP events bracket the decode launches of every TIMING_EVERY-th timed
-    # step (the first one included); the other steps record only the staging
-    # buffer's event.  Each event recorded on the stream holds the GPU ~5 us,
-    # so timing every step would itself lower the whole-step rate.
-    timed = [i for i in range(args.steps) if i % TIMING_EVERY == 0]
+    # HIP events bracket the decode launches of every K-th timed step
+    # (--time-every, default TIMING_EVERY; the first one included); the other
+    # steps record only the staging buffer's event.  Each event recorded on
+    # the stream holds the GPU ~5 us, so timing every step would itself lower
+    # the whole-step rate (every 4th against every 8th step: 5936 against
+    # 5951 GB/s whole step on the Llama-3-8B layer, three runs each, within
+    # run-to-run spread).
+    timed = [i for i in range(args.steps) if i % max(args.time_every, 1) == 0]
     evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in timed}
     total_kv = 0
     lens_seen = []
