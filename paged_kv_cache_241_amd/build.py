@@ -75,6 +75,18 @@ def build(verbose: bool = False) -> str:
           os.path.join(BUILD, "decode_shared.o"), os.path.join(BUILD, "pa_api.o"),
           os.path.join(BUILD, "block_allocator.o"), os.path.join(BUILD, "vmm.o")], verbose)
     os.replace(tmp, LIB)
+    # a C caller of the ABI for the tests (plain C99 and the HIP runtime; it
+    # finds libpa.so next to the package through its run path)
+    c_src = os.path.join(ROOT, "tests", "c_abi_decode.c")
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if os.path.exists(c_src) and cc:
+        rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
+        _run([cc, "-std=c99", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+              "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"), c_src,
+              "-o", os.path.join(ROOT, "tests", "c_abi_decode"),
+              "-L", PKG, "-lpa", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+              "-Wl,-rpath,$ORIGIN/../paged_kv_cache_241_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")],
+             verbose)
     # the benchmark's achievable-bandwidth probe (not part of the library)
     probe_src = os.path.join(ROOT, "bench_read_probe.hip")
     if os.path.exists(probe_src):
