@@ -227,6 +227,7 @@ class Pool:
             need = self.workspace_bytes(b, hq, max(int(max_context), int(partition_tokens) + 1),
                                         partition_tokens)
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        assert workspace.is_cuda and workspace.is_contiguous()
         tail = (q.data_ptr(), _DTYPES[self.kv_dtype], hq, float(scale),
                 block_tables.data_ptr(), int(block_tables.shape[1]), context_lens.data_ptr(), b,
                 int(max_context), int(partition_tokens), seq_shared.data_ptr(),
@@ -359,6 +360,7 @@ class Pool:
         assert self._device, "host-only pool"
         assert context_lens.is_cuda and context_lens.dtype == torch.int32 and context_lens.is_contiguous()
         b = int(context_lens.shape[0])
+        assert workspace is None or (workspace.is_cuda and workspace.is_contiguous())
         made = ctypes.c_int32(0)
         capi.check(self.lib.pa_decode_plan(
             self.handle, context_lens.data_ptr(), b, int(num_q_heads), int(max_context),
@@ -397,6 +399,7 @@ class Pool:
         if need and workspace is None:
             assert not planned, "a planned decode reads its plan from the caller's workspace"
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        assert workspace is None or (workspace.is_cuda and workspace.is_contiguous())
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         args = (q.data_ptr(), _DTYPES[self.kv_dtype], hq, float(scale),
