@@ -222,6 +222,7 @@ class Pool:
         assert tuple(seq_shared.shape) == (b,) and tuple(context_lens.shape) == (b,)
         if out is None:
             out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
+        assert out.is_cuda and out.is_contiguous() and out.dtype == torch.float32 and tuple(out.shape) == (b, hq, d)
         if workspace is None:
             # at least two partitions: the shared pass always writes partials
             need = self.workspace_bytes(b, hq, max(int(max_context), int(partition_tokens) + 1),
@@ -394,7 +395,7 @@ class Pool:
             assert req_ids.is_cuda and req_ids.dtype == torch.int32 and tuple(req_ids.shape) == (b,)
         if out is None:
             out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
-        assert out.is_contiguous() and out.dtype == torch.float32 and tuple(out.shape) == (b, hq, d)
+        assert out.is_cuda and out.is_contiguous() and out.dtype == torch.float32 and tuple(out.shape) == (b, hq, d)
         need = self.workspace_bytes(b, hq, max_context, partition_tokens)
         if need and workspace is None:
             assert not planned, "a planned decode reads its plan from the caller's workspace"
@@ -445,7 +446,7 @@ class Pool:
         assert slots.is_cuda and slots.dtype == torch.int32 and tuple(slots.shape) == (b,)
         if out is None:
             out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
-        assert out.is_contiguous() and out.dtype == torch.float32 and tuple(out.shape) == (b, hq, d)
+        assert out.is_cuda and out.is_contiguous() and out.dtype == torch.float32 and tuple(out.shape) == (b, hq, d)
         capi.check(self.lib.pa_append_decode_noalloc(
             self.handle, layer, k.data_ptr(), v.data_ptr(), slots.data_ptr(), q.data_ptr(),
             _DTYPES[self.kv_dtype], hq, float(scale),
